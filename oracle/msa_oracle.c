@@ -1,0 +1,233 @@
+/*
+ * msa_oracle.c -- plain, slow, fp64 CPU oracle for the MSA forward pass.
+ *
+ * TEST INFRASTRUCTURE ONLY (see msa_oracle.h).  Written as the definition of
+ * the method, step by step, with no blocking, fusion or reordering beyond
+ * what that definition states.  OpenMP only splits independent
+ * (query, group) or (query, head) rows across threads; each row is computed
+ * by one thread in a fixed order, so results do not depend on the thread
+ * count.
+ *
+ * Sources (page title, section):
+ *   - "MiniMax Sparse Attention" paper summary (hyper.ai), Method: token score
+ *     is the index-q / index-k dot product over visible keys, block score is
+ *     the max over the block, Top-k per GQA group, the local block always
+ *     kept; Main Branch is standard scaled-dot-product attention over the
+ *     gathered tokens of the chosen blocks.
+ *   - zhichai.net write-up, section 2 (architecture): one index-q and one
+ *     index-k head per GQA group; Bk = 128, k = 16, budget k*Bk tokens (so k
+ *     counts the local block); every query head of a group shares the
+ *     group's block set but keeps its own query.
+ *   - same write-up, section 4.1 (exp-free Top-k): only the order of the
+ *     scores matters, so no exponential is taken before selection.
+ * Readings where the pages are silent: ties go to the lowest block id,
+ * the output list is ascending with -1 padding, key t is visible to the
+ * query at position p iff t <= p.
+ */
+#include "msa_oracle.h"
+
+#include <math.h>
+#include <omp.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* Exact widening of one stored element to fp64. */
+static double widen(const void* base, int dtype, int64_t idx) {
+  if (dtype == MO_F64) return ((const double*)base)[idx];
+  if (dtype == MO_F32) return (double)((const float*)base)[idx];
+  uint32_t bits = (uint32_t)((const uint16_t*)base)[idx] << 16; /* bf16 -> fp32 */
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return (double)f;
+}
+
+static int check_problem(const mo_problem* p, int dtype) {
+  if (!p) return -1;
+  if (p->batch < 1 || p->n_q < 1 || p->n_k < 1 || p->h_q < 1 || p->h_kv < 1) return -2;
+  if (p->d < 1 || p->d_idx < 1 || p->block_size < 1 || p->topk < 1) return -3;
+  if (p->h_q % p->h_kv) return -4;
+  if (p->q_offset < 0 || p->q_offset + p->n_q > p->n_k) return -5;
+  if (dtype != MO_F32 && dtype != MO_BF16 && dtype != MO_F64) return -6;
+  return 0;
+}
+
+static int64_t num_blocks(const mo_problem* p) {
+  return ((int64_t)p->n_k + p->block_size - 1) / p->block_size;
+}
+
+static void row_of(const mo_problem* p, const int64_t* rows, int64_t r, int64_t* b, int64_t* i) {
+  if (rows) {
+    *b = rows[2 * r];
+    *i = rows[2 * r + 1];
+  } else {
+    *b = r / p->n_q;
+    *i = r % p->n_q;
+  }
+}
+
+static int check_rows(const mo_problem* p, const int64_t* rows, int64_t n_rows) {
+  if (n_rows < 0) return -7;
+  if (!rows) return n_rows == (int64_t)p->batch * p->n_q ? 0 : -8;
+  for (int64_t r = 0; r < n_rows; ++r)
+    if (rows[2 * r] < 0 || rows[2 * r] >= p->batch || rows[2 * r + 1] < 0 || rows[2 * r + 1] >= p->n_q)
+      return -9;
+  return 0;
+}
+
+int mo_num_threads(void) { return omp_get_max_threads(); }
+
+/* Steps 1 and 2: token scores and Block Max Pooling. */
+int mo_block_scores(const mo_problem* p, const void* iq, const void* ik, int dtype,
+                    const int64_t* rows, int64_t n_rows, double* scores) {
+  int rc = check_problem(p, dtype);
+  if (rc) return rc;
+  if ((rc = check_rows(p, rows, n_rows))) return rc;
+  if (!iq || !ik || !scores) return -1;
+  const int64_t nblk = num_blocks(p), H = p->h_kv, D = p->d_idx, Bk = p->block_size;
+
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t rg = 0; rg < n_rows * H; ++rg) {
+    const int64_t r = rg / H, g = rg % H;
+    int64_t b, i;
+    row_of(p, rows, r, &b, &i);
+    const int64_t pos = p->q_offset + i;
+    const int64_t L = pos / Bk; /* local block */
+    double* S = scores + (r * H + g) * nblk;
+    for (int64_t j = 0; j < nblk; ++j) S[j] = -INFINITY;
+    const int64_t qbase = ((b * p->n_q + i) * H + g) * D;
+    for (int64_t j = 0; j < L; ++j) {
+      double best = -INFINITY;
+      for (int64_t t = j * Bk; t < (j + 1) * Bk; ++t) {
+        if (t > pos || t >= p->n_k) continue; /* visible tokens only */
+        const int64_t kbase = ((b * p->n_k + t) * H + g) * D;
+        double s = 0.0;
+        for (int64_t c = 0; c < D; ++c) s += widen(iq, dtype, qbase + c) * widen(ik, dtype, kbase + c);
+        if (s > best) best = s;
+      }
+      S[j] = best;
+    }
+  }
+  return 0;
+}
+
+typedef struct {
+  double s;
+  int32_t j;
+} cand_t;
+
+/* Order for Top-k: higher score first; equal scores -> lower block id first. */
+static int by_score_desc_id_asc(const void* a, const void* b) {
+  const cand_t* x = (const cand_t*)a;
+  const cand_t* y = (const cand_t*)b;
+  if (x->s > y->s) return -1;
+  if (x->s < y->s) return 1;
+  return (x->j > y->j) - (x->j < y->j);
+}
+
+static int by_int_asc(const void* a, const void* b) {
+  const int32_t x = *(const int32_t*)a, y = *(const int32_t*)b;
+  return (x > y) - (x < y);
+}
+
+/* Step 3: the local block plus the top-(k-1) candidates; no exponential. */
+int mo_select(const mo_problem* p, const double* scores, const int64_t* rows, int64_t n_rows,
+              int32_t* ids) {
+  int rc = check_problem(p, MO_F64);
+  if (rc) return rc;
+  if ((rc = check_rows(p, rows, n_rows))) return rc;
+  if (!scores || !ids) return -1;
+  const int64_t nblk = num_blocks(p), H = p->h_kv, K = p->topk, Bk = p->block_size;
+
+#pragma omp parallel
+  {
+    cand_t* cand = (cand_t*)malloc(sizeof(cand_t) * (size_t)(nblk > 0 ? nblk : 1));
+    int32_t* chosen = (int32_t*)malloc(sizeof(int32_t) * (size_t)(K + 1));
+#pragma omp for schedule(static)
+    for (int64_t rg = 0; rg < n_rows * H; ++rg) {
+      const int64_t r = rg / H;
+      int64_t b, i;
+      row_of(p, rows, r, &b, &i);
+      const int64_t L = (p->q_offset + i) / Bk;
+      const double* S = scores + rg * nblk;
+      int32_t* out = ids + rg * K;
+      int64_t n = 0;
+      if (L <= K - 1) {
+        for (int64_t j = 0; j < L; ++j) chosen[n++] = (int32_t)j; /* every candidate */
+      } else {
+        for (int64_t j = 0; j < L; ++j) {
+          cand[j].s = S[j];
+          cand[j].j = (int32_t)j;
+        }
+        qsort(cand, (size_t)L, sizeof(cand_t), by_score_desc_id_asc);
+        for (int64_t m = 0; m < K - 1; ++m) chosen[n++] = cand[m].j;
+      }
+      chosen[n++] = (int32_t)L; /* the local block is always kept */
+      qsort(chosen, (size_t)n, sizeof(int32_t), by_int_asc);
+      for (int64_t m = 0; m < K; ++m) out[m] = m < n ? chosen[m] : -1;
+    }
+    free(cand);
+    free(chosen);
+  }
+  return 0;
+}
+
+/* Step 4: exact softmax attention restricted to the selected blocks. */
+int mo_attend(const mo_problem* p, const void* q, const void* k, const void* v, int dtype,
+              const int32_t* ids, const int64_t* rows, int64_t n_rows, double* out, double* lse) {
+  int rc = check_problem(p, dtype);
+  if (rc) return rc;
+  if ((rc = check_rows(p, rows, n_rows))) return rc;
+  if (!q || !k || !v || !ids || !out) return -1;
+  const int64_t Hq = p->h_q, Hkv = p->h_kv, G = Hq / Hkv, D = p->d, K = p->topk, Bk = p->block_size;
+  const int64_t nblk = num_blocks(p);
+  const double scale = p->softmax_scale > 0 ? p->softmax_scale : 1.0 / sqrt((double)D);
+
+#pragma omp parallel
+  {
+    /* Worst case: every block selected. */
+    const int64_t cap = (K < nblk ? K : nblk) * Bk;
+    double* x = (double*)malloc(sizeof(double) * (size_t)cap);
+    int64_t* tok = (int64_t*)malloc(sizeof(int64_t) * (size_t)cap);
+#pragma omp for schedule(dynamic, 4)
+    for (int64_t rh = 0; rh < n_rows * Hq; ++rh) {
+      const int64_t r = rh / Hq, h = rh % Hq, g = h / G;
+      int64_t b, i;
+      row_of(p, rows, r, &b, &i);
+      const int64_t pos = p->q_offset + i;
+      const int32_t* sel = ids + (r * Hkv + g) * K;
+      /* T: visible tokens of the selected blocks. */
+      int64_t n = 0;
+      for (int64_t s = 0; s < K; ++s) {
+        const int64_t j = sel[s];
+        if (j < 0 || j >= nblk) continue;
+        for (int64_t t = j * Bk; t < (j + 1) * Bk; ++t)
+          if (t <= pos && t < p->n_k) tok[n++] = t;
+      }
+      const int64_t qbase = ((b * p->n_q + i) * Hq + h) * D;
+      double m = -INFINITY;
+      for (int64_t a = 0; a < n; ++a) {
+        const int64_t kbase = ((b * p->n_k + tok[a]) * Hkv + g) * D;
+        double s = 0.0;
+        for (int64_t c = 0; c < D; ++c) s += widen(q, dtype, qbase + c) * widen(k, dtype, kbase + c);
+        x[a] = scale * s;
+        if (x[a] > m) m = x[a];
+      }
+      double l = 0.0;
+      for (int64_t a = 0; a < n; ++a) {
+        x[a] = exp(x[a] - m);
+        l += x[a];
+      }
+      double* o = out + rh * D;
+      for (int64_t c = 0; c < D; ++c) o[c] = 0.0;
+      for (int64_t a = 0; a < n; ++a) {
+        const int64_t vbase = ((b * p->n_k + tok[a]) * Hkv + g) * D;
+        for (int64_t c = 0; c < D; ++c) o[c] += x[a] * widen(v, dtype, vbase + c);
+      }
+      for (int64_t c = 0; c < D; ++c) o[c] /= l;
+      if (lse) lse[rh] = m + log(l);
+    }
+    free(x);
+    free(tok);
+  }
+  return 0;
+}

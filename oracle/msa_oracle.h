@@ -1,0 +1,76 @@
+/*
+ * msa_oracle.h -- plain fp64 CPU oracle for the MiniMax Sparse Attention (MSA)
+ * forward pass.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This library is what the GPU kernels are checked
+ * against.  Only the test-suite, the smoke check and the CPU-baseline leg of
+ * the benchmark may load it; the product path never does.  It shares no code,
+ * header or table with the HIP library.
+ *
+ * What it computes (MiniMax Sparse Attention, arXiv 2606.13392 summary page,
+ * "Method"; the same paper's abstract; the zhichai.net write-up, section 2):
+ *   1. token score  s_t = <idx_q[b,i,g,:], idx_k[b,t,g,:]>  (no scale)
+ *   2. block score  S_j = max over the tokens t of key block j of s_t
+ *      (Block Max Pooling), for every candidate block j < L(i), where
+ *      L(i) = floor(p(i)/Bk) is the block holding the query position
+ *      p(i) = q_offset + i.  Candidates are the blocks wholly before L(i).
+ *   3. selection    {L(i)} plus the (k-1) best candidates ordered by
+ *      (S descending, block id ascending); all candidates when there are at
+ *      most k-1 of them.  Emitted ascending, padded with -1 to length k.
+ *   4. attention    exact softmax attention of every query head h of group
+ *      g = h / (Hq/Hkv) over the visible tokens (t <= p(i), t < Nk) of the
+ *      selected blocks, softmax scale 1/sqrt(d) unless given.
+ * Every sum and product is carried out in IEEE fp64; bf16 and fp32 inputs are
+ * widened exactly.
+ *
+ * Tensor layouts (all contiguous, token-major):
+ *   q  [B, Nq, Hq,  d]      k, v [B, Nk, Hkv, d]
+ *   iq [B, Nq, Hkv, d_idx]  ik   [B, Nk, Hkv, d_idx]
+ *
+ * Query subsets: every routine takes `rows`, a list of n_rows (b, i) pairs
+ * stored as rows[2r] = b, rows[2r+1] = i.  rows == NULL means every (b, i)
+ * in batch-major order (n_rows must then equal B*Nq).  Outputs are indexed by
+ * r, the position in that list.
+ *
+ * Return value: 0 on success, a negative number for an invalid argument.
+ */
+#ifndef MSA_ORACLE_H
+#define MSA_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { MO_F32 = 0, MO_BF16 = 1, MO_F64 = 2 };
+
+typedef struct {
+  int32_t batch, n_q, n_k, h_q, h_kv, d, d_idx, block_size, topk;
+  int64_t q_offset;
+  double softmax_scale; /* <= 0 means 1/sqrt(d) */
+} mo_problem;
+
+/* Block scores.  scores: double [n_rows][h_kv][nblk], nblk = ceil(Nk/Bk).
+ * Entries for non-candidate blocks (j >= L(i)) are set to -INFINITY. */
+int mo_block_scores(const mo_problem* p, const void* iq, const void* ik, int dtype,
+                    const int64_t* rows, int64_t n_rows, double* scores);
+
+/* Selection from block scores laid out as mo_block_scores writes them.
+ * ids: int32 [n_rows][h_kv][topk], ascending, -1 padded. */
+int mo_select(const mo_problem* p, const double* scores, const int64_t* rows, int64_t n_rows,
+              int32_t* ids);
+
+/* Exact softmax attention over the tokens of the blocks listed in ids
+ * (int32 [n_rows][h_kv][topk], -1 entries ignored).
+ * out: double [n_rows][h_q][d]; lse: double [n_rows][h_q] (may be NULL). */
+int mo_attend(const mo_problem* p, const void* q, const void* k, const void* v, int dtype,
+              const int32_t* ids, const int64_t* rows, int64_t n_rows, double* out, double* lse);
+
+/* Number of OpenMP threads the routines above use. */
+int mo_num_threads(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

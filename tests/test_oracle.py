@@ -1,0 +1,389 @@
+"""Pins of the fp64 CPU oracle against facts fixed by the pages and by mathematics.
+
+Nothing here re-types the oracle's formulas.  Each pin is one of:
+  * a hand-worked example (tests/golden/worked_example_bk2.json);
+  * a closed form on planted data (block max pooling, causality);
+  * brute-force enumeration (Top-k with ties on tiny inputs);
+  * a special case that reduces to a library routine (k >= number of blocks
+    gives dense causal GQA attention: torch's scaled_dot_product_attention in
+    fp64; any selection gives SDPA with the selection as a boolean mask);
+  * an invariant (permutation inside a block, monotone transforms of the
+    scores, V == 1, one-hot V).
+``test_planted_mistakes_are_caught`` builds mutated copies of the oracle
+(one plausible mistake each) and checks that at least one pin fails for each.
+
+Sources: MiniMax Sparse Attention paper summary (hyper.ai), Method;
+zhichai.net write-up sections 2 and 4.1; readings for what the pages leave
+open (ties to the lowest id, ascending ids with -1 padding, t <= p causality).
+"""
+import itertools
+import json
+import math
+import os
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import build as obuild
+from oracle import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand(shape, rng, scale=1.0):
+    return rng.standard_normal(shape) * scale
+
+
+def _inputs(rng, B, Nq, Nk, Hq, Hkv, d, di):
+    return dict(q=_rand((B, Nq, Hq, d), rng), k=_rand((B, Nk, Hkv, d), rng), v=_rand((B, Nk, Hkv, d), rng),
+                iq=_rand((B, Nq, Hkv, di), rng), ik=_rand((B, Nk, Hkv, di), rng))
+
+
+def _sdpa_masked(prob, q, k, v, allowed):
+    """torch SDPA in fp64 with a boolean mask allowed[b, i, g, t] (True = attend)."""
+    G = prob.h_q // prob.h_kv
+    qt = torch.from_numpy(q).permute(0, 2, 1, 3)                                # [B,Hq,Nq,d]
+    kt = torch.from_numpy(k).permute(0, 2, 1, 3).repeat_interleave(G, dim=1)     # [B,Hq,Nk,d]
+    vt = torch.from_numpy(v).permute(0, 2, 1, 3).repeat_interleave(G, dim=1)
+    m = torch.from_numpy(allowed).permute(0, 2, 1, 3).repeat_interleave(G, dim=1)  # [B,Hq,Nq,Nk]
+    scale = prob.softmax_scale if prob.softmax_scale > 0 else 1.0 / math.sqrt(prob.d)
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=m, scale=scale)
+    logits = torch.matmul(qt, kt.transpose(-1, -2)) * scale
+    lse = torch.logsumexp(logits.masked_fill(~m, -math.inf), dim=-1)
+    return o.permute(0, 2, 1, 3).numpy(), lse.permute(0, 2, 1).numpy()
+
+
+def _causal_allowed(prob):
+    B, Nq, Nk = prob.batch, prob.n_q, prob.n_k
+    pos = prob.q_offset + np.arange(Nq)
+    allowed = np.arange(Nk)[None, :] <= pos[:, None]
+    return np.broadcast_to(allowed[None, :, None, :], (B, Nq, prob.h_kv, Nk)).copy()
+
+
+# ----------------------------------------------------------------------------
+# Pins.  Each takes an Oracle instance and raises AssertionError on failure.
+# ----------------------------------------------------------------------------
+
+def pin_golden_worked_example(orc):
+    g = json.load(open(os.path.join(GOLDEN, "worked_example_bk2.json")))
+    prob = O.make_problem(**g["problem"])
+    iq = np.array(g["idx_q"], dtype=np.float64).reshape(1, 8, 1, 2)
+    ik = np.array(g["idx_k"], dtype=np.float64).reshape(1, 8, 1, 2)
+    q = np.array(g["q"], dtype=np.float64).reshape(1, 8, 2, 2)
+    k = np.array(g["k"], dtype=np.float64).reshape(1, 8, 1, 2)
+    v = np.array(g["v"], dtype=np.float64).reshape(1, 8, 1, 2)
+    s = orc.block_scores(prob, iq, ik)
+    exp_s = np.array([[np.nan if x is None else x for x in row] for row in g["expect_scores"]])
+    got_s = s[:, 0, :]
+    cand = ~np.isnan(exp_s)
+    assert np.array_equal(got_s[cand], exp_s[cand]), (got_s, exp_s)
+    assert np.all(np.isneginf(got_s[~cand]))
+    ids = orc.select(prob, s)
+    assert np.array_equal(ids[:, 0, :], np.array(g["expect_ids"])), ids[:, 0, :]
+    out, lse = orc.attend(prob, q, k, v, ids)
+    np.testing.assert_allclose(out, np.array(g["expect_out"]), rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(lse, np.array(g["expect_lse"]), rtol=1e-14, atol=1e-14)
+
+
+def pin_maxpool_closed_form(orc):
+    """idx_q = a_i e0; block j: every token c_j e0 except one spike (c_j + e_j) e0.
+    Then S_j = a_i (c_j + e_j) if a_i > 0 and a_i c_j if a_i < 0 (exact in fp64)."""
+    rng = np.random.default_rng(7)
+    B, Nq, Nk, H, di, Bk = 1, 40, 40, 2, 4, 4
+    nb = Nk // Bk
+    prob = O.make_problem(B, Nq, Nk, 2, H, 4, di, Bk, 3)
+    a = rng.choice([-2.0, -0.5, 0.25, 1.0, 3.0], size=(Nq, H))
+    iq = np.zeros((B, Nq, H, di))
+    iq[0, :, :, 0] = a
+    c = rng.integers(-8, 8, size=(nb, H)).astype(np.float64) / 4
+    e = rng.integers(1, 8, size=(nb, H)).astype(np.float64) / 2
+    spike = rng.integers(0, Bk, size=(nb, H))
+    ik = np.zeros((B, Nk, H, di))
+    ik[0, :, :, 1:] = rng.standard_normal((Nk, H, di - 1))  # orthogonal to idx_q: no effect
+    for j in range(nb):
+        for g in range(H):
+            ik[0, j * Bk:(j + 1) * Bk, g, 0] = c[j, g]
+            ik[0, j * Bk + spike[j, g], g, 0] = c[j, g] + e[j, g]
+    s = orc.block_scores(prob, iq, ik)
+    for i in range(Nq):
+        L = i // Bk
+        for g in range(H):
+            exp = np.where(a[i, g] > 0, a[i, g] * (c[:, g] + e[:, g]), a[i, g] * c[:, g])
+            assert np.array_equal(s[i, g, :L], exp[:L]), (i, g)
+            assert np.all(np.isneginf(s[i, g, L:]))
+
+
+def pin_scores_ignore_future_and_token_order(orc):
+    """Permuting tokens inside a key block leaves block scores unchanged, and so
+    does any change to keys at or after the local block."""
+    rng = np.random.default_rng(11)
+    B, N, H, di, Bk = 2, 48, 2, 8, 4
+    prob = O.make_problem(B, N, N, 4, H, 8, di, Bk, 3)
+    x = _inputs(rng, B, N, N, 4, H, 8, di)
+    s0 = orc.block_scores(prob, x["iq"], x["ik"])
+    ik2 = x["ik"].copy()
+    for j in range(N // Bk):
+        perm = rng.permutation(Bk)
+        ik2[:, j * Bk:(j + 1) * Bk] = ik2[:, j * Bk + perm]
+    assert np.array_equal(s0, orc.block_scores(prob, x["iq"], ik2))
+    # keys of the last four blocks scaled up: only queries whose candidates
+    # include those blocks may change.
+    ik3 = x["ik"].copy()
+    ik3[:, 32:] *= 1e3
+    s3 = orc.block_scores(prob, x["iq"], ik3)
+    assert np.array_equal(s0[:, :, :8], s3[:, :, :8])
+    qs = np.arange(B * N) % N
+    early = qs < 36  # L(i) <= 8: candidates are blocks 0..7 only
+    assert np.array_equal(s0[early], s3[early])
+
+
+def _brute_select(S, L, K):
+    """Enumerate every (K-1)-subset of the candidates 0..L-1; keep the ones in
+    which each member outranks each non-member under (score desc, id asc)."""
+    if L <= K - 1:
+        return list(range(L + 1))
+    cands = range(L)
+    found = []
+    for T in itertools.combinations(cands, K - 1):
+        Ts = set(T)
+        ok = all((S[a] > S[b]) or (S[a] == S[b] and a < b) for a in Ts for b in cands if b not in Ts)
+        if ok:
+            found.append(T)
+    assert len(found) == 1, found
+    return sorted(list(found[0]) + [L])
+
+
+def pin_topk_bruteforce(orc):
+    rng = np.random.default_rng(3)
+    for K in (1, 2, 3, 4):
+        B, N, H, Bk = 1, 36, 3, 4  # 9 blocks
+        prob = O.make_problem(B, N, N, H, H, 2, 2, Bk, K)
+        nb = 9
+        # integer scores in a narrow range: many ties
+        S = rng.integers(-2, 3, size=(N, H, nb)).astype(np.float64)
+        for i in range(N):
+            S[i, :, i // Bk:] = -np.inf
+        ids = orc.select(prob, S)
+        for i in range(N):
+            for g in range(H):
+                exp = _brute_select(S[i, g], i // Bk, K)
+                exp = exp + [-1] * (K - len(exp))
+                assert list(ids[i, g]) == exp, (K, i, g, list(ids[i, g]), exp)
+
+
+def pin_topk_special_cases(orc):
+    B, N, H, Bk, K = 1, 64, 1, 4, 5  # 16 blocks
+    prob = O.make_problem(B, N, N, H, H, 2, 2, Bk, K)
+    S = np.zeros((N, H, 16))
+    for i in range(N):
+        S[i, :, i // Bk:] = -np.inf
+    ids = orc.select(prob, S)
+    for i in range(N):
+        L = i // Bk
+        if L <= K - 1:
+            exp = list(range(L + 1)) + [-1] * (K - L - 1)
+        else:  # all tied: the lowest ids win
+            exp = list(range(K - 1)) + [L]
+        assert list(ids[i, 0]) == exp, (i, list(ids[i, 0]), exp)
+    # -0.0 and +0.0 are equal scores: the lower id wins
+    S2 = S.copy()
+    S2[N - 1, 0, 0] = -0.0
+    S2[N - 1, 0, 1:15] = 0.0
+    assert list(orc.select(prob, S2)[N - 1, 0]) == [0, 1, 2, 3, 15]
+
+
+def pin_exp_free(orc):
+    """Top-k on raw scores equals Top-k on softmax probabilities (the softmax
+    is strictly increasing), zhichai.net write-up section 4.1."""
+    rng = np.random.default_rng(5)
+    B, N, H, Bk, K = 1, 256, 2, 4, 6
+    prob = O.make_problem(B, N, N, H, H, 2, 2, Bk, K)
+    S = rng.standard_normal((N, H, 64))
+    P = np.zeros_like(S)
+    for i in range(N):
+        L = i // Bk
+        S[i, :, L:] = -np.inf
+        if L:
+            P[i, :, :L] = torch.softmax(torch.from_numpy(S[i, :, :L]), dim=-1).numpy()
+        P[i, :, L:] = -np.inf
+    assert np.array_equal(orc.select(prob, S), orc.select(prob, P))
+    # and invariance to any positive scale and shift
+    assert np.array_equal(orc.select(prob, S), orc.select(prob, 3.0 * S - 7.0))
+
+
+def pin_dense_equals_sdpa(orc):
+    """k >= number of blocks: MSA is dense causal GQA attention."""
+    rng = np.random.default_rng(13)
+    for (B, Nq, Nk, off, Hq, Hkv, d, Bk) in [(2, 24, 24, 0, 4, 2, 8, 4), (1, 10, 27, 17, 6, 3, 16, 4),
+                                             (1, 9, 9, 0, 2, 1, 4, 8)]:
+        nb = (Nk + Bk - 1) // Bk
+        prob = O.make_problem(B, Nq, Nk, Hq, Hkv, d, 4, Bk, nb + 1, off)
+        x = _inputs(rng, B, Nq, Nk, Hq, Hkv, d, 4)
+        ids, out, lse, _ = orc.forward(prob, x["q"], x["k"], x["v"], x["iq"], x["ik"])
+        ref, ref_lse = _sdpa_masked(prob, x["q"], x["k"], x["v"], _causal_allowed(prob))
+        np.testing.assert_allclose(out, ref.reshape(out.shape), rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse, ref_lse.reshape(lse.shape), rtol=0, atol=1e-12)
+
+
+def pin_sparse_equals_masked_sdpa(orc):
+    """Any selection: attention over the visible tokens of the chosen blocks is
+    SDPA with that token set as a boolean mask (shared by the group's heads)."""
+    rng = np.random.default_rng(17)
+    B, N, Hq, Hkv, d, di, Bk, K = 2, 40, 6, 2, 8, 4, 4, 3
+    prob = O.make_problem(B, N, N, Hq, Hkv, d, di, Bk, K)
+    x = _inputs(rng, B, N, N, Hq, Hkv, d, di)
+    ids, out, lse, _ = orc.forward(prob, x["q"], x["k"], x["v"], x["iq"], x["ik"])
+    allowed = np.zeros((B, N, Hkv, N), dtype=bool)
+    idr = ids.reshape(B, N, Hkv, K)
+    for b in range(B):
+        for i in range(N):
+            for g in range(Hkv):
+                for j in idr[b, i, g]:
+                    if j >= 0:
+                        allowed[b, i, g, j * Bk:(j + 1) * Bk] = True
+    allowed &= _causal_allowed(prob)
+    ref, ref_lse = _sdpa_masked(prob, x["q"], x["k"], x["v"], allowed)
+    np.testing.assert_allclose(out, ref.reshape(out.shape), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, ref_lse.reshape(lse.shape), rtol=0, atol=1e-12)
+
+
+def pin_value_invariants(orc):
+    """V == 1 gives O == 1; one-hot V recovers a probability vector that sums to
+    one, vanishes off the visible selected tokens and peaks where q.k peaks."""
+    rng = np.random.default_rng(19)
+    B, N, Hq, Hkv, Bk, K = 1, 32, 2, 1, 4, 3
+    d = 32  # one-hot over the 32 tokens
+    prob = O.make_problem(B, N, N, Hq, Hkv, d, 2, Bk, K)
+    x = _inputs(rng, B, N, N, Hq, Hkv, d, 2)
+    ones = np.ones_like(x["v"])
+    ids, out, _, _ = orc.forward(prob, x["q"], x["k"], ones, x["iq"], x["ik"])
+    np.testing.assert_allclose(out, 1.0, rtol=0, atol=1e-14)
+    eye = np.eye(N).reshape(1, N, 1, N)
+    out, _ = orc.attend(prob, x["q"], x["k"], eye, ids)
+    for i in range(N):
+        vis = np.zeros(N, dtype=bool)
+        for j in ids[i, 0]:
+            if j >= 0:
+                vis[j * Bk:(j + 1) * Bk] = True
+        vis[i + 1:] = False
+        for h in range(Hq):
+            p = out[i, h]
+            assert abs(p.sum() - 1) < 1e-13
+            assert np.all(p[~vis] == 0)
+            logits = x["k"][0, :, 0, :] @ x["q"][0, i, h, :]
+            assert np.argmax(p) == np.flatnonzero(vis)[np.argmax(logits[vis])]
+
+
+def pin_causal_diagonal(orc):
+    """The query's own position is visible (t <= p): a key at t = p that matches
+    the query takes (almost) all the weight; keys after p never do."""
+    B, N, Hq, Hkv, d, Bk, K = 1, 16, 1, 1, 4, 4, 4
+    prob = O.make_problem(B, N, N, Hq, Hkv, d, 2, Bk, K, 0, 1.0)
+    q = np.zeros((B, N, Hq, d))
+    q[..., 0] = 1.0
+    k = np.zeros((B, N, Hkv, d))
+    v = np.zeros((B, N, Hkv, d))
+    v[0, :, 0, 1] = np.arange(N)
+    ids = np.tile(np.arange(K, dtype=np.int32), (N, 1)).reshape(N, 1, K)
+    for i in range(N):
+        kk = k.copy()
+        kk[0, i, 0, 0] = 800.0       # the diagonal key
+        kk[0, i + 1:, 0, 0] = 1600.0  # future keys: must be invisible
+        out, lse = orc.attend(prob, q, kk, v, ids[i:i + 1], rows=[[0, i]])
+        assert out[0, 0, 1] == i, (i, out[0, 0])
+        assert lse[0, 0] == 800.0
+
+
+PINS = [pin_golden_worked_example, pin_maxpool_closed_form, pin_scores_ignore_future_and_token_order,
+        pin_topk_bruteforce, pin_topk_special_cases, pin_exp_free, pin_dense_equals_sdpa,
+        pin_sparse_equals_masked_sdpa, pin_value_invariants, pin_causal_diagonal]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_oracle_pin(pin):
+    pin(O.default())
+
+
+def test_row_subsets_match_full():
+    """Evaluating a list of (b, i) rows gives the same values as the full run."""
+    rng = np.random.default_rng(23)
+    B, N, Hq, Hkv, d, di, Bk, K = 2, 24, 4, 2, 8, 4, 4, 3
+    prob = O.make_problem(B, N, N, Hq, Hkv, d, di, Bk, K)
+    x = _inputs(rng, B, N, N, Hq, Hkv, d, di)
+    ids, out, lse, s = O.forward(prob, x["q"], x["k"], x["v"], x["iq"], x["ik"])
+    rows = [[1, 5], [0, 23], [1, 0]]
+    ids2, out2, lse2, s2 = O.forward(prob, x["q"], x["k"], x["v"], x["iq"], x["ik"], rows=rows)
+    flat = [b * N + i for b, i in rows]
+    assert np.array_equal(ids[flat], ids2)
+    assert np.array_equal(out[flat], out2) and np.array_equal(lse[flat], lse2)
+    assert np.array_equal(s[flat], s2)
+
+
+def test_bf16_and_f32_inputs_widen_exactly():
+    rng = np.random.default_rng(29)
+    B, N, Hq, Hkv, d, di, Bk, K = 1, 16, 2, 1, 8, 8, 4, 2
+    prob = O.make_problem(B, N, N, Hq, Hkv, d, di, Bk, K)
+    x = {n: torch.from_numpy(a).to(torch.bfloat16) for n, a in _inputs(rng, B, N, N, Hq, Hkv, d, di).items()}
+    r_bf = O.forward(prob, x["q"], x["k"], x["v"], x["iq"], x["ik"])
+    x64 = {n: t.to(torch.float64).numpy() for n, t in x.items()}
+    r_64 = O.forward(prob, x64["q"], x64["k"], x64["v"], x64["iq"], x64["ik"])
+    x32 = {n: t.to(torch.float32) for n, t in x.items()}
+    r_32 = O.forward(prob, x32["q"], x32["k"], x32["v"], x32["iq"], x32["ik"])
+    for a, b, c in zip(r_bf, r_64, r_32):
+        assert np.array_equal(a, b) and np.array_equal(a, c)
+
+
+def test_invalid_arguments_rejected():
+    prob = O.make_problem(1, 8, 4, 2, 1, 2, 2, 2, 2)  # n_q > n_k
+    with pytest.raises(ValueError):
+        O.block_scores(prob, np.zeros((1, 8, 1, 2)), np.zeros((1, 4, 1, 2)))
+    prob = O.make_problem(1, 4, 4, 3, 2, 2, 2, 2, 2)  # h_q not a multiple of h_kv
+    with pytest.raises(ValueError):
+        O.block_scores(prob, np.zeros((1, 4, 2, 2)), np.zeros((1, 4, 2, 2)))
+
+
+# Plausible mistakes, planted by text substitution into a copy of the oracle.
+MUTANTS = {
+    "drops_diagonal_token": ("if (t <= pos && t < p->n_k) tok[n++] = t;", "if (t < pos && t < p->n_k) tok[n++] = t;"),
+    "forgets_local_block": ("chosen[n++] = (int32_t)L; /* the local block is always kept */", ""),
+    "ties_to_highest_id": ("return (x->j > y->j) - (x->j < y->j);", "return (x->j < y->j) - (x->j > y->j);"),
+    "sum_pooling": ("if (s > best) best = s;", "best = (best == -INFINITY ? 0.0 : best) + s;"),
+    "min_pooling": ("if (s > best) best = s;", "if (s < best || best == -INFINITY) best = s;"),
+    "scale_one_over_d": ("1.0 / sqrt((double)D)", "1.0 / (double)D"),
+    "strided_group_map": ("g = h / G;", "g = h % Hkv;"),
+    "k_excludes_local": ("for (int64_t m = 0; m < K - 1; ++m) chosen[n++] = cand[m].j;",
+                         "for (int64_t m = 0; m < K && m < L; ++m) chosen[n++] = cand[m].j;"),
+    "values_from_keys": ("o[c] += x[a] * widen(v, dtype, vbase + c);", "o[c] += x[a] * widen(k, dtype, vbase + c);"),
+    # (Dropping the visibility test inside the max pool is not a mistake one can
+    # catch: candidate blocks lie wholly before the query, so it never fires.)
+    "scores_include_local_block": ("for (int64_t j = 0; j < L; ++j) {\n      double best",
+                                   "for (int64_t j = 0; j <= L && j < nblk; ++j) {\n      double best"),
+}
+
+
+def test_planted_mistakes_are_caught(tmp_path):
+    src = open(os.path.join(os.path.dirname(obuild.__file__), "msa_oracle.c")).read()
+    hdr = os.path.join(os.path.dirname(obuild.__file__), "msa_oracle.h")
+    survivors = []
+    for name, (old, new) in MUTANTS.items():
+        assert src.count(old) == 1, f"mutant {name}: anchor text not found exactly once"
+        d = tmp_path / name
+        d.mkdir()
+        shutil.copy(hdr, d / "msa_oracle.h")
+        (d / "msa_oracle.c").write_text(src.replace(old, new))
+        so = str(d / "libm.so")
+        subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off", "-o", so,
+                        str(d / "msa_oracle.c"), "-lm"], check=True, capture_output=True)
+        orc = O.Oracle(so)
+        failed = []
+        for pin in PINS:
+            try:
+                pin(orc)
+            except (AssertionError, ValueError, IndexError):
+                failed.append(pin.__name__)
+        if not failed:
+            survivors.append(name)
+    assert not survivors, f"mutants not caught by any pin: {survivors}"
