@@ -1,0 +1,251 @@
+"""Python binding of libmsa (``include/msa.h``): argument marshalling only.
+
+Every step of the MSA forward pass runs in the HIP kernels of ``libmsa.so``;
+this module checks tensor shapes on the host, hands raw device pointers and
+torch's current HIP stream to the C entry points, and raises on any non-zero
+status.  There is no fallback: without the built library every call raises.
+"""
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmsa.so")
+
+MSA_OK, MSA_ERR_INVALID_ARG, MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE, MSA_ERR_HIP = 0, -1, -2, -3, -4
+F32, BF16 = 0, 1
+SCHED_AUTO, SCHED_KV_OUTER, SCHED_Q_OUTER = 0, 1, 2
+OP_INDEX_TOPK, OP_ATTENTION, OP_FORWARD = 0, 1, 2
+_SCHED = {"auto": SCHED_AUTO, "kv_outer": SCHED_KV_OUTER, "q_outer": SCHED_Q_OUTER}
+
+
+class Problem(ctypes.Structure):
+    """Mirror of msa_problem_t."""
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("n_q", ctypes.c_int32), ("n_k", ctypes.c_int32),
+        ("h_q", ctypes.c_int32), ("h_kv", ctypes.c_int32), ("d", ctypes.c_int32),
+        ("d_idx", ctypes.c_int32), ("block_size", ctypes.c_int32), ("topk", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("q_offset", ctypes.c_int64), ("softmax_scale", ctypes.c_float),
+        ("sched", ctypes.c_int32),
+    ]
+
+
+class MSAError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        msg = f"{what}: {_lib().msa_status_string(status).decode()} ({status})"
+        if status == MSA_ERR_HIP:
+            msg += f", hipError {_lib().msa_last_hip_error()}"
+        super().__init__(msg)
+
+
+_L = None
+
+EXPORTS = ["msa_status_string", "msa_last_hip_error", "msa_validate", "msa_workspace_size", "msa_block_scores",
+           "msa_topk_from_scores", "msa_index_topk", "msa_invert", "msa_sparse_attention", "msa_forward",
+           "msa_profile_enable", "msa_profile_reset", "msa_profile_count", "msa_profile_read"]
+
+
+def _lib():
+    global _L
+    if _L is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m block_sparse_long_bk_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER(Problem)
+        vp, st = ctypes.c_void_p, ctypes.c_int
+        L.msa_status_string.argtypes = [st]
+        L.msa_status_string.restype = ctypes.c_char_p
+        L.msa_last_hip_error.restype = ctypes.c_int
+        L.msa_validate.argtypes = [P]
+        L.msa_workspace_size.argtypes = [P, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t),
+                                         ctypes.POINTER(ctypes.c_size_t)]
+        L.msa_block_scores.argtypes = [P, vp, vp, vp, vp]
+        L.msa_topk_from_scores.argtypes = [P, vp, vp, vp]
+        L.msa_index_topk.argtypes = [P, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.msa_invert.argtypes = [P, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.msa_sparse_attention.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.msa_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.msa_profile_enable.argtypes = [ctypes.c_int]
+        L.msa_profile_count.restype = ctypes.c_int
+        L.msa_profile_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
+                                       ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+        for name in EXPORTS:
+            if name not in ("msa_status_string", "msa_last_hip_error", "msa_profile_count"):
+                getattr(L, name).restype = ctypes.c_int
+        _L = L
+    return _L
+
+
+def lib():
+    """The loaded ctypes handle of libmsa.so."""
+    return _lib()
+
+
+def problem(batch, n_q, n_k, h_q, h_kv, d, d_idx, topk, dtype="bf16", q_offset=0, block_size=128,
+            softmax_scale=0.0, sched="auto"):
+    return Problem(batch, n_q, n_k, h_q, h_kv, d, d_idx, block_size, topk,
+                   BF16 if dtype in ("bf16", torch.bfloat16) else F32, q_offset, softmax_scale,
+                   _SCHED[sched] if isinstance(sched, str) else int(sched))
+
+
+def problem_of(wl, sched="auto", **kw):
+    """Problem for a workload description from ``inputs``."""
+    p = dict(batch=wl.batch, n_q=wl.n_q, n_k=wl.n_k, h_q=wl.h_q, h_kv=wl.h_kv, d=wl.d, d_idx=wl.d_idx,
+             topk=wl.topk, dtype=wl.dtype, q_offset=wl.q_offset, block_size=wl.block_size, sched=sched)
+    p.update(kw)
+    return problem(**p)
+
+
+def nblk(p):
+    return (p.n_k + p.block_size - 1) // p.block_size
+
+
+def _check(rc, what):
+    if rc != MSA_OK:
+        raise MSAError(rc, what)
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _expect(t, shape, dtype, name):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous() or t.device.type != "cuda":
+        raise ValueError(f"{name}: expected contiguous cuda {dtype} {tuple(shape)}, got "
+                         f"{t.device} {t.dtype} {tuple(t.shape)} contiguous={t.is_contiguous()}")
+
+
+def _tdtype(p):
+    return torch.bfloat16 if p.dtype == BF16 else torch.float32
+
+
+def validate(p):
+    return _lib().msa_validate(ctypes.byref(p))
+
+
+def workspace_size(p, op):
+    """(bytes for a single pass, least bytes accepted)."""
+    full, least = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(_lib().msa_workspace_size(ctypes.byref(p), op, ctypes.byref(full), ctypes.byref(least)),
+           "msa_workspace_size")
+    return full.value, least.value
+
+
+def alloc_workspace(p, op, device="cuda", minimal=False):
+    full, least = workspace_size(p, op)
+    n = least if minimal else full
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def _ws(ws):
+    return (_ptr(ws), ws.numel()) if ws is not None else (None, 0)
+
+
+def block_scores(p, iq, ik, scores=None):
+    dt = _tdtype(p)
+    _expect(iq, (p.batch, p.n_q, p.h_kv, p.d_idx), dt, "idx_q")
+    _expect(ik, (p.batch, p.n_k, p.h_kv, p.d_idx), dt, "idx_k")
+    if scores is None:
+        scores = torch.empty((p.batch, p.h_kv, p.n_q, nblk(p)), dtype=torch.float32, device=iq.device)
+    _check(_lib().msa_block_scores(ctypes.byref(p), _ptr(iq), _ptr(ik), _ptr(scores), _stream()), "msa_block_scores")
+    return scores
+
+
+def topk_from_scores(p, scores, ids=None):
+    _expect(scores, (p.batch, p.h_kv, p.n_q, nblk(p)), torch.float32, "scores")
+    if ids is None:
+        ids = torch.empty((p.batch, p.n_q, p.h_kv, p.topk), dtype=torch.int32, device=scores.device)
+    _check(_lib().msa_topk_from_scores(ctypes.byref(p), _ptr(scores), _ptr(ids), _stream()), "msa_topk_from_scores")
+    return ids
+
+
+def index_topk(p, iq, ik, ids=None, ws=None):
+    dt = _tdtype(p)
+    _expect(iq, (p.batch, p.n_q, p.h_kv, p.d_idx), dt, "idx_q")
+    _expect(ik, (p.batch, p.n_k, p.h_kv, p.d_idx), dt, "idx_k")
+    if ids is None:
+        ids = torch.empty((p.batch, p.n_q, p.h_kv, p.topk), dtype=torch.int32, device=iq.device)
+    if ws is None:
+        ws = alloc_workspace(p, OP_INDEX_TOPK, iq.device)
+    wp, wn = _ws(ws)
+    _check(_lib().msa_index_topk(ctypes.byref(p), _ptr(iq), _ptr(ik), _ptr(ids), wp, wn, _stream()), "msa_index_topk")
+    return ids
+
+
+def invert(p, ids, ws=None):
+    """(offsets [B, Hkv, nblk+1], entries [B, Hkv, Nq*topk]) of the block -> query lists."""
+    _expect(ids, (p.batch, p.n_q, p.h_kv, p.topk), torch.int32, "block_ids")
+    offsets = torch.empty((p.batch, p.h_kv, nblk(p) + 1), dtype=torch.int32, device=ids.device)
+    entries = torch.empty((p.batch, p.h_kv, p.n_q * p.topk), dtype=torch.int32, device=ids.device)
+    if ws is None:
+        ws = alloc_workspace(p, OP_ATTENTION, ids.device)
+    wp, wn = _ws(ws)
+    _check(_lib().msa_invert(ctypes.byref(p), _ptr(ids), _ptr(offsets), _ptr(entries), wp, wn, _stream()),
+           "msa_invert")
+    return offsets, entries
+
+
+def sparse_attention(p, q, k, v, ids, out=None, lse=None, want_lse=True, ws=None):
+    dt = _tdtype(p)
+    _expect(q, (p.batch, p.n_q, p.h_q, p.d), dt, "q")
+    _expect(k, (p.batch, p.n_k, p.h_kv, p.d), dt, "k")
+    _expect(v, (p.batch, p.n_k, p.h_kv, p.d), dt, "v")
+    _expect(ids, (p.batch, p.n_q, p.h_kv, p.topk), torch.int32, "block_ids")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((p.batch, p.n_q, p.h_q), dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = alloc_workspace(p, OP_ATTENTION, q.device)
+    wp, wn = _ws(ws)
+    _check(_lib().msa_sparse_attention(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(ids), _ptr(out), _ptr(lse),
+                                       wp, wn, _stream()), "msa_sparse_attention")
+    return out, lse
+
+
+def forward(p, q, k, v, iq, ik, ids=None, out=None, lse=None, want_lse=True, ws=None):
+    dt = _tdtype(p)
+    _expect(q, (p.batch, p.n_q, p.h_q, p.d), dt, "q")
+    _expect(k, (p.batch, p.n_k, p.h_kv, p.d), dt, "k")
+    _expect(v, (p.batch, p.n_k, p.h_kv, p.d), dt, "v")
+    _expect(iq, (p.batch, p.n_q, p.h_kv, p.d_idx), dt, "idx_q")
+    _expect(ik, (p.batch, p.n_k, p.h_kv, p.d_idx), dt, "idx_k")
+    if ids is None:
+        ids = torch.empty((p.batch, p.n_q, p.h_kv, p.topk), dtype=torch.int32, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((p.batch, p.n_q, p.h_q), dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = alloc_workspace(p, OP_FORWARD, q.device)
+    wp, wn = _ws(ws)
+    _check(_lib().msa_forward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(iq), _ptr(ik), _ptr(ids), _ptr(out),
+                              _ptr(lse), wp, wn, _stream()), "msa_forward")
+    return ids, out, lse
+
+
+def profile_enable(on=True):
+    _check(_lib().msa_profile_enable(1 if on else 0), "msa_profile_enable")
+
+
+def profile_reset():
+    _check(_lib().msa_profile_reset(), "msa_profile_reset")
+
+
+def profile_read():
+    """{kernel name: (total ms, launches)} since the last reset."""
+    L = _lib()
+    res = {}
+    for i in range(L.msa_profile_count()):
+        name, ms, n = ctypes.c_char_p(), ctypes.c_double(), ctypes.c_int64()
+        _check(L.msa_profile_read(i, ctypes.byref(name), ctypes.byref(ms), ctypes.byref(n)), "msa_profile_read")
+        res[name.value.decode()] = (ms.value, n.value)
+    return res

@@ -1,0 +1,565 @@
+// attention.hip -- Main Branch of MiniMax Sparse Attention on gfx950.
+//
+// Exact scaled-dot-product softmax attention of every query head over the
+// visible tokens (t <= position) of its GQA group's selected 128-token key
+// blocks (paper summary page, "Method"; zhichai.net write-up, section 2: the
+// heads of a group share the group's blocks but keep their own queries).
+//
+// Both schedules compute, per (query head, selected block), the block's
+// online-softmax partial (max m, sum l, normalised output o = acc/l) and merge
+// the partials of a row with a log-sum-exp combine -- the standard
+// FlashAttention recurrence (cited by the Fireworks note on KV-stationary
+// attention), which is exact up to rounding order.
+//
+//  * k_attn_kvouter -- KV-stationary (the paper's KV-outer path, abstract and
+//    "Key Contributions").  One workgroup per work item (block j, up to 512
+//    (query, head) rows that chose j).  K_j (row-major) and V_j (transposed) are
+//    staged once in LDS; 32-row tiles of the gathered queries stream through
+//        S^T = K_j Q^T      (MFMA: A = K rows from LDS, B = Q rows from HBM)
+//        O^T = V_j^T P^T    (MFMA: A = V^T rows from LDS, B = P from registers)
+//    Computing the transposed products keeps each query row inside one lane
+//    pair, so the softmax is in-register (plus one swap between wave halves)
+//    and P never touches LDS.  Each (query, head, slot) partial has exactly one
+//    writer: no atomics.
+//  * k_attn_qouter -- query-stationary (the baseline schedule of the Fireworks
+//    note, "The design space").  One workgroup per (query, group, split) keeps
+//    the group's query heads resident and walks its selected blocks; the four
+//    waves split each block's 128 keys and merge their states at the end.
+//  * k_combine -- log-sum-exp merge of the partials into the output.
+#include "msa_device.h"
+#include "msa_internal.h"
+
+namespace msa {
+namespace {
+
+template <typename T> struct Pack4;
+template <> struct Pack4<bf16_t> { using type = bf16x4; };
+template <> struct Pack4<float> { using type = f32x4; };
+
+// LDS geometry of one staged key block: K row-major [128][D], V transposed
+// [D][128].  Pitches are padded so the 32 rows read by a half-wave fall on
+// distinct banks.
+template <typename T, int D>
+struct KvLds {
+  static constexpr int KPITCH = D * (int)sizeof(T) + 16;
+  static constexpr int VPITCH = kBk * (int)sizeof(T) + (sizeof(T) == 2 ? 8 : 16);
+  static constexpr int KBYTES = kBk * KPITCH;
+  static constexpr int BYTES = KBYTES + D * VPITCH;
+};
+
+// Stage K_j and V_j^T of one (b, g) into LDS.  256 threads.  Rows past n_k are
+// zero-filled (they are masked anyway).
+template <typename T, int D>
+__device__ __forceinline__ void stage_kv(char* lds, const T* kbase, const T* vbase, int64_t tok_stride, int j,
+                                         int n_k, int tid) {
+  using L = KvLds<T, D>;
+  // K: 16-byte chunks, row-major copy.
+  constexpr int CPR = D * (int)sizeof(T) / 16;
+  constexpr int KCH = kBk * CPR;
+#pragma unroll
+  for (int u = 0; u < (KCH + 255) / 256; ++u) {
+    const int c = tid + u * 256;
+    if (c < KCH) {
+      const int row = c / CPR, col = c % CPR;
+      const int64_t t = (int64_t)j * kBk + row;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (t < n_k) v = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(kbase + t * tok_stride) + col * 16);
+      *reinterpret_cast<uint4*>(lds + row * L::KPITCH + col * 16) = v;
+    }
+  }
+  // V^T: each thread takes 8 d-values of 4 consecutive keys and writes four
+  // keys per transposed row at once.
+  constexpr int DCH = D / 8;             // 8-element chunks per key row
+  constexpr int KG = 256 / DCH;          // key groups of 4 per pass
+  constexpr int PASSES = kBk / (4 * KG);
+  char* vt = lds + L::KBYTES;
+  const int dch = tid % DCH, kg = tid / DCH;
+#pragma unroll
+  for (int ps = 0; ps < PASSES; ++ps) {
+    const int key0 = (ps * KG + kg) * 4;
+    frag_t<T> x[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t t = (int64_t)j * kBk + key0 + r;
+      x[r] = t < n_k ? load8(vbase + t * tok_stride + dch * 8) : zero_frag<T>();
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      typename Pack4<T>::type w;
+      w[0] = x[0][e];
+      w[1] = x[1][e];
+      w[2] = x[2][e];
+      w[3] = x[3][e];
+      *reinterpret_cast<typename Pack4<T>::type*>(vt + (dch * 8 + e) * L::VPITCH + key0 * (int)sizeof(T)) = w;
+    }
+  }
+}
+
+// A fragment of V^T for k-step (mt, a): row d, keys 32mt+16a+4h+[0..3] and +8.
+template <typename T, int D>
+__device__ __forceinline__ frag_t<T> vt_frag(const char* lds, int d, int mt, int a, int half) {
+  using L = KvLds<T, D>;
+  const T* row = reinterpret_cast<const T*>(lds + L::KBYTES + d * L::VPITCH);
+  const int k0 = 32 * mt + 16 * a + 4 * half;
+  const typename Pack4<T>::type lo = *reinterpret_cast<const typename Pack4<T>::type*>(row + k0);
+  const typename Pack4<T>::type hi = *reinterpret_cast<const typename Pack4<T>::type*>(row + k0 + 8);
+  frag_t<T> f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f[e] = lo[e];
+    f[4 + e] = hi[e];
+  }
+  return f;
+}
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) { return static_cast<bf16_t>(x); }
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+
+// One 32-row tile of one key block: S^T = K Q^T, mask, softmax statistics,
+// O^T = V^T P^T.  Lane (c = lane%32, h = lane/32) ends with the tile row c's
+// block max (log2 domain, already scaled) m, sum l, and its 64 of the D output
+// values in o[dt][e] for d = 32dt + 8(e/4) + 4h + e%4.
+template <typename T, int D>
+__device__ __forceinline__ void block_tile(const char* lds, const frag_t<T> (&qf)[D / 16], float c_log2, int64_t key0,
+                                           int64_t vis_end, bool need_mask, float& m, float& l,
+                                           f32x16 (&o)[D / 32]) {
+  using L = KvLds<T, D>;
+  const int lane = threadIdx.x & 63, half = lane >> 5;
+  f32x16 s[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    s[mt] = f32x16{};
+    const T* arow = reinterpret_cast<const T*>(lds + (mt * 32 + (lane & 31)) * L::KPITCH) + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) mma(load8(arow + 16 * ks), qf[ks], s[mt]);
+  }
+  if (need_mask) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t t = key0 + 32 * mt + 8 * (e / 4) + 4 * half + (e % 4);
+        if (t >= vis_end) s[mt][e] = -__builtin_huge_valf();
+      }
+  }
+  float mx = -__builtin_huge_valf();
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) mx = fmaxf(mx, max16(s[mt]));
+  mx = fmaxf(mx, xor_shfl(mx, 32));
+  const float mref = mx == -__builtin_huge_valf() ? 0.f : mx * c_log2;
+  float sum = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float p = exp2_fast(fmaf(s[mt][e], c_log2, -mref));
+      s[mt][e] = p;
+      sum += p;
+    }
+  sum += xor_shfl(sum, 32);
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16{};
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      frag_t<T> pb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pb[e] = from_f32<T>(s[mt][8 * a + e]);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) mma(vt_frag<T, D>(lds, 32 * dt + (lane & 31), mt, a, half), pb, o[dt]);
+    }
+  m = mx == -__builtin_huge_valf() ? -__builtin_huge_valf() : mref;
+  l = sum;
+}
+
+struct KvArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* entries;
+  const int32_t* item_count;
+  const int4* items;
+  float* part_o;
+  float* part_lse;
+  int Nq, Nk, Hq, Hkv, G, topk, S, q0, nq, items_cap;
+  int64_t q_offset;
+  float c_log2;  // softmax scale * log2(e)
+};
+
+template <typename T, int D>
+__global__ void __launch_bounds__(256, 2) k_attn_kvouter(KvArgs a) {
+  using L = KvLds<T, D>;
+  __shared__ __attribute__((aligned(16))) char lds[L::BYTES];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
+  const int bg = blockIdx.y, b = bg / a.Hkv, g = bg % a.Hkv;
+  // Items of one (b, g) are spread so that each XCD (workgroup id mod 8) runs a
+  // contiguous run of them: neighbouring items share their key block in L2.
+  const int n = a.item_count[bg];
+  const int per = (n + 7) / 8;
+  const int x = blockIdx.x;
+  const int item = (x % 8) * per + x / 8;
+  if (x / 8 >= per || item >= n) return;
+  const int4 it = a.items[(int64_t)bg * a.items_cap + item];
+  const int j = it.x, e0 = it.y, e1 = it.z;
+  const int nrows = (e1 - e0) * a.G;
+
+  const int64_t tok_stride = (int64_t)a.Hkv * D;
+  const T* kb = static_cast<const T*>(a.k) + (int64_t)b * a.Nk * tok_stride + g * D;
+  const T* vb = static_cast<const T*>(a.v) + (int64_t)b * a.Nk * tok_stride + g * D;
+  stage_kv<T, D>(lds, kb, vb, tok_stride, j, a.Nk, tid);
+  __syncthreads();
+
+  const int32_t* ent = a.entries + (int64_t)bg * a.nq * a.topk + e0;
+  const T* qbase = static_cast<const T*>(a.q);
+  const int64_t key0 = (int64_t)j * kBk;
+  for (int tile = wave; tile * 32 < nrows; tile += 4) {
+    const int r = tile * 32 + (lane & 31);
+    const bool valid = r < nrows;
+    const int e = valid ? ent[r / a.G] : 0;
+    const int qq = e / a.topk, slot = e % a.topk;  // chunk-relative query, slot
+    const int h = g * a.G + r % a.G;
+    frag_t<T> qf[D / 16];
+    const T* qrow = qbase + (((int64_t)b * a.Nq + a.q0 + qq) * a.Hq + h) * D + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) qf[ks] = valid ? load8(qrow + 16 * ks) : zero_frag<T>();
+    const int64_t pos = a.q_offset + a.q0 + qq;
+    const int64_t vis_end = min(pos + 1, (int64_t)a.Nk);  // keys t < vis_end are visible
+    // Masking is only needed where the block reaches past a row's position.
+    int need = (valid && key0 + kBk > vis_end) ? 1 : 0;
+    need = __any(need);
+    float m, l;
+    f32x16 o[D / 32];
+    block_tile<T, D>(lds, qf, a.c_log2, key0, vis_end, need != 0, m, l, o);
+    if (valid) {
+      const int64_t prow = (((int64_t)b * a.nq + qq) * a.Hq + h) * a.S + slot;
+      float* po = a.part_o + prow * D;
+      const float inv = 1.f / l;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          f32x4 w;
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) w[rr] = o[dt][4 * i + rr] * inv;
+          *reinterpret_cast<f32x4*>(po + 32 * dt + 8 * i + 4 * half) = w;
+        }
+      if (half == 0) a.part_lse[prow] = (m + log2_fast(l)) * kLn2;
+    }
+  }
+}
+
+struct QoArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* ids;
+  void* out;
+  float* lse;
+  float* part_o;
+  float* part_lse;
+  int Nq, Nk, Hq, Hkv, G, topk, nsplit, q0, nq;
+  int64_t q_offset;
+  float c_log2;
+};
+
+// grid: x = nq * Hkv, y = nsplit, z = B.  256 threads; wave w owns keys
+// [32w, 32w + 32) of every block.
+template <typename T, int D>
+__global__ void __launch_bounds__(256, 2) k_attn_qouter(QoArgs a) {
+  using L = KvLds<T, D>;
+  __shared__ __attribute__((aligned(16))) char lds[L::BYTES];
+  __shared__ float stat[4][2][32];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
+  const int qq = blockIdx.x / a.Hkv, g = blockIdx.x % a.Hkv;
+  const int split = blockIdx.y, b = blockIdx.z;
+  const int64_t qglob = (int64_t)a.q0 + qq;
+  const int64_t pos = a.q_offset + qglob;
+  const int64_t vis_end = min(pos + 1, (int64_t)a.Nk);
+  const int per = (a.topk + a.nsplit - 1) / a.nsplit;
+  const int s0 = split * per, s1 = min(a.topk, s0 + per);
+
+  const int c = lane & 31;
+  const bool valid = c < a.G;
+  const int h = g * a.G + (valid ? c : 0);
+  const T* qrow = static_cast<const T*>(a.q) + ((((int64_t)b * a.Nq + qglob) * a.Hq + h) * D) + 8 * half;
+  frag_t<T> qf[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) qf[ks] = valid ? load8(qrow + 16 * ks) : zero_frag<T>();
+
+  const int64_t tok_stride = (int64_t)a.Hkv * D;
+  const T* kb = static_cast<const T*>(a.k) + (int64_t)b * a.Nk * tok_stride + g * D;
+  const T* vb = static_cast<const T*>(a.v) + (int64_t)b * a.Nk * tok_stride + g * D;
+  const int32_t* sel = a.ids + ((((int64_t)b * a.Nq + qglob) * a.Hkv) + g) * a.topk;
+
+  float m = -__builtin_huge_valf(), l = 0.f;
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16{};
+
+  for (int s = s0; s < s1; ++s) {
+    const int j = sel[s];
+    if (j < 0) continue;  // uniform across the workgroup
+    __syncthreads();
+    stage_kv<T, D>(lds, kb, vb, tok_stride, j, a.Nk, tid);
+    __syncthreads();
+    // wave's 32 keys: S^T tile for M-tile `wave`
+    f32x16 sc = f32x16{};
+    const T* arow = reinterpret_cast<const T*>(lds + (wave * 32 + c) * L::KPITCH) + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) mma(load8(arow + 16 * ks), qf[ks], sc);
+    const int64_t kbase = (int64_t)j * kBk + wave * 32;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int64_t t = kbase + 8 * (e / 4) + 4 * half + (e % 4);
+      if (t >= vis_end) sc[e] = -__builtin_huge_valf();
+    }
+    float mx = max16(sc);
+    mx = fmaxf(mx, xor_shfl(mx, 32));
+    const float mnew = fmaxf(m, mx == -__builtin_huge_valf() ? -__builtin_huge_valf() : mx * a.c_log2);
+    const float mref = mnew == -__builtin_huge_valf() ? 0.f : mnew;
+    const float alpha = exp2_fast(m - mref);
+    float sum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float p = exp2_fast(fmaf(sc[e], a.c_log2, -mref));
+      sc[e] = p;
+      sum += p;
+    }
+    sum += xor_shfl(sum, 32);
+    l = l * alpha + sum;
+    m = mnew;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
+#pragma unroll
+    for (int aa = 0; aa < 2; ++aa) {
+      frag_t<T> pb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pb[e] = from_f32<T>(sc[8 * aa + e]);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) mma(vt_frag<T, D>(lds, 32 * dt + c, wave, aa, half), pb, o[dt]);
+    }
+  }
+  // Merge the four waves' states through LDS (reusing the staging area).
+  __syncthreads();
+  float* ob = reinterpret_cast<float*>(lds);  // [4 waves][D][32]
+  if (half == 0) {
+    stat[wave][0][c] = m;
+    stat[wave][1][c] = l;
+  }
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int d = 32 * dt + 8 * (e / 4) + 4 * half + (e % 4);
+      ob[(wave * D + d) * 32 + c] = o[dt][e];
+    }
+  __syncthreads();
+  // threads: row c2 = tid % 32, d-range split over tid / 32 (8 groups)
+  const int c2 = tid & 31, dg = tid >> 5;
+  if (c2 < a.G) {
+    float M = -__builtin_huge_valf();
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, stat[w][0][c2]);
+    const float Mref = M == -__builtin_huge_valf() ? 0.f : M;
+    float wgt[4], Ls = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      wgt[w] = exp2_fast(stat[w][0][c2] - Mref);
+      Ls += wgt[w] * stat[w][1][c2];
+    }
+    const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+    const int h2 = g * a.G + c2;
+    const float lse_v = Ls > 0.f ? (M + log2_fast(Ls)) * kLn2 : -__builtin_huge_valf();
+    constexpr int DPG = D / 8;
+    if (a.nsplit == 1) {
+      T* orow = static_cast<T*>(a.out) + (((int64_t)b * a.Nq + qglob) * a.Hq + h2) * D;
+      for (int d = dg * DPG; d < (dg + 1) * DPG; ++d) {
+        float acc = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) acc += wgt[w] * ob[(w * D + d) * 32 + c2];
+        orow[d] = from_f32<T>(acc * inv);
+      }
+      if (dg == 0 && a.lse) a.lse[((int64_t)b * a.Nq + qglob) * a.Hq + h2] = lse_v;
+    } else {
+      const int64_t prow = (((int64_t)b * a.nq + qq) * a.Hq + h2) * a.nsplit + split;
+      float* po = a.part_o + prow * D;
+      for (int d = dg * DPG; d < (dg + 1) * DPG; ++d) {
+        float acc = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) acc += wgt[w] * ob[(w * D + d) * 32 + c2];
+        po[d] = acc * inv;
+      }
+      if (dg == 0) a.part_lse[prow] = lse_v;
+    }
+  }
+}
+
+struct CombArgs {
+  const float* part_o;
+  const float* part_lse;
+  const int32_t* ids;
+  void* out;
+  float* lse;
+  int Nq, Hq, Hkv, G, topk, S, q0, nq, ids_slots;
+};
+
+// One wave per (b, query, head): merge its S partials.
+template <typename T, int D>
+__global__ void __launch_bounds__(256) k_combine(CombArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (b, qq, h)
+  const int b = blockIdx.y;
+  if (row >= (int64_t)a.nq * a.Hq) return;
+  const int qq = (int)(row / a.Hq), h = (int)(row % a.Hq), g = h / a.G;
+  const int64_t prow = ((int64_t)b * a.nq + qq) * a.Hq + h;
+  const int32_t* sel = a.ids + (((int64_t)b * a.Nq + a.q0 + qq) * a.Hkv + g) * a.topk;
+  // slot statistics: lane s < S holds slot s
+  float ls = -__builtin_huge_valf();
+  if (lane < a.S) {
+    const bool ok = a.ids_slots ? (sel[lane] >= 0) : true;
+    if (ok) ls = a.part_lse[prow * a.S + lane];
+  }
+  float M = ls;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, xor_shfl(M, m));
+  const float Mref = M == -__builtin_huge_valf() ? 0.f : M;
+  const float w = ls == -__builtin_huge_valf() ? 0.f : exp2_fast((ls - Mref) * kLog2e);
+  float W = w;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) W += xor_shfl(W, m);
+  constexpr int VPL = D / 64;  // values per lane
+  float acc[VPL];
+#pragma unroll
+  for (int u = 0; u < VPL; ++u) acc[u] = 0.f;
+  const float* po = a.part_o + prow * a.S * D;
+  for (int s = 0; s < a.S; ++s) {
+    const float ws = __shfl(w, s, 64);
+    if (ws != 0.f) {
+#pragma unroll
+      for (int u = 0; u < VPL; ++u) acc[u] = fmaf(ws, po[(int64_t)s * D + lane * VPL + u], acc[u]);
+    }
+  }
+  const float inv = W > 0.f ? 1.f / W : 0.f;
+  T* orow = static_cast<T*>(a.out) + (((int64_t)b * a.Nq + a.q0 + qq) * a.Hq + h) * D;
+#pragma unroll
+  for (int u = 0; u < VPL; ++u) orow[lane * VPL + u] = from_f32<T>(acc[u] * inv);
+  if (lane == 0 && a.lse)
+    a.lse[((int64_t)b * a.Nq + a.q0 + qq) * a.Hq + h] = W > 0.f ? M + log2_fast(W) * kLn2 : -__builtin_huge_valf();
+}
+
+}  // namespace
+
+hipError_t launch_attn_kvouter(const Shape& s, const InvertPlan& p, int q0, int nq, const void* q, const void* k,
+                               const void* v, const InvertOut& inv, Partials part, hipStream_t st) {
+  static const int kid = prof_register("attn_kvouter");
+  KvArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.entries = inv.entries;
+  a.item_count = inv.item_count;
+  a.items = inv.items;
+  a.part_o = part.o;
+  a.part_lse = part.lse;
+  a.Nq = s.Nq;
+  a.Nk = s.Nk;
+  a.Hq = s.Hq;
+  a.Hkv = s.Hkv;
+  a.G = s.Hq / s.Hkv;
+  a.topk = s.topk;
+  a.S = part.S;
+  a.q0 = q0;
+  a.nq = nq;
+  a.items_cap = p.items_cap;
+  a.q_offset = s.q_offset;
+  a.c_log2 = s.scale * kLog2e;
+  const dim3 grid(p.items_cap, s.B * s.Hkv);
+  prof_begin(st, kid);
+  if (s.dtype == kBF16) {
+    if (s.D == 64) hipLaunchKernelGGL((k_attn_kvouter<bf16_t, 64>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((k_attn_kvouter<bf16_t, 128>), grid, dim3(256), 0, st, a);
+  } else {
+    if (s.D == 64) hipLaunchKernelGGL((k_attn_kvouter<float, 64>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((k_attn_kvouter<float, 128>), grid, dim3(256), 0, st, a);
+  }
+  const hipError_t e = hipGetLastError();
+  prof_end(st, kid);
+  return e;
+}
+
+hipError_t launch_attn_qouter(const Shape& s, int q0, int nq, int nsplit, const void* q, const void* k,
+                              const void* v, const int32_t* ids, void* out, float* lse, Partials part,
+                              hipStream_t st) {
+  static const int kid = prof_register("attn_qouter");
+  QoArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.ids = ids;
+  a.out = out;
+  a.lse = lse;
+  a.part_o = part.o;
+  a.part_lse = part.lse;
+  a.Nq = s.Nq;
+  a.Nk = s.Nk;
+  a.Hq = s.Hq;
+  a.Hkv = s.Hkv;
+  a.G = s.Hq / s.Hkv;
+  a.topk = s.topk;
+  a.nsplit = nsplit;
+  a.q0 = q0;
+  a.nq = nq;
+  a.q_offset = s.q_offset;
+  a.c_log2 = s.scale * kLog2e;
+  const dim3 grid(nq * s.Hkv, nsplit, s.B);
+  prof_begin(st, kid);
+  if (s.dtype == kBF16) {
+    if (s.D == 64) hipLaunchKernelGGL((k_attn_qouter<bf16_t, 64>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((k_attn_qouter<bf16_t, 128>), grid, dim3(256), 0, st, a);
+  } else {
+    if (s.D == 64) hipLaunchKernelGGL((k_attn_qouter<float, 64>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((k_attn_qouter<float, 128>), grid, dim3(256), 0, st, a);
+  }
+  const hipError_t e = hipGetLastError();
+  prof_end(st, kid);
+  return e;
+}
+
+hipError_t launch_combine(const Shape& s, int q0, int nq, const Partials& part, const int32_t* ids,
+                          bool ids_slots, void* out, float* lse, hipStream_t st) {
+  static const int kid = prof_register("combine");
+  CombArgs a;
+  a.part_o = part.o;
+  a.part_lse = part.lse;
+  a.ids = ids;
+  a.out = out;
+  a.lse = lse;
+  a.Nq = s.Nq;
+  a.Hq = s.Hq;
+  a.Hkv = s.Hkv;
+  a.G = s.Hq / s.Hkv;
+  a.topk = s.topk;
+  a.S = part.S;
+  a.q0 = q0;
+  a.nq = nq;
+  a.ids_slots = ids_slots ? 1 : 0;
+  const int64_t rows = (int64_t)nq * s.Hq;
+  const dim3 grid((unsigned)((rows + 3) / 4), s.B);
+  prof_begin(st, kid);
+  if (s.dtype == kBF16) {
+    if (s.D == 64) hipLaunchKernelGGL((k_combine<bf16_t, 64>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((k_combine<bf16_t, 128>), grid, dim3(256), 0, st, a);
+  } else {
+    if (s.D == 64) hipLaunchKernelGGL((k_combine<float, 64>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((k_combine<float, 128>), grid, dim3(256), 0, st, a);
+  }
+  const hipError_t e = hipGetLastError();
+  prof_end(st, kid);
+  return e;
+}
+
+}  // namespace msa

@@ -1,0 +1,352 @@
+// index.hip -- Index Branch of MiniMax Sparse Attention on gfx950.
+//
+// Block score of key block j for query i of GQA group g (paper summary page,
+// "Method"; zhichai.net write-up, section 2: one index-q and one index-k head
+// per group):
+//     S[b,g,i,j] = max_{t in block j} <idx_q[b,i,g,:], idx_k[b,t,g,:]>
+// for the candidate blocks j < L(i) = floor((q_offset + i) / 128), followed by
+// an exp-free Top-(k-1) that always adds the local block L(i) (write-up,
+// section 4.1: only the order of the scores matters, so no exponential).
+//
+// Two kernels:
+//  * k_index_tile -- prefill.  A workgroup owns 512 consecutive queries of one
+//    group (their index queries stay in VGPRs as the MFMA B operand) and sweeps
+//    the candidate key blocks in order.  Each 128 x d_idx key block is staged
+//    once in LDS (double buffered) and multiplied on the matrix cores as
+//    S^T = K_blk * Q^T, so each lane's accumulators hold one query's scores for
+//    16 keys and the max pool is an in-register max plus one lane swap.  The
+//    token scores never leave registers; the block score goes straight into the
+//    lane's running Top-k list, so the score matrix never reaches HBM.
+//  * k_index_scan -- decode / few queries.  Streams idx_k block by block (each
+//    128-token block of all groups is one contiguous span), VALU dot products
+//    against the few index queries kept in LDS; writes block scores, which
+//    k_topk_rows then selects from.
+#include "msa_device.h"
+#include "msa_internal.h"
+
+namespace msa {
+namespace {
+
+struct TileArgs {
+  const void* iq;
+  const void* ik;
+  int32_t* ids;
+  float* scores;
+  int Nq, Nk, Hkv, topk, nblk, n_tiles;
+  int64_t q_offset;
+};
+
+constexpr int kTileWaves = 8;
+
+template <typename T, int DI, int NT, int KMAX, bool WRITE_S, bool TOPK>
+__global__ void __launch_bounds__(kTileWaves * 64) k_index_tile(TileArgs a) {
+  constexpr int WAVES = kTileWaves;
+  constexpr int TQ = WAVES * NT * 32;  // queries per workgroup
+  constexpr int ROW_BYTES = DI * (int)sizeof(T);
+  constexpr int PITCH = ROW_BYTES + 16;  // padded LDS row: conflict-free 16-byte reads
+  constexpr int KSTEPS = DI / 16;
+  constexpr int CPR = ROW_BYTES / 16;  // 16-byte chunks per key row
+  constexpr int CHUNKS = kBk * CPR;
+  constexpr int NTHR = WAVES * 64;
+  constexpr int LOADS = (CHUNKS + NTHR - 1) / NTHR;
+  __shared__ __attribute__((aligned(16))) char lds[2][kBk * PITCH];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
+  const int g = blockIdx.x % a.Hkv;
+  const int tile = a.n_tiles - 1 - (int)(blockIdx.x / a.Hkv);  // heaviest tiles first
+  const int b = blockIdx.y;
+  const int q0 = tile * TQ;
+  const int q_last = min(q0 + TQ, a.Nq) - 1;
+  const int j_end = (int)((a.q_offset + q_last) / kBk);
+
+  const T* iq = static_cast<const T*>(a.iq);
+  const int64_t krow = (int64_t)a.Hkv * DI;  // elements between consecutive tokens
+  const char* ikb = reinterpret_cast<const char*>(static_cast<const T*>(a.ik) + (int64_t)b * a.Nk * krow + g * DI);
+
+  // Index queries of this wave as B operands: column = query, k = d_idx.
+  frag_t<T> bq[NT][KSTEPS];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int q = q0 + wave * NT * 32 + nt * 32 + (lane & 31);
+    const T* p = iq + (((int64_t)b * a.Nq + q) * a.Hkv + g) * DI + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) bq[nt][ks] = q < a.Nq ? load8(p + 16 * ks) : zero_frag<T>();
+  }
+
+  // Query owned by this lane after the max-pool exchange.
+  const int q_own = q0 + wave * NT * 32 + (NT == 2 ? lane : (lane & 31));
+  const bool own_valid = q_own < a.Nq && (NT == 2 || half == 0);
+  const int L_own = own_valid ? (int)((a.q_offset + q_own) / kBk) : 0;
+
+  TopList<KMAX> list;
+  list.init();
+
+  if (j_end > 0) {
+    uint4 stage[LOADS];
+    auto gload = [&](int j) {
+#pragma unroll
+      for (int u = 0; u < LOADS; ++u) {
+        const int c = tid + u * NTHR;
+        if (c < CHUNKS) {
+          const int row = c / CPR, col = c % CPR;
+          stage[u] = *reinterpret_cast<const uint4*>(ikb + ((int64_t)j * kBk + row) * krow * (int64_t)sizeof(T) + col * 16);
+        }
+      }
+    };
+    auto lstore = [&](int buf) {
+#pragma unroll
+      for (int u = 0; u < LOADS; ++u) {
+        const int c = tid + u * NTHR;
+        if (c < CHUNKS) {
+          const int row = c / CPR, col = c % CPR;
+          *reinterpret_cast<uint4*>(&lds[buf][row * PITCH + col * 16]) = stage[u];
+        }
+      }
+    };
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    for (int j = 0; j < j_end; ++j) {
+      const int cur = j & 1;
+      if (j + 1 < j_end) gload(j + 1);
+      float run[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) run[nt] = -__builtin_huge_valf();
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        f32x16 acc[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x16{};
+        const T* arow = reinterpret_cast<const T*>(&lds[cur][(mt * 32 + (lane & 31)) * PITCH]) + 8 * half;
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+          const frag_t<T> A = load8(arow + 16 * ks);
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) mma(A, bq[nt][ks], acc[nt]);
+        }
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) run[nt] = fmaxf(run[nt], max16(acc[nt]));
+      }
+      // Each half of the wave saw 64 of the 128 keys; swap halves so that lane l
+      // ends with the full block max of query q0 + wave*NT*32 + l.
+      float own;
+      if (NT == 2) {
+        const float give = half ? run[0] : run[1];
+        own = fmaxf(half ? run[1] : run[0], xor_shfl(give, 32));
+      } else {
+        own = fmaxf(run[0], xor_shfl(run[0], 32));
+      }
+      if (j < L_own) {
+        if (TOPK) list.offer(own, j);
+        if (WRITE_S) a.scores[(((int64_t)b * a.Hkv + g) * a.Nq + q_own) * a.nblk + j] = own;
+      }
+      if (j + 1 < j_end) lstore(cur ^ 1);
+      __syncthreads();
+    }
+  }
+  if (TOPK && own_valid) {
+    int cand[KMAX];
+#pragma unroll
+    for (int p = 0; p < KMAX; ++p) cand[p] = list.j[p];
+    const int nsel = min(a.topk - 1, L_own);
+    write_selection<KMAX>(cand, nsel, L_own, a.topk, a.ids + (((int64_t)b * a.Nq + q_own) * a.Hkv + g) * a.topk);
+  }
+}
+
+struct ScanArgs {
+  const void* iq;
+  const void* ik;
+  float* scores;
+  int Nq, Nk, Hkv, nblk, blocks_per_wg, j_end;
+  int64_t q_offset;
+};
+
+constexpr int kScanThreads = 256;
+constexpr int kScanUnroll = 8;
+
+// One workgroup scores `blocks_per_wg` consecutive key blocks of one batch
+// entry for every group and every query (Nq <= NQ).
+template <typename T, int DI, int NQ>
+__global__ void __launch_bounds__(kScanThreads) k_index_scan(ScanArgs a) {
+  constexpr int C = DI / 8;                      // lanes per (token, group) row
+  constexpr int ROWS_IT = kScanThreads / C;      // rows per sweep of the workgroup
+  extern __shared__ __attribute__((aligned(16))) float smem[];
+  float* qs = smem;                              // [NQ][Hkv][DI] index queries (fp32)
+  float* dots = smem + NQ * a.Hkv * DI;          // [NQ][Hkv][128] token scores of one block
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = blockIdx.y;
+  const int H = a.Hkv;
+  const T* iq = static_cast<const T*>(a.iq);
+  const T* ik = static_cast<const T*>(a.ik);
+  for (int e = tid; e < a.Nq * H * DI; e += kScanThreads)
+    qs[e] = to_f32(iq[(int64_t)b * a.Nq * H * DI + e]);
+  __syncthreads();
+
+  const int c = tid % C, rsub = tid / C;
+  const int rows = kBk * H;
+  const int iters = rows / ROWS_IT;  // H * DI / 16 (exact: 128*8 divisible by C)
+  const int jb = blockIdx.x * a.blocks_per_wg;
+  const int je = min(jb + a.blocks_per_wg, a.j_end);
+  for (int j = jb; j < je; ++j) {
+    const T* blk = ik + ((int64_t)b * a.Nk + (int64_t)j * kBk) * H * DI;
+    for (int it0 = 0; it0 < iters; it0 += kScanUnroll) {
+      frag_t<T> x[kScanUnroll];
+#pragma unroll
+      for (int u = 0; u < kScanUnroll; ++u) {
+        const int row = (it0 + u) * ROWS_IT + rsub;
+        x[u] = (it0 + u < iters) ? load8(blk + (int64_t)row * DI + c * 8) : zero_frag<T>();
+      }
+#pragma unroll
+      for (int u = 0; u < kScanUnroll; ++u) {
+        const int row = (it0 + u) * ROWS_IT + rsub;
+        const int tok = row / H, grp = row % H;
+#pragma unroll
+        for (int qi = 0; qi < NQ; ++qi) {
+          if (qi < a.Nq) {
+            const float* qv = qs + (qi * H + grp) * DI + c * 8;
+            float acc = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc = fmaf(to_f32(x[u][e]), qv[e], acc);
+#pragma unroll
+            for (int m = C / 2; m >= 1; m >>= 1) acc += xor_shfl(acc, m);
+            if (c == 0 && it0 + u < iters) dots[(qi * H + grp) * kBk + tok] = acc;
+          }
+        }
+      }
+    }
+    __syncthreads();
+    // max over the 128 tokens of block j for every (query, group)
+    for (int r = wave; r < a.Nq * H; r += kScanThreads / 64) {
+      float m = fmaxf(dots[r * kBk + lane], dots[r * kBk + 64 + lane]);
+#pragma unroll
+      for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, xor_shfl(m, s));
+      const int qi = r / H, grp = r % H;
+      const int L = (int)((a.q_offset + qi) / kBk);
+      if (lane == 0 && j < L) a.scores[(((int64_t)b * H + grp) * a.Nq + qi) * a.nblk + j] = m;
+    }
+    __syncthreads();
+  }
+}
+
+__global__ void k_fill_neg_inf(float* p, size_t n) {
+  for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (size_t)gridDim.x * blockDim.x)
+    p[e] = -__builtin_huge_valf();
+}
+
+template <typename T, int DI, bool WRITE_S, bool TOPK>
+hipError_t tile_dispatch(const Shape& s, const TileArgs& a, dim3 grid, hipStream_t st) {
+  constexpr int NT = (DI * (int)sizeof(T) <= 256) ? 2 : 1;
+  const int kneed = s.topk - 1;
+  if (!TOPK || kneed <= 8) {
+    hipLaunchKernelGGL((k_index_tile<T, DI, NT, 8, WRITE_S, TOPK>), grid, dim3(kTileWaves * 64), 0, st, a);
+  } else if (kneed <= 16) {
+    hipLaunchKernelGGL((k_index_tile<T, DI, NT, 16, WRITE_S, TOPK>), grid, dim3(kTileWaves * 64), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((k_index_tile<T, DI, NT, 32, WRITE_S, TOPK>), grid, dim3(kTileWaves * 64), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+template <typename T, bool WRITE_S, bool TOPK>
+hipError_t tile_dispatch_di(const Shape& s, const TileArgs& a, dim3 grid, hipStream_t st) {
+  switch (s.DI) {
+    case 32: return tile_dispatch<T, 32, WRITE_S, TOPK>(s, a, grid, st);
+    case 64: return tile_dispatch<T, 64, WRITE_S, TOPK>(s, a, grid, st);
+    default: return tile_dispatch<T, 128, WRITE_S, TOPK>(s, a, grid, st);
+  }
+}
+
+template <typename T, int DI>
+hipError_t scan_dispatch(const Shape& s, const ScanArgs& a, dim3 grid, hipStream_t st) {
+  const int nq = s.Nq <= 1 ? 1 : s.Nq <= 2 ? 2 : s.Nq <= 4 ? 4 : 8;
+  const size_t shm_q = (size_t)nq * s.Hkv * (DI + kBk) * sizeof(float);
+  if (s.Nq <= 1) hipLaunchKernelGGL((k_index_scan<T, DI, 1>), grid, dim3(kScanThreads), shm_q, st, a);
+  else if (s.Nq <= 2) hipLaunchKernelGGL((k_index_scan<T, DI, 2>), grid, dim3(kScanThreads), shm_q, st, a);
+  else if (s.Nq <= 4) hipLaunchKernelGGL((k_index_scan<T, DI, 4>), grid, dim3(kScanThreads), shm_q, st, a);
+  else hipLaunchKernelGGL((k_index_scan<T, DI, 8>), grid, dim3(kScanThreads), shm_q, st, a);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t scan_dispatch_di(const Shape& s, const ScanArgs& a, dim3 grid, hipStream_t st) {
+  switch (s.DI) {
+    case 32: return scan_dispatch<T, 32>(s, a, grid, st);
+    case 64: return scan_dispatch<T, 64>(s, a, grid, st);
+    default: return scan_dispatch<T, 128>(s, a, grid, st);
+  }
+}
+
+constexpr int kScanMaxQueries = 8;
+
+}  // namespace
+
+bool index_use_tile(const Shape& s) { return s.Nq > kScanMaxQueries; }
+
+static int tile_queries(const Shape& s) {
+  const int NT = (s.DI * (s.dtype == kBF16 ? 2 : 4) <= 256) ? 2 : 1;
+  return kTileWaves * NT * 32;
+}
+
+hipError_t launch_index_tile(const Shape& s, const void* iq, const void* ik, int32_t* ids, float* scores,
+                             hipStream_t st) {
+  static const int kid_topk = prof_register("index_tile_topk");
+  static const int kid_scores = prof_register("index_tile_scores");
+  const int kid = ids ? kid_topk : kid_scores;
+  TileArgs a;
+  a.iq = iq;
+  a.ik = ik;
+  a.ids = ids;
+  a.scores = scores;
+  a.Nq = s.Nq;
+  a.Nk = s.Nk;
+  a.Hkv = s.Hkv;
+  a.topk = s.topk;
+  a.nblk = s.nblk;
+  a.n_tiles = (s.Nq + tile_queries(s) - 1) / tile_queries(s);
+  a.q_offset = s.q_offset;
+  const dim3 grid(a.n_tiles * s.Hkv, s.B);
+  prof_begin(st, kid);
+  hipError_t e;
+  if (s.dtype == kBF16)
+    e = ids ? tile_dispatch_di<bf16_t, false, true>(s, a, grid, st) : tile_dispatch_di<bf16_t, true, false>(s, a, grid, st);
+  else
+    e = ids ? tile_dispatch_di<float, false, true>(s, a, grid, st) : tile_dispatch_di<float, true, false>(s, a, grid, st);
+  prof_end(st, kid);
+  return e;
+}
+
+hipError_t launch_index_scan(const Shape& s, const void* iq, const void* ik, float* scores, hipStream_t st) {
+  static const int kid = prof_register("index_scan");
+  if (s.Nq > kScanMaxQueries) return hipErrorInvalidValue;
+  ScanArgs a;
+  a.iq = iq;
+  a.ik = ik;
+  a.scores = scores;
+  a.Nq = s.Nq;
+  a.Nk = s.Nk;
+  a.Hkv = s.Hkv;
+  a.nblk = s.nblk;
+  a.q_offset = s.q_offset;
+  a.j_end = (int)((s.q_offset + s.Nq - 1) / kBk);  // candidates of the last query
+  if (a.j_end <= 0) return hipSuccess;
+  a.blocks_per_wg = 2;
+  const dim3 grid((a.j_end + a.blocks_per_wg - 1) / a.blocks_per_wg, s.B);
+  prof_begin(st, kid);
+  const hipError_t e = s.dtype == kBF16 ? scan_dispatch_di<bf16_t>(s, a, grid, st) : scan_dispatch_di<float>(s, a, grid, st);
+  prof_end(st, kid);
+  return e;
+}
+
+hipError_t launch_fill_neg_inf(float* p, size_t n, hipStream_t st) {
+  static const int kid = prof_register("fill_neg_inf");
+  if (n == 0) return hipSuccess;
+  const size_t blocks = std::min<size_t>((n + 255) / 256, 65536);
+  prof_begin(st, kid);
+  hipLaunchKernelGGL(k_fill_neg_inf, dim3((unsigned)blocks), dim3(256), 0, st, p, n);
+  const hipError_t e = hipGetLastError();
+  prof_end(st, kid);
+  return e;
+}
+
+}  // namespace msa

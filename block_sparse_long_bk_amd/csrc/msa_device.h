@@ -1,0 +1,160 @@
+// msa_device.h -- device-side building blocks shared by the MSA kernels
+// (gfx950 / CDNA4, wave64).
+//
+// MFMA operand layout used throughout (v_mfma_f32_32x32x16_bf16, and eight
+// v_mfma_f32_32x32x2_f32 issued back to back for fp32 inputs):
+//   A (32 x 16): lane l holds row l%32, k = 8*(l/32) + e, e = 0..7
+//   B (16 x 32): lane l holds col l%32, k = 8*(l/32) + e
+//   C (32 x 32): lane l holds col l%32, rows 8*(e/4) + 4*(l/32) + e%4, e = 0..15
+// For fp32 the eight 32x32x2 steps take element e of A and B in step e; any
+// fixed assignment of the 16 k-values works as long as A and B agree.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msa {
+
+typedef __bf16 bf16_t;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(8 * sizeof(float)))) float f32x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+constexpr int kBk = 128;        // key block size (tokens)
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <typename T> struct FragOf;
+template <> struct FragOf<bf16_t> { using type = bf16x8; };
+template <> struct FragOf<float> { using type = f32x8; };
+// Eight consecutive k-values of one MFMA operand row/column.
+template <typename T> using frag_t = typename FragOf<T>::type;
+
+__device__ __forceinline__ void mma(const bf16x8& a, const bf16x8& b, f32x16& c) {
+  c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(const f32x8& a, const f32x8& b, f32x16& c) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], b[e], c, 0, 0, 0);
+}
+
+// 8 elements from a 16-byte aligned address (global or LDS).
+__device__ __forceinline__ bf16x8 load8(const bf16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
+__device__ __forceinline__ f32x8 load8(const float* p) {
+  const f32x4 lo = *reinterpret_cast<const f32x4*>(p);
+  const f32x4 hi = *reinterpret_cast<const f32x4*>(p + 4);
+  return f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+template <typename T> __device__ __forceinline__ frag_t<T> zero_frag() { return frag_t<T>{}; }
+
+__device__ __forceinline__ float to_f32(bf16_t x) { return static_cast<float>(x); }
+__device__ __forceinline__ float to_f32(float x) { return x; }
+
+// Hardware base-2 exponential / logarithm (v_exp_f32, v_log_f32).
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ float max16(const f32x16& v) {
+  float m = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+  m = fmaxf(m, fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
+  m = fmaxf(m, fmaxf(fmaxf(v[8], v[9]), fmaxf(v[10], v[11])));
+  m = fmaxf(m, fmaxf(fmaxf(v[12], v[13]), fmaxf(v[14], v[15])));
+  return m;
+}
+
+__device__ __forceinline__ float xor_shfl(float v, int mask) { return __shfl_xor(v, mask, kWave); }
+__device__ __forceinline__ int xor_shfl(int v, int mask) { return __shfl_xor(v, mask, kWave); }
+
+// Per-lane list of the KMAX best (score, block id) pairs seen so far, best
+// first; order = score descending, id ascending.  Ids must be offered in
+// increasing order, so a newcomer only passes an entry with a strictly lower
+// score (equal scores keep the earlier, lower id in front).  Empty slots hold
+// (-inf, INT32_MAX); only finite scores are ever admitted.
+template <int KMAX>
+struct TopList {
+  float s[KMAX];
+  int j[KMAX];
+
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int p = 0; p < KMAX; ++p) {
+      s[p] = -__builtin_huge_valf();
+      j[p] = INT32_MAX;
+    }
+  }
+
+  __device__ __forceinline__ void offer(float x, int id) {
+    if (x > s[KMAX - 1]) {
+      s[KMAX - 1] = x;
+      j[KMAX - 1] = id;
+#pragma unroll
+      for (int p = KMAX - 1; p > 0; --p) {
+        const bool up = s[p] > s[p - 1];
+        const float ts = s[p], tp = s[p - 1];
+        const int js = j[p], jp = j[p - 1];
+        s[p - 1] = up ? ts : tp;
+        s[p] = up ? tp : ts;
+        j[p - 1] = up ? js : jp;
+        j[p] = up ? jp : js;
+      }
+    }
+  }
+
+  // Drop the front entry (used by the wave-level merge).
+  __device__ __forceinline__ void pop() {
+#pragma unroll
+    for (int p = 0; p < KMAX - 1; ++p) {
+      s[p] = s[p + 1];
+      j[p] = j[p + 1];
+    }
+    s[KMAX - 1] = -__builtin_huge_valf();
+    j[KMAX - 1] = INT32_MAX;
+  }
+};
+
+// Sort N ints ascending in registers (bitonic network; N a power of two).
+template <int N>
+__device__ __forceinline__ void sort_asc(int (&a)[N]) {
+#pragma unroll
+  for (int size = 2; size <= N; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const int p = i ^ stride;
+        if (p > i) {
+          const bool asc = (i & size) == 0;
+          const int x = a[i], y = a[p];
+          const bool sw = asc ? (x > y) : (x < y);
+          a[i] = sw ? y : x;
+          a[p] = sw ? x : y;
+        }
+      }
+    }
+  }
+}
+
+// Write one selection row: the first `nsel` (<= k-1) ids of `cand` (KMAX
+// entries; unused ones are INT32_MAX), then the local block L, then -1 up to
+// topk.  `cand` is sorted here.  All candidate ids are < L.
+template <int KMAX>
+__device__ __forceinline__ void write_selection(int (&cand)[KMAX], int nsel, int L, int topk, int32_t* out) {
+#pragma unroll
+  for (int p = 0; p < KMAX; ++p)
+    if (p >= nsel) cand[p] = INT32_MAX;
+  sort_asc<KMAX>(cand);
+#pragma unroll
+  for (int p = 0; p <= KMAX; ++p) {
+    if (p < topk) {
+      int v = -1;
+      if (p < nsel) v = cand[p < KMAX ? p : KMAX - 1];
+      else if (p == nsel) v = L;
+      out[p] = v;
+    }
+  }
+}
+
+}  // namespace msa

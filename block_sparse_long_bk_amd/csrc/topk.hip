@@ -1,0 +1,78 @@
+// topk.hip -- exp-free Top-k over rows of block scores (gfx950).
+//
+// Selection rule (paper summary page, "Method"; zhichai.net write-up,
+// sections 2 and 4.1): the local block L(i) = floor((q_offset + i)/128) is
+// always kept; the other k-1 slots go to the candidate blocks j < L(i) with the
+// highest raw scores -- no exponential, since only the order matters.  Equal
+// scores go to the lower block id.  The row is emitted ascending, -1 padded.
+//
+// One wave per (b, g, i) row.  Lane l scans blocks l, l+64, ... in increasing
+// order keeping its own best-KMAX list in registers; the 64 lists are then
+// merged by k-1 rounds of a wave-wide arg-max on (score, -id), the winning
+// lane popping its head.  Integer/compare work only; no LDS, no atomics.
+#include "msa_device.h"
+#include "msa_internal.h"
+
+namespace msa {
+namespace {
+
+template <int KMAX>
+__global__ void __launch_bounds__(256) k_topk_rows(const float* __restrict__ S, int32_t* __restrict__ ids, int Nq,
+                                                   int Hkv, int nblk, int topk, int64_t q_offset, int64_t nrows) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= nrows) return;  // whole wave leaves together
+  const int i = (int)(row % Nq);
+  const int64_t bg = row / Nq;
+  const int g = (int)(bg % Hkv);
+  const int64_t b = bg / Hkv;
+  const int L = (int)((q_offset + i) / kBk);
+  const float* Sr = S + row * nblk;
+
+  TopList<KMAX> list;
+  list.init();
+  for (int j = lane; j < L; j += 64) list.offer(Sr[j], j);
+
+  const int nsel = min(topk - 1, L);
+  int sel[KMAX];
+#pragma unroll
+  for (int r = 0; r < KMAX; ++r) {
+    sel[r] = INT32_MAX;
+    if (r < nsel) {
+      float bs = list.s[0];
+      int bj = list.j[0];
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) {
+        const float os = xor_shfl(bs, m);
+        const int oj = xor_shfl(bj, m);
+        const bool take = (os > bs) || (os == bs && oj < bj);
+        bs = take ? os : bs;
+        bj = take ? oj : bj;
+      }
+      sel[r] = bj;
+      if (list.j[0] == bj) list.pop();
+    }
+  }
+  if (lane == 0) write_selection<KMAX>(sel, nsel, L, topk, ids + (((int64_t)b * Nq + i) * Hkv + g) * topk);
+}
+
+}  // namespace
+
+hipError_t launch_topk_rows(const Shape& s, const float* scores, int32_t* ids, hipStream_t st) {
+  static const int kid = prof_register("topk_rows");
+  const int64_t nrows = (int64_t)s.B * s.Hkv * s.Nq;
+  const dim3 grid((unsigned)((nrows + 3) / 4));
+  const int kneed = s.topk - 1;
+  prof_begin(st, kid);
+  if (kneed <= 8)
+    hipLaunchKernelGGL(k_topk_rows<8>, grid, dim3(256), 0, st, scores, ids, s.Nq, s.Hkv, s.nblk, s.topk, s.q_offset, nrows);
+  else if (kneed <= 16)
+    hipLaunchKernelGGL(k_topk_rows<16>, grid, dim3(256), 0, st, scores, ids, s.Nq, s.Hkv, s.nblk, s.topk, s.q_offset, nrows);
+  else
+    hipLaunchKernelGGL(k_topk_rows<32>, grid, dim3(256), 0, st, scores, ids, s.Nq, s.Hkv, s.nblk, s.topk, s.q_offset, nrows);
+  const hipError_t e = hipGetLastError();
+  prof_end(st, kid);
+  return e;
+}
+
+}  // namespace msa

@@ -1,0 +1,158 @@
+/*
+ * msa.h -- C ABI of libmsa: the MiniMax Sparse Attention (MSA) forward hot
+ * path on AMD MI355X (gfx950).
+ *
+ * The method (MiniMax Sparse Attention abstract; paper summary page, "Method";
+ * zhichai.net write-up, section 2):
+ *   Index Branch, per GQA group g and query i at position p = q_offset + i:
+ *     token score  s_t = <idx_q[b,i,g,:], idx_k[b,t,g,:]>          (no scale)
+ *     block score  S_j = max over the tokens t of key block j of s_t
+ *                  (Block Max Pooling) for the candidate blocks j < L,
+ *                  L = floor(p / Bk) being the block holding the query;
+ *     selection    {L} plus the k-1 best candidates by (S desc, id asc);
+ *                  every candidate when there are at most k-1.  The
+ *                  selection is exp-free: it uses the raw scores (zhichai.net
+ *                  write-up, section 4.1).
+ *   Main Branch: each query head h of group g = h / (Hq/Hkv) attends with
+ *     exact softmax (scale 1/sqrt(d) unless given) over the tokens t <= p of
+ *     the group's selected blocks.
+ *
+ * Tensor layouts (contiguous, token-major "BNHD"; element type = dtype):
+ *   q      [B, Nq, Hq,  d]          k, v   [B, Nk, Hkv, d]
+ *   idx_q  [B, Nq, Hkv, d_idx]      idx_k  [B, Nk, Hkv, d_idx]
+ *   out    [B, Nq, Hq,  d]          lse    [B, Nq, Hq]        (fp32, natural log)
+ *   block_ids [B, Nq, Hkv, topk]    int32, ascending, -1 padded
+ *   scores [B, Hkv, Nq, nblk]       fp32, nblk = ceil(Nk / Bk)
+ *
+ * Conventions for every call:
+ *   - All tensor pointers are device pointers, 16-byte aligned, owned by the
+ *     caller.  Inputs are read only; outputs are fully overwritten and must not
+ *     alias inputs.  `ws` is caller-owned device scratch of `ws_bytes` bytes
+ *     (its contents on entry do not matter and are clobbered).
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is queued
+ *     asynchronously on it; the library never allocates device memory and
+ *     never synchronises the device.
+ *   - Arguments are validated before any HIP call.  Errors: MSA_ERR_INVALID_ARG
+ *     (inconsistent or out-of-range shape, NULL pointer, misalignment),
+ *     MSA_ERR_UNSUPPORTED (valid but not built: see below), MSA_ERR_WORKSPACE
+ *     (ws_bytes below what msa_workspace_size reports as the minimum),
+ *     MSA_ERR_HIP (a HIP call failed; msa_last_hip_error gives its code).
+ *     No C++ exception crosses this boundary.
+ *   - Results are bitwise reproducible for identical inputs and do not depend
+ *     on how the library splits the work (query chunks, workspace size).
+ *
+ * Supported: dtype MSA_BF16 or MSA_F32; block_size 128; d in {64, 128};
+ * d_idx in {32, 64, 128}; 1 <= topk <= 32; Hq / Hkv a power of two <= 32;
+ * 0 <= q_offset and q_offset + Nq <= Nk.
+ */
+#ifndef MSA_H
+#define MSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MSA_OK = 0,
+  MSA_ERR_INVALID_ARG = -1,
+  MSA_ERR_UNSUPPORTED = -2,
+  MSA_ERR_WORKSPACE = -3,
+  MSA_ERR_HIP = -4
+} msa_status_t;
+
+typedef enum { MSA_F32 = 0, MSA_BF16 = 1 } msa_dtype_t;
+
+/* Attention schedule.  KV_OUTER keeps one selected KV block resident and
+ * streams the queries that chose it (KV-stationary; the paper's co-designed
+ * path, abstract and "Key Contributions").  Q_OUTER keeps the query resident
+ * and gathers its blocks (the query-stationary baseline of the Fireworks note
+ * on KV-stationary attention, "The design space").  AUTO picks KV_OUTER when
+ * the average number of times a selected KV token is re-read,
+ * Nq*topk*Bk/Nk, exceeds 2.85 (the reuse crossover quoted in that note), and
+ * Q_OUTER otherwise. */
+typedef enum { MSA_SCHED_AUTO = 0, MSA_SCHED_KV_OUTER = 1, MSA_SCHED_Q_OUTER = 2 } msa_sched_t;
+
+typedef struct {
+  int32_t batch, n_q, n_k, h_q, h_kv, d, d_idx, block_size, topk;
+  int32_t dtype;         /* msa_dtype_t */
+  int64_t q_offset;      /* query i sits at position q_offset + i */
+  float softmax_scale;   /* <= 0 means 1/sqrt(d) */
+  int32_t sched;         /* msa_sched_t */
+} msa_problem_t;
+
+typedef enum { MSA_OP_INDEX_TOPK = 0, MSA_OP_ATTENTION = 1, MSA_OP_FORWARD = 2 } msa_op_t;
+
+/* Human-readable name of a status code (static storage). */
+const char* msa_status_string(msa_status_t status);
+
+/* The hipError_t of the last failing HIP call on this thread (0 if none). */
+int msa_last_hip_error(void);
+
+/* Validate a problem without touching the GPU. */
+msa_status_t msa_validate(const msa_problem_t* prob);
+
+/* Workspace for one call of `op`: *bytes = size that lets the whole problem
+ * run in one pass; *min_bytes (may be NULL) = the least the call accepts (it
+ * then processes the queries in chunks). */
+msa_status_t msa_workspace_size(const msa_problem_t* prob, int op, size_t* bytes, size_t* min_bytes);
+
+/* Index Branch step 1+2 alone: block scores (Block Max Pooling of the
+ * index-q . index-k token scores; paper summary "Method").  Writes `scores`
+ * [B, Hkv, Nq, nblk] fp32: S_j for candidate blocks j < L(i), -inf elsewhere. */
+msa_status_t msa_block_scores(const msa_problem_t* prob, const void* idx_q, const void* idx_k,
+                              float* scores, void* stream);
+
+/* Index Branch step 3 alone: exp-free Top-k over given block scores (laid out
+ * as msa_block_scores writes them; only j < L(i) is read), forcing the local
+ * block, ties to the lower id (zhichai.net write-up, sections 2 and 4.1).
+ * Writes block_ids [B, Nq, Hkv, topk]. */
+msa_status_t msa_topk_from_scores(const msa_problem_t* prob, const float* scores, int32_t* block_ids,
+                                  void* stream);
+
+/* Index Branch: block scores and Top-k in one call; writes block_ids.
+ * Needs the MSA_OP_INDEX_TOPK workspace (zero bytes for most prefill
+ * shapes, where scoring and selection run fused). */
+msa_status_t msa_index_topk(const msa_problem_t* prob, const void* idx_q, const void* idx_k,
+                            int32_t* block_ids, void* ws, size_t ws_bytes, void* stream);
+
+/* Block -> query inversion used by the KV-outer schedule (the paper's
+ * skew-tolerant, atomic-free bookkeeping, "Key Contributions"): for each
+ * (b, g), offsets [B, Hkv, nblk+1] (int32, exclusive prefix of the number of
+ * (query, slot) pairs that chose each block) and entries [B, Hkv, Nq*topk]
+ * (int32 i*topk + slot, grouped by block, ascending within a block; entries
+ * past offsets[nblk] are unspecified).  Deterministic.  Needs the
+ * MSA_OP_ATTENTION workspace. */
+msa_status_t msa_invert(const msa_problem_t* prob, const int32_t* block_ids, int32_t* offsets,
+                        int32_t* entries, void* ws, size_t ws_bytes, void* stream);
+
+/* Main Branch: exact softmax attention of every query head over the visible
+ * tokens of its group's blocks in block_ids (paper summary "Method"), in the
+ * schedule prob->sched.  Writes out (dtype of the inputs) and, if lse is not
+ * NULL, the log-sum-exp of the scaled logits. */
+msa_status_t msa_sparse_attention(const msa_problem_t* prob, const void* q, const void* k, const void* v,
+                                  const int32_t* block_ids, void* out, float* lse, void* ws, size_t ws_bytes,
+                                  void* stream);
+
+/* Index Branch then Main Branch: writes block_ids, out and (optionally) lse. */
+msa_status_t msa_forward(const msa_problem_t* prob, const void* q, const void* k, const void* v,
+                         const void* idx_q, const void* idx_k, int32_t* block_ids, void* out, float* lse,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/* Kernel timing for measurement.  While enabled, every kernel launch is
+ * bracketed by two hipEvents on its stream (a small overhead per launch).
+ * msa_profile_read synchronises on those events and returns, for kernel
+ * number `index` (0 <= index < msa_profile_count()), its name (static
+ * storage), the summed duration in milliseconds and the launch count since the
+ * last reset.  These are the only calls that wait on the GPU. */
+msa_status_t msa_profile_enable(int on);
+msa_status_t msa_profile_reset(void);
+int msa_profile_count(void);
+msa_status_t msa_profile_read(int index, const char** name, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MSA_H */

@@ -171,6 +171,36 @@ int mo_select(const mo_problem* p, const double* scores, const int64_t* rows, in
   return 0;
 }
 
+/* Block -> query lists by plain counting: count, exclusive prefix, then place
+ * every pick walking the queries and slots in ascending order. */
+int mo_invert(const mo_problem* p, const int32_t* ids, int32_t* offsets, int32_t* entries) {
+  int rc = check_problem(p, MO_F64);
+  if (rc) return rc;
+  if (!ids || !offsets || !entries) return -1;
+  const int64_t nblk = num_blocks(p), H = p->h_kv, K = p->topk, Nq = p->n_q;
+  for (int64_t b = 0; b < p->batch; ++b)
+    for (int64_t g = 0; g < H; ++g) {
+      int32_t* off = offsets + (b * H + g) * (nblk + 1);
+      int32_t* ent = entries + (b * H + g) * (Nq * K);
+      for (int64_t j = 0; j <= nblk; ++j) off[j] = 0;
+      for (int64_t i = 0; i < Nq; ++i)
+        for (int64_t s = 0; s < K; ++s) {
+          const int32_t j = ids[((b * Nq + i) * H + g) * K + s];
+          if (j >= 0 && j < nblk) off[j + 1] += 1;
+        }
+      for (int64_t j = 0; j < nblk; ++j) off[j + 1] += off[j];
+      int32_t* fill = (int32_t*)calloc((size_t)nblk, sizeof(int32_t));
+      if (!fill) return -10;
+      for (int64_t i = 0; i < Nq; ++i)
+        for (int64_t s = 0; s < K; ++s) {
+          const int32_t j = ids[((b * Nq + i) * H + g) * K + s];
+          if (j >= 0 && j < nblk) ent[off[j] + fill[j]++] = (int32_t)(i * K + s);
+        }
+      free(fill);
+    }
+  return 0;
+}
+
 /* Step 4: exact softmax attention restricted to the selected blocks. */
 int mo_attend(const mo_problem* p, const void* q, const void* k, const void* v, int dtype,
               const int32_t* ids, const int64_t* rows, int64_t n_rows, double* out, double* lse) {

@@ -67,6 +67,15 @@ int mo_select(const mo_problem* p, const double* scores, const int64_t* rows, in
 int mo_attend(const mo_problem* p, const void* q, const void* k, const void* v, int dtype,
               const int32_t* ids, const int64_t* rows, int64_t n_rows, double* out, double* lse);
 
+/* Block -> query lists (the bookkeeping a KV-outer schedule needs; the paper
+ * summary's "Key Contributions" name KV-outer attention): for each (b, g),
+ * offsets[(b*h_kv+g)*(nblk+1) + j] = number of (i, slot) pairs with
+ * ids[b,i,g,slot] < j and >= 0 (so offsets[.., nblk] = all valid picks), and
+ * entries[(b*h_kv+g)*(n_q*topk) + ...] = i*topk + slot for every pick, grouped
+ * by block j, ascending in (i, slot) within a block.  ids: [B, Nq, h_kv, topk]
+ * covering every query (no row subset). */
+int mo_invert(const mo_problem* p, const int32_t* ids, int32_t* offsets, int32_t* entries);
+
 /* Number of OpenMP threads the routines above use. */
 int mo_num_threads(void);
 

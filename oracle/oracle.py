@@ -125,7 +125,8 @@ def load(path):
     L.mo_block_scores.argtypes = [P, vp, vp, ctypes.c_int, vp, ctypes.c_int64, vp]
     L.mo_select.argtypes = [P, vp, vp, ctypes.c_int64, vp]
     L.mo_attend.argtypes = [P, vp, vp, vp, ctypes.c_int, vp, vp, ctypes.c_int64, vp, vp]
-    for f in (L.mo_block_scores, L.mo_select, L.mo_attend):
+    L.mo_invert.argtypes = [P, vp, vp, vp]
+    for f in (L.mo_block_scores, L.mo_select, L.mo_attend, L.mo_invert):
         f.restype = ctypes.c_int
     L.mo_num_threads.restype = ctypes.c_int
     return L
@@ -180,3 +181,15 @@ def _rows(prob, rows):
 
 def _ptr(a):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def invert(prob, ids, orc=None):
+    """Block -> query lists: (offsets [B, h_kv, nblk+1], entries [B, h_kv, n_q*topk])."""
+    orc = orc or default()
+    ids = np.ascontiguousarray(np.asarray(ids, dtype=np.int32)).reshape(prob.batch, prob.n_q, prob.h_kv, prob.topk)
+    offsets = np.empty((prob.batch, prob.h_kv, nblk(prob) + 1), dtype=np.int32)
+    entries = np.full((prob.batch, prob.h_kv, prob.n_q * prob.topk), -1, dtype=np.int32)
+    rc = orc.L.mo_invert(ctypes.byref(prob), _ptr(ids), _ptr(offsets), _ptr(entries))
+    if rc:
+        raise ValueError(f"mo_invert: invalid argument ({rc})")
+    return offsets, entries

@@ -1,0 +1,103 @@
+"""CPU checks of the C ABI: the library loads, exports every entry point that
+include/msa.h declares, and validates arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_sparse_long_bk_amd import api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "msa.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(msa_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(api.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = api.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def good(**kw):
+    p = dict(batch=1, n_q=1024, n_k=1024, h_q=8, h_kv=2, d=64, d_idx=32, topk=4, dtype="f32")
+    p.update(kw)
+    return api.problem(**p)
+
+
+def test_status_strings():
+    L = api.lib()
+    for code in (0, -1, -2, -3, -4):
+        assert L.msa_status_string(code)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), api.MSA_OK),
+    (dict(dtype="bf16", d=128, d_idx=128, h_q=64, h_kv=8, topk=16), api.MSA_OK),
+    (dict(batch=0), api.MSA_ERR_INVALID_ARG),
+    (dict(n_q=0), api.MSA_ERR_INVALID_ARG),
+    (dict(h_q=6, h_kv=4), api.MSA_ERR_INVALID_ARG),
+    (dict(n_q=2000), api.MSA_ERR_INVALID_ARG),            # n_q > n_k
+    (dict(q_offset=1), api.MSA_ERR_INVALID_ARG),           # q_offset + n_q > n_k
+    (dict(q_offset=-1, n_q=10), api.MSA_ERR_INVALID_ARG),
+    (dict(topk=0), api.MSA_ERR_INVALID_ARG),
+    (dict(softmax_scale=float("nan")), api.MSA_ERR_INVALID_ARG),
+    (dict(sched=7), api.MSA_ERR_INVALID_ARG),
+    (dict(block_size=64), api.MSA_ERR_UNSUPPORTED),
+    (dict(d=96), api.MSA_ERR_UNSUPPORTED),
+    (dict(d_idx=48), api.MSA_ERR_UNSUPPORTED),
+    (dict(topk=33), api.MSA_ERR_UNSUPPORTED),
+    (dict(h_q=12, h_kv=2), api.MSA_ERR_UNSUPPORTED),      # 6 heads per group
+    (dict(h_q=64, h_kv=1), api.MSA_ERR_UNSUPPORTED),      # 64 heads per group
+])
+def test_validate(kw, status):
+    assert api.validate(good(**kw)) == status
+
+
+def test_invalid_dtype_code():
+    p = good()
+    p.dtype = 5
+    assert api.validate(p) == api.MSA_ERR_INVALID_ARG
+
+
+def test_entry_points_reject_before_any_hip_call():
+    L = api.lib()
+    p = good()
+    x = ctypes.c_void_p(4096)  # never dereferenced: validation fails first
+    null = None
+    assert L.msa_forward(ctypes.byref(p), null, x, x, x, x, x, x, null, null, 0, null) == api.MSA_ERR_INVALID_ARG
+    assert L.msa_sparse_attention(ctypes.byref(p), x, x, x, x, null, null, null, 0, null) == api.MSA_ERR_INVALID_ARG
+    mis = ctypes.c_void_p(4100)  # not 16-byte aligned
+    assert L.msa_index_topk(ctypes.byref(p), mis, x, x, null, 0, null) == api.MSA_ERR_INVALID_ARG
+    assert L.msa_block_scores(None, x, x, x, null) == api.MSA_ERR_INVALID_ARG
+    bad = good(d=96)
+    assert L.msa_forward(ctypes.byref(bad), x, x, x, x, x, x, x, null, null, 0, null) == api.MSA_ERR_UNSUPPORTED
+    # attention with too little workspace
+    big = good(dtype="bf16", n_q=32768, n_k=32768, h_q=64, h_kv=8, d=128, d_idx=128, topk=16, sched="kv_outer")
+    assert L.msa_sparse_attention(ctypes.byref(big), x, x, x, x, x, null, x, 1024, null) == api.MSA_ERR_WORKSPACE
+    assert L.msa_workspace_size(ctypes.byref(p), 9, ctypes.byref(ctypes.c_size_t()), None) == api.MSA_ERR_INVALID_ARG
+
+
+def test_workspace_sizes():
+    pre = good(dtype="bf16", n_q=32768, n_k=32768, h_q=64, h_kv=8, d=128, d_idx=128, topk=16)
+    full, least = api.workspace_size(pre, api.OP_INDEX_TOPK)
+    assert full == least == 0  # fused scoring + selection needs no scratch
+    full, least = api.workspace_size(pre, api.OP_ATTENTION)
+    # KV-outer partials: fp32 output + lse per (query, head, slot)
+    assert full >= 32768 * 64 * 16 * (128 * 4 + 4)
+    assert least < full / 64
+    dec = good(dtype="bf16", batch=16, n_q=1, n_k=1 << 20, q_offset=(1 << 20) - 1, h_q=64, h_kv=8, d=128,
+               d_idx=128, topk=16)
+    full, least = api.workspace_size(dec, api.OP_INDEX_TOPK)
+    assert full == 16 * 8 * 1 * 8192 * 4  # block scores of the decode scan
+    fwd, _ = api.workspace_size(dec, api.OP_FORWARD)
+    att, _ = api.workspace_size(dec, api.OP_ATTENTION)
+    assert fwd == max(full, att)

@@ -336,6 +336,29 @@ def test_bf16_and_f32_inputs_widen_exactly():
         assert np.array_equal(a, b) and np.array_equal(a, c)
 
 
+def test_invert_matches_definition():
+    """Block -> query lists: for every block, exactly the (query, slot) picks of
+    that block, ascending; brute force over every (block, query, slot)."""
+    rng = np.random.default_rng(31)
+    B, N, Hkv, K, Bk = 2, 40, 3, 4, 4
+    prob = O.make_problem(B, N, N, Hkv, Hkv, 2, 2, Bk, K)
+    nb = N // Bk
+    ids = rng.integers(-1, nb, size=(B, N, Hkv, K)).astype(np.int32)
+    for b in range(B):  # a query never picks a block twice
+        for i in range(N):
+            for g in range(Hkv):
+                row = rng.choice(nb, size=K, replace=False)
+                row[rng.random(K) < 0.2] = -1
+                ids[b, i, g] = row
+    off, ent = O.invert(prob, ids)
+    for b in range(B):
+        for g in range(Hkv):
+            assert off[b, g, 0] == 0 and off[b, g, -1] == int((ids[b, :, g] >= 0).sum())
+            for j in range(nb):
+                want = [i * K + s for i in range(N) for s in range(K) if ids[b, i, g, s] == j]
+                assert list(ent[b, g, off[b, g, j]:off[b, g, j + 1]]) == want
+
+
 def test_invalid_arguments_rejected():
     prob = O.make_problem(1, 8, 4, 2, 1, 2, 2, 2, 2)  # n_q > n_k
     with pytest.raises(ValueError):
