@@ -1,0 +1,240 @@
+"""Benchmark of the MSA forward hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill_32k]
+                    [--sched auto|kv_outer|q_outer] [--no-cpu] [--no-decode]
+
+One step = msa_forward (index scores + Top-k, inversion, attention, combine)
+over one batch of the seeded synthetic workload, inputs already in HBM.
+Prints one JSON line.  ``value`` is effective TFLOP/s over the selected,
+unmasked tokens, 4*d per (query head, key), divided by the whole forward
+step time.  The decode leg (16 sequences x 1M cached tokens, one new token
+each) reports microseconds per generated token.  Per-kernel times come from
+hipEvents that libmsa records around each launch on the launch stream.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from block_sparse_long_bk_amd import api, inputs  # noqa: E402
+
+METRIC = "MSA fwd effective TFLOP/s (selected tokens) & decode µs/token @1M ctx"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 matrix
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def selected_tokens(wl, ids):
+    """Sum over (b, i, g) of the visible tokens in the selected blocks."""
+    Bk = wl.block_size
+    pos = wl.q_offset + torch.arange(wl.n_q, device=ids.device, dtype=torch.int64).view(1, -1, 1, 1)
+    j = ids.to(torch.int64)
+    start = j * Bk
+    n = torch.minimum(pos - start + 1, torch.full_like(start, Bk))
+    n = torch.minimum(n, wl.n_k - start)
+    n = torch.where(j >= 0, n.clamp(min=0), torch.zeros_like(n))
+    return int(n.sum().item())
+
+
+def attention_flops(wl, ids):
+    G = wl.h_q // wl.h_kv
+    return 4.0 * wl.d * G * selected_tokens(wl, ids)
+
+
+def index_flops(wl):
+    L = (wl.q_offset + np.arange(wl.n_q, dtype=np.int64)) // wl.block_size
+    return 2.0 * wl.d_idx * wl.h_kv * wl.batch * float(L.sum()) * wl.block_size
+
+
+def time_steps(fn, steps, warmup):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    api.profile_reset()
+    api.profile_enable(True)
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(st)
+    for _ in range(steps):
+        fn()
+    e1.record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    api.profile_enable(False)
+    kern = {k: (ms / n, n / steps) for k, (ms, n) in api.profile_read().items() if n}
+    return e0.elapsed_time(e1) / steps, wall * 1e3 / steps, kern
+
+
+def source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
+    were taken on the current kernel source (else None)."""
+    try:
+        data = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    rec = data.get(workload, {}).get(kernel)
+    if not rec or rec.get("source_hash") != source_hash(rec.get("sources", [])):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, x, n_sample):
+    """The fp64 oracle (as it stands) on an evenly spaced sample of queries."""
+    from oracle import oracle as O
+
+    h = {k: v.cpu() for k, v in x.items()}
+    prob = O.problem_of(wl)
+    qi = np.unique(np.linspace(0, wl.n_q - 1, n_sample).astype(np.int64))
+    rows = np.stack([np.zeros_like(qi), qi], axis=1)
+    t0 = time.perf_counter()
+    s = O.block_scores(prob, h["iq"], h["ik"], rows)
+    ids = O.select(prob, s, rows)
+    O.attend(prob, h["q"], h["k"], h["v"], ids, rows)
+    dt = time.perf_counter() - t0
+    ids_t = torch.from_numpy(ids).view(len(qi), 1, wl.h_kv, wl.topk)
+    # selected visible tokens for the sampled queries
+    pos = torch.from_numpy(wl.q_offset + qi).view(-1, 1, 1, 1)
+    j = ids_t.to(torch.int64)
+    n = torch.minimum(pos - j * wl.block_size + 1, torch.full_like(j, wl.block_size))
+    n = torch.where(j >= 0, n.clamp(min=0), torch.zeros_like(n))
+    flops = 4.0 * wl.d * (wl.h_q // wl.h_kv) * float(n.sum())
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": O.num_threads(), "kind": "oracle",
+            "sample": f"{len(qi)} of {wl.n_q} queries (evenly spaced), all {wl.h_q} heads; index scores, "
+                      f"Top-k and attention in fp64; {dt:.1f} s",
+            "seconds": dt}
+
+
+def run_prefill(args):
+    wl = inputs.WORKLOADS[args.workload]
+    x = inputs.generate(wl, device="cuda")
+    p = api.problem_of(wl, sched=args.sched)
+    ws = api.alloc_workspace(p, api.OP_FORWARD)
+    ids = torch.empty((wl.batch, wl.n_q, wl.h_kv, wl.topk), dtype=torch.int32, device="cuda")
+    out = torch.empty_like(x["q"])
+    lse = torch.empty((wl.batch, wl.n_q, wl.h_q), dtype=torch.float32, device="cuda")
+
+    def step():
+        api.forward(p, x["q"], x["k"], x["v"], x["iq"], x["ik"], ids=ids, out=out, lse=lse, ws=ws)
+
+    step()
+    torch.cuda.synchronize()
+    fl_attn = attention_flops(wl, ids)
+    fl_idx = index_flops(wl)
+    ms, wall_ms, kern = time_steps(step, args.steps, args.warmup)
+    res = dict(wl=wl, x=x, ms=ms, wall_ms=wall_ms, kern=kern, fl_attn=fl_attn, fl_idx=fl_idx, ws=ws.numel())
+    del ws, out, lse
+    return res
+
+
+def run_decode(args):
+    wl = inputs.WORKLOADS["decode_16x1m"]
+    x = inputs.generate(wl, device="cuda")
+    p = api.problem_of(wl, sched="auto")
+    ws = api.alloc_workspace(p, api.OP_FORWARD)
+    ids = torch.empty((wl.batch, wl.n_q, wl.h_kv, wl.topk), dtype=torch.int32, device="cuda")
+    out = torch.empty_like(x["q"])
+
+    def step():
+        api.forward(p, x["q"], x["k"], x["v"], x["iq"], x["ik"], ids=ids, out=out, want_lse=False, ws=ws)
+
+    step()
+    torch.cuda.synchronize()
+    steps = max(3, args.steps)
+    ms, wall_ms, kern = time_steps(step, steps, args.warmup)
+    # algorithmic bytes: idx_k of every candidate block, the selected K/V
+    # tokens, the index and attention queries, block scores, ids and outputs
+    L = (wl.q_offset + wl.n_q - 1) // wl.block_size
+    e = 2
+    b_idx = wl.batch * L * wl.block_size * wl.h_kv * wl.d_idx * e
+    sel = selected_tokens(wl, ids)
+    b_kv = sel * wl.d * 2 * e
+    b_small = wl.batch * (wl.h_kv * wl.d_idx + 2 * wl.h_q * wl.d) * e + wl.batch * wl.h_kv * L * 4 * 2
+    total = b_idx + b_kv + b_small
+    del x, ws
+    torch.cuda.empty_cache()
+    return {"workload": wl.name, "us_per_token": ms * 1e3 / (wl.batch * wl.n_q), "ms_per_step": ms,
+            "algorithmic_bytes": total, "hbm_GBs": total / ms / 1e6, "hbm_frac": total / ms / 1e6 / PEAK_HBM_GBS,
+            "kernels_ms": {k: round(v[0], 4) for k, v in kern.items()}}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="prefill_32k", choices=sorted(inputs.WORKLOADS))
+    ap.add_argument("--sched", default="auto", choices=["auto", "kv_outer", "q_outer"])
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=1024)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: the MSA forward path here is a single-GPU build "
+              "(see DESIGN.md for how it would shard); --gpus must be 1", file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    r = run_prefill(args)
+    wl, kern = r["wl"], r["kern"]
+    value = r["fl_attn"] / r["ms"] / 1e9  # TFLOP/s
+    peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
+    dom = max(kern, key=lambda k: kern[k][0] * kern[k][1])
+    # algorithmic work of the dominant kernel per launch
+    if dom.startswith("attn_"):
+        achieved = r["fl_attn"] / kern[dom][1] / kern[dom][0] / 1e9
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s"}
+    elif dom.startswith("index_tile"):
+        achieved = r["fl_idx"] / kern[dom][0] / 1e9
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": None, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["kernel"] = dom
+    roof["frac"] = roof["achieved"] / roof["peak"] if roof["achieved"] else None
+    roof["traffic"] = measured_traffic(dom, wl.name)
+    line = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": r["ms"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.batch, "n_q": wl.n_q, "n_k": wl.n_k, "q_offset": wl.q_offset,
+                   "block_size": wl.block_size, "topk": wl.topk, "h_q": wl.h_q, "h_kv": wl.h_kv, "d": wl.d,
+                   "d_idx": wl.d_idx, "sched": args.sched, "hot_frac": wl.hot_frac},
+        "roofline": roof,
+        "attention_tflops_per_step": r["fl_attn"] / 1e12, "index_tflops_per_step": r["fl_idx"] / 1e12,
+        "index_TFLOPs": None, "wall_ms_per_step": r["wall_ms"],
+        "kernels_ms": {k: round(v[0], 4) for k, v in kern.items()},
+        "kernel_launches_per_step": {k: v[1] for k, v in kern.items()},
+        "workspace_bytes": r["ws"],
+    }
+    it = [k for k in kern if k.startswith("index_tile")]
+    if it:
+        line["index_TFLOPs"] = r["fl_idx"] / kern[it[0]][0] / 1e9
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(wl, r["x"], args.cpu_sample)
+    del r
+    torch.cuda.empty_cache()
+    if not args.no_decode:
+        line["decode"] = run_decode(args)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

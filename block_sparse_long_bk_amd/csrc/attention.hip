@@ -121,9 +121,9 @@ template <> __device__ __forceinline__ float from_f32<float>(float x) { return x
 // block max (log2 domain, already scaled) m, sum l, and its 64 of the D output
 // values in o[dt][e] for d = 32dt + 8(e/4) + 4h + e%4.
 template <typename T, int D>
-__device__ __forceinline__ void block_tile(const char* lds, const frag_t<T> (&qf)[D / 16], float c_log2, int64_t key0,
-                                           int64_t vis_end, bool need_mask, float& m, float& l,
-                                           f32x16 (&o)[D / 32]) {
+// Keys at offsets >= vis (0..128) inside the block are masked when need_mask.
+__device__ __forceinline__ void block_tile(const char* lds, const frag_t<T> (&qf)[D / 16], float c_log2, int vis,
+                                           bool need_mask, float& m, float& l, f32x16 (&o)[D / 32]) {
   using L = KvLds<T, D>;
   const int lane = threadIdx.x & 63, half = lane >> 5;
   f32x16 s[4];
@@ -134,13 +134,14 @@ __device__ __forceinline__ void block_tile(const char* lds, const frag_t<T> (&qf
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) mma(load8(arow + 16 * ks), qf[ks], s[mt]);
   }
+  __builtin_amdgcn_sched_barrier(0);
   if (need_mask) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int64_t t = key0 + 32 * mt + 8 * (e / 4) + 4 * half + (e % 4);
-        if (t >= vis_end) s[mt][e] = -__builtin_huge_valf();
+        const int t = 32 * mt + 8 * (e / 4) + 4 * half + (e % 4);
+        if (t >= vis) s[mt][e] = -__builtin_huge_valf();
       }
   }
   float mx = -__builtin_huge_valf();
@@ -158,6 +159,7 @@ __device__ __forceinline__ void block_tile(const char* lds, const frag_t<T> (&qf
       sum += p;
     }
   sum += xor_shfl(sum, 32);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16{};
 #pragma unroll
@@ -174,6 +176,35 @@ __device__ __forceinline__ void block_tile(const char* lds, const frag_t<T> (&qf
   l = sum;
 }
 
+// Query rows of one 32-row tile of a KV-outer work item.
+struct TileRows {
+  bool valid;
+  int qq, slot, h;
+};
+__device__ __forceinline__ TileRows tile_rows(const int32_t* ent, int tile, int nrows, int G, int topk, int g) {
+  const int r = tile * 32 + (threadIdx.x & 31);
+  TileRows t;
+  t.valid = r < nrows;
+  const int e = t.valid ? ent[r / G] : 0;
+  t.qq = e / topk;
+  t.slot = e % topk;
+  t.h = g * G + r % G;
+  return t;
+}
+template <typename T, int D>
+__device__ __forceinline__ void load_q_rows(frag_t<T> (&qf)[D / 16], const T* qbase, const TileRows& t, int b, int Nq,
+                                            int Hq, int q0, int half) {
+  const T* qrow = qbase + (((int64_t)b * Nq + q0 + t.qq) * Hq + t.h) * D + 8 * half;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) qf[ks] = t.valid ? load8(qrow + 16 * ks) : zero_frag<T>();
+}
+// Partial store.  (Non-temporal stores were measured several times slower
+// here: the partial-line writes then miss the L2 write combining.)
+template <typename V>
+__device__ __forceinline__ void store_stream(void* p, const V& v) {
+  *reinterpret_cast<V*>(p) = v;
+}
+
 struct KvArgs {
   const void* q;
   const void* k;
@@ -181,7 +212,7 @@ struct KvArgs {
   const int32_t* entries;
   const int32_t* item_count;
   const int4* items;
-  float* part_o;
+  void* part_o;  // [B, nq, Hq, S, D] in the input dtype
   float* part_lse;
   int Nq, Nk, Hq, Hkv, G, topk, S, q0, nq, items_cap;
   int64_t q_offset;
@@ -214,39 +245,41 @@ __global__ void __launch_bounds__(256, 2) k_attn_kvouter(KvArgs a) {
   const int32_t* ent = a.entries + (int64_t)bg * a.nq * a.topk + e0;
   const T* qbase = static_cast<const T*>(a.q);
   const int64_t key0 = (int64_t)j * kBk;
+  // Gathered query rows of tile t: row r = t*32 + lane%32 <-> (entry r/G, head r%G).
+  // The next tile's rows are fetched while the current one computes.
+  TileRows cur = tile_rows(ent, wave, nrows, a.G, a.topk, g);
+  frag_t<T> qf[D / 16];
+  load_q_rows<T, D>(qf, qbase, cur, b, a.Nq, a.Hq, a.q0, half);
   for (int tile = wave; tile * 32 < nrows; tile += 4) {
-    const int r = tile * 32 + (lane & 31);
-    const bool valid = r < nrows;
-    const int e = valid ? ent[r / a.G] : 0;
-    const int qq = e / a.topk, slot = e % a.topk;  // chunk-relative query, slot
-    const int h = g * a.G + r % a.G;
-    frag_t<T> qf[D / 16];
-    const T* qrow = qbase + (((int64_t)b * a.Nq + a.q0 + qq) * a.Hq + h) * D + 8 * half;
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) qf[ks] = valid ? load8(qrow + 16 * ks) : zero_frag<T>();
-    const int64_t pos = a.q_offset + a.q0 + qq;
+    const TileRows nxt = tile_rows(ent, tile + 4, nrows, a.G, a.topk, g);
+    frag_t<T> qn[D / 16];
+    load_q_rows<T, D>(qn, qbase, nxt, b, a.Nq, a.Hq, a.q0, half);
+    const int64_t pos = a.q_offset + a.q0 + cur.qq;
     const int64_t vis_end = min(pos + 1, (int64_t)a.Nk);  // keys t < vis_end are visible
+    const int vis = (int)max((int64_t)0, min((int64_t)kBk, vis_end - key0));
     // Masking is only needed where the block reaches past a row's position.
-    int need = (valid && key0 + kBk > vis_end) ? 1 : 0;
-    need = __any(need);
+    const int need = __any(cur.valid && vis < kBk);
     float m, l;
     f32x16 o[D / 32];
-    block_tile<T, D>(lds, qf, a.c_log2, key0, vis_end, need != 0, m, l, o);
-    if (valid) {
-      const int64_t prow = (((int64_t)b * a.nq + qq) * a.Hq + h) * a.S + slot;
-      float* po = a.part_o + prow * D;
+    block_tile<T, D>(lds, qf, a.c_log2, vis, need != 0, m, l, o);
+    if (cur.valid) {
+      const int64_t prow = (((int64_t)b * a.nq + cur.qq) * a.Hq + cur.h) * a.S + cur.slot;
+      T* po = static_cast<T*>(a.part_o) + prow * D;
       const float inv = 1.f / l;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          f32x4 w;
+          typename Pack4<T>::type w;
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr) w[rr] = o[dt][4 * i + rr] * inv;
-          *reinterpret_cast<f32x4*>(po + 32 * dt + 8 * i + 4 * half) = w;
+          for (int rr = 0; rr < 4; ++rr) w[rr] = from_f32<T>(o[dt][4 * i + rr] * inv);
+          store_stream(po + 32 * dt + 8 * i + 4 * half, w);
         }
       if (half == 0) a.part_lse[prow] = (m + log2_fast(l)) * kLn2;
     }
+    cur = nxt;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) qf[ks] = qn[ks];
   }
 }
 
@@ -257,7 +290,7 @@ struct QoArgs {
   const int32_t* ids;
   void* out;
   float* lse;
-  float* part_o;
+  void* part_o;
   float* part_lse;
   int Nq, Nk, Hq, Hkv, G, topk, nsplit, q0, nq;
   int64_t q_offset;
@@ -386,12 +419,12 @@ __global__ void __launch_bounds__(256, 2) k_attn_qouter(QoArgs a) {
       if (dg == 0 && a.lse) a.lse[((int64_t)b * a.Nq + qglob) * a.Hq + h2] = lse_v;
     } else {
       const int64_t prow = (((int64_t)b * a.nq + qq) * a.Hq + h2) * a.nsplit + split;
-      float* po = a.part_o + prow * D;
+      T* po = static_cast<T*>(a.part_o) + prow * D;
       for (int d = dg * DPG; d < (dg + 1) * DPG; ++d) {
         float acc = 0.f;
 #pragma unroll
         for (int w = 0; w < 4; ++w) acc += wgt[w] * ob[(w * D + d) * 32 + c2];
-        po[d] = acc * inv;
+        po[d] = from_f32<T>(acc * inv);
       }
       if (dg == 0) a.part_lse[prow] = lse_v;
     }
@@ -399,7 +432,7 @@ __global__ void __launch_bounds__(256, 2) k_attn_qouter(QoArgs a) {
 }
 
 struct CombArgs {
-  const float* part_o;
+  const void* part_o;
   const float* part_lse;
   const int32_t* ids;
   void* out;
@@ -407,47 +440,68 @@ struct CombArgs {
   int Nq, Hq, Hkv, G, topk, S, q0, nq, ids_slots;
 };
 
-// One wave per (b, query, head): merge its S partials.
+template <typename T> struct Pack8;
+template <> struct Pack8<bf16_t> { using type = bf16x8; };
+template <> struct Pack8<float> { using type = f32x8; };
+
+// D/8 lanes per (b, query, head) row, 8 output values per lane: merge the S
+// partials of the row by log-sum-exp weights.  Slots with block id -1
+// (KV-outer) or lse = -inf (empty query-outer split) carry no weight.
 template <typename T, int D>
 __global__ void __launch_bounds__(256) k_combine(CombArgs a) {
+  constexpr int LPH = D / 8;     // lanes per row
+  constexpr int RPW = 64 / LPH;  // rows per wave
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (b, qq, h)
+  const int sub = lane % LPH;
+  const int64_t row = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW + lane / LPH;  // (qq, h)
   const int b = blockIdx.y;
-  if (row >= (int64_t)a.nq * a.Hq) return;
+  if (row >= (int64_t)a.nq * a.Hq) return;  // no cross-lane work below
   const int qq = (int)(row / a.Hq), h = (int)(row % a.Hq), g = h / a.G;
   const int64_t prow = ((int64_t)b * a.nq + qq) * a.Hq + h;
   const int32_t* sel = a.ids + (((int64_t)b * a.Nq + a.q0 + qq) * a.Hkv + g) * a.topk;
-  // slot statistics: lane s < S holds slot s
-  float ls = -__builtin_huge_valf();
-  if (lane < a.S) {
-    const bool ok = a.ids_slots ? (sel[lane] >= 0) : true;
-    if (ok) ls = a.part_lse[prow * a.S + lane];
-  }
-  float M = ls;
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, xor_shfl(M, m));
-  const float Mref = M == -__builtin_huge_valf() ? 0.f : M;
-  const float w = ls == -__builtin_huge_valf() ? 0.f : exp2_fast((ls - Mref) * kLog2e);
-  float W = w;
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) W += xor_shfl(W, m);
-  constexpr int VPL = D / 64;  // values per lane
-  float acc[VPL];
-#pragma unroll
-  for (int u = 0; u < VPL; ++u) acc[u] = 0.f;
-  const float* po = a.part_o + prow * a.S * D;
+  const float* pl = a.part_lse + prow * a.S;
+  float M = -__builtin_huge_valf();
   for (int s = 0; s < a.S; ++s) {
-    const float ws = __shfl(w, s, 64);
-    if (ws != 0.f) {
+    const bool ok = !a.ids_slots || sel[s] >= 0;
+    if (ok) M = fmaxf(M, pl[s]);
+  }
+  const float Mref = M == -__builtin_huge_valf() ? 0.f : M;
+  float acc[8];
 #pragma unroll
-      for (int u = 0; u < VPL; ++u) acc[u] = fmaf(ws, po[(int64_t)s * D + lane * VPL + u], acc[u]);
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  float W = 0.f;
+  const T* po = static_cast<const T*>(a.part_o) + prow * a.S * D + sub * 8;
+  // Eight slots per round: all their loads are issued before any is used.
+  for (int s0 = 0; s0 < a.S; s0 += 8) {
+    frag_t<T> v[8];
+    float w[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int s = s0 + u;
+      const bool ok = s < a.S && (!a.ids_slots || sel[s] >= 0);
+      const float ls = ok ? pl[s] : -__builtin_huge_valf();
+      w[u] = ls == -__builtin_huge_valf() ? 0.f : exp2_fast((ls - Mref) * kLog2e);
+      v[u] = s < a.S ? load8(po + (int64_t)s * D) : zero_frag<T>();
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      W += w[u];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = w[u] != 0.f ? fmaf(w[u], to_f32(v[u][e]), acc[e]) : acc[e];
     }
   }
   const float inv = W > 0.f ? 1.f / W : 0.f;
-  T* orow = static_cast<T*>(a.out) + (((int64_t)b * a.Nq + a.q0 + qq) * a.Hq + h) * D;
+  T* orow = static_cast<T*>(a.out) + (((int64_t)b * a.Nq + a.q0 + qq) * a.Hq + h) * D + sub * 8;
+  typename Pack8<T>::type ov;
 #pragma unroll
-  for (int u = 0; u < VPL; ++u) orow[lane * VPL + u] = from_f32<T>(acc[u] * inv);
-  if (lane == 0 && a.lse)
+  for (int e = 0; e < 8; ++e) ov[e] = from_f32<T>(acc[e] * inv);
+  if constexpr (sizeof(T) == 2) {
+    *reinterpret_cast<bf16x8*>(orow) = ov;
+  } else {
+    *reinterpret_cast<f32x4*>(orow) = f32x4{ov[0], ov[1], ov[2], ov[3]};
+    *reinterpret_cast<f32x4*>(orow + 4) = f32x4{ov[4], ov[5], ov[6], ov[7]};
+  }
+  if (sub == 0 && a.lse)
     a.lse[((int64_t)b * a.Nq + a.q0 + qq) * a.Hq + h] = W > 0.f ? M + log2_fast(W) * kLn2 : -__builtin_huge_valf();
 }
 
@@ -548,7 +602,8 @@ hipError_t launch_combine(const Shape& s, int q0, int nq, const Partials& part, 
   a.nq = nq;
   a.ids_slots = ids_slots ? 1 : 0;
   const int64_t rows = (int64_t)nq * s.Hq;
-  const dim3 grid((unsigned)((rows + 3) / 4), s.B);
+  const int rows_per_wg = 4 * (64 / (s.D / 8));
+  const dim3 grid((unsigned)((rows + rows_per_wg - 1) / rows_per_wg), s.B);
   prof_begin(st, kid);
   if (s.dtype == kBF16) {
     if (s.D == 64) hipLaunchKernelGGL((k_combine<bf16_t, 64>), grid, dim3(256), 0, st, a);

@@ -38,6 +38,31 @@ struct TileArgs {
 
 constexpr int kTileWaves = 8;
 
+// Global -> registers -> LDS staging of one 128-token key block (16-byte
+// chunks; CPR chunks per token row, row stride `rowb` bytes in HBM).
+template <int LOADS, int CPR, int CHUNKS, int NTHR>
+__device__ __forceinline__ void tile_gload(u32x4 (&stage)[LOADS], const char* base, int j, int64_t rowb, int tid) {
+#pragma unroll
+  for (int u = 0; u < LOADS; ++u) {
+    const int c = tid + u * NTHR;
+    if (c < CHUNKS) {
+      const int row = c / CPR, col = c % CPR;
+      stage[u] = *reinterpret_cast<const u32x4*>(base + ((int64_t)j * kBk + row) * rowb + col * 16);
+    }
+  }
+}
+template <int LOADS, int CPR, int CHUNKS, int NTHR, int PITCH>
+__device__ __forceinline__ void tile_lstore(const u32x4 (&stage)[LOADS], char* buf, int tid) {
+#pragma unroll
+  for (int u = 0; u < LOADS; ++u) {
+    const int c = tid + u * NTHR;
+    if (c < CHUNKS) {
+      const int row = c / CPR, col = c % CPR;
+      *reinterpret_cast<u32x4*>(buf + row * PITCH + col * 16) = stage[u];
+    }
+  }
+}
+
 template <typename T, int DI, int NT, int KMAX, bool WRITE_S, bool TOPK>
 __global__ void __launch_bounds__(kTileWaves * 64) k_index_tile(TileArgs a) {
   constexpr int WAVES = kTileWaves;
@@ -82,33 +107,13 @@ __global__ void __launch_bounds__(kTileWaves * 64) k_index_tile(TileArgs a) {
   list.init();
 
   if (j_end > 0) {
-    uint4 stage[LOADS];
-    auto gload = [&](int j) {
-#pragma unroll
-      for (int u = 0; u < LOADS; ++u) {
-        const int c = tid + u * NTHR;
-        if (c < CHUNKS) {
-          const int row = c / CPR, col = c % CPR;
-          stage[u] = *reinterpret_cast<const uint4*>(ikb + ((int64_t)j * kBk + row) * krow * (int64_t)sizeof(T) + col * 16);
-        }
-      }
-    };
-    auto lstore = [&](int buf) {
-#pragma unroll
-      for (int u = 0; u < LOADS; ++u) {
-        const int c = tid + u * NTHR;
-        if (c < CHUNKS) {
-          const int row = c / CPR, col = c % CPR;
-          *reinterpret_cast<uint4*>(&lds[buf][row * PITCH + col * 16]) = stage[u];
-        }
-      }
-    };
-    gload(0);
-    lstore(0);
+    u32x4 stage[LOADS];
+    tile_gload<LOADS, CPR, CHUNKS, NTHR>(stage, ikb, 0, krow * (int64_t)sizeof(T), tid);
+    tile_lstore<LOADS, CPR, CHUNKS, NTHR, PITCH>(stage, lds[0], tid);
     __syncthreads();
     for (int j = 0; j < j_end; ++j) {
       const int cur = j & 1;
-      if (j + 1 < j_end) gload(j + 1);
+      if (j + 1 < j_end) tile_gload<LOADS, CPR, CHUNKS, NTHR>(stage, ikb, j + 1, krow * (int64_t)sizeof(T), tid);
       float run[NT];
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) run[nt] = -__builtin_huge_valf();
@@ -140,7 +145,7 @@ __global__ void __launch_bounds__(kTileWaves * 64) k_index_tile(TileArgs a) {
         if (TOPK) list.offer(own, j);
         if (WRITE_S) a.scores[(((int64_t)b * a.Hkv + g) * a.Nq + q_own) * a.nblk + j] = own;
       }
-      if (j + 1 < j_end) lstore(cur ^ 1);
+      if (j + 1 < j_end) tile_lstore<LOADS, CPR, CHUNKS, NTHR, PITCH>(stage, lds[cur ^ 1], tid);
       __syncthreads();
     }
   }

@@ -94,6 +94,10 @@ int qouter_splits(const msa::Shape& s) {
 
 // ---- workspace layout ------------------------------------------------------
 
+// Partial outputs are kept in the input dtype (bf16 partials add one bf16
+// rounding of a normalised output, well inside the bf16 output tolerance).
+size_t elem_bytes(const msa::Shape& s) { return s.dtype == msa::kBF16 ? 2 : 4; }
+
 struct KvLayout {
   size_t offsets, entries, item_count, items, inv_scratch, part_o, part_lse, total;
 };
@@ -114,7 +118,7 @@ KvLayout kv_layout(const msa::Shape& s, int nc) {
   L.inv_scratch = off;
   off += align_up(msa::invert_ws_bytes(s, p));
   L.part_o = off;
-  off += align_up((size_t)s.B * nc * s.Hq * s.topk * s.D * 4);
+  off += align_up((size_t)s.B * nc * s.Hq * s.topk * s.D * elem_bytes(s));
   L.part_lse = off;
   off += align_up((size_t)s.B * nc * s.Hq * s.topk * 4);
   L.total = off;
@@ -123,7 +127,7 @@ KvLayout kv_layout(const msa::Shape& s, int nc) {
 
 size_t qo_bytes(const msa::Shape& s, int nc, int nsplit) {
   if (nsplit <= 1) return 0;
-  return align_up((size_t)s.B * nc * s.Hq * nsplit * s.D * 4) + align_up((size_t)s.B * nc * s.Hq * nsplit * 4);
+  return align_up((size_t)s.B * nc * s.Hq * nsplit * s.D * elem_bytes(s)) + align_up((size_t)s.B * nc * s.Hq * nsplit * 4);
 }
 
 size_t attn_bytes(const msa_problem_t* p, const msa::Shape& s, int nc) {
@@ -181,7 +185,7 @@ msa_status_t run_attention(const msa_problem_t* p, const msa::Shape& s, const vo
     inv.item_count = reinterpret_cast<int32_t*>(w + L.item_count);
     inv.items = reinterpret_cast<int4*>(w + L.items);
     msa::Partials part;
-    part.o = reinterpret_cast<float*>(w + L.part_o);
+    part.o = w + L.part_o;
     part.lse = reinterpret_cast<float*>(w + L.part_lse);
     part.S = s.topk;
     for (int q0 = 0; q0 < s.Nq && e == hipSuccess; q0 += nc) {
@@ -193,8 +197,8 @@ msa_status_t run_attention(const msa_problem_t* p, const msa::Shape& s, const vo
   } else {
     const int ns = qouter_splits(s);
     msa::Partials part;
-    part.o = reinterpret_cast<float*>(w);
-    part.lse = reinterpret_cast<float*>(w + (ns > 1 ? align_up((size_t)s.B * nc * s.Hq * ns * s.D * 4) : 0));
+    part.o = w;
+    part.lse = reinterpret_cast<float*>(w + (ns > 1 ? align_up((size_t)s.B * nc * s.Hq * ns * s.D * elem_bytes(s)) : 0));
     part.S = ns;
     for (int q0 = 0; q0 < s.Nq && e == hipSuccess; q0 += nc) {
       const int nq = std::min(nc, s.Nq - q0);

@@ -60,10 +60,10 @@ hipError_t launch_invert(const Shape& s, const InvertPlan& p, const int32_t* ids
                          void* ws, hipStream_t st);
 
 // Main Branch -----------------------------------------------------------------
-// Partial results per (b, i, h, slot): normalised output o (fp32, D values) and
-// the log-sum-exp of the slot's scaled logits.
+// Partial results per (b, i, h, slot): normalised output o (D values in the
+// input dtype) and the log-sum-exp (fp32) of the slot's scaled logits.
 struct Partials {
-  float* o;    // [B, nq, Hq, S, D]
+  void* o;     // [B, nq, Hq, S, D]
   float* lse;  // [B, nq, Hq, S]
   int S;       // slots per (query, head)
 };
