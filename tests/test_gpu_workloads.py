@@ -1,0 +1,107 @@
+"""GPU parity at the full sizes of the five measured workloads, in the launch
+configuration bench.py times (msa_forward, AUTO schedule, full workspace).
+
+The oracle evaluates a stratified sample of queries (first, last, block
+boundaries, evenly spaced); the selection of every sampled (query, group) row
+must match (tie band allowed and counted), and attention is checked on the
+sampled rows after substituting the oracle's selection into the GPU's table
+(so selection ties cannot mask attention errors).
+"""
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_long_bk_amd import api, inputs
+from oracle import oracle as O
+
+from tests.parity import assert_attention, check_selection, host, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def sample_queries(wl, n):
+    Bk = wl.block_size
+    qs = set(np.linspace(0, wl.n_q - 1, n).astype(int).tolist())
+    qs |= {0, wl.n_q - 1}
+    # queries just before / at / after a block boundary
+    for p in np.linspace(wl.q_offset, wl.q_offset + wl.n_q - 1, 8).astype(int):
+        b = (p // Bk) * Bk
+        for pos in (b - 1, b, b + 1):
+            if wl.q_offset <= pos < wl.q_offset + wl.n_q:
+                qs.add(pos - wl.q_offset)
+    return np.array(sorted(qs), dtype=np.int64)
+
+
+def run_workload(name, n_sample, batches=None, scheds=("auto",)):
+    wl = inputs.WORKLOADS[name]
+    print(f"[{name}] generating", flush=True)
+    x = inputs.generate(wl, device="cuda")
+    p = api.problem_of(wl, sched="auto")
+    ids, out, lse = api.forward(p, x["q"], x["k"], x["v"], x["iq"], x["ik"])
+    torch.cuda.synchronize()
+    print(f"[{name}] forward done", flush=True)
+    qi = sample_queries(wl, n_sample)
+    batches = batches if batches is not None else list(range(wl.batch))
+    ids_fixed = ids.clone()
+    stats = dict(exact=0, tie=0, fail=0)
+    ora = {}
+    for b in batches:
+        sub = wl.with_(batch=1)
+        prob = O.problem_of(sub)
+        hx = {k: host(v[b:b + 1]) for k, v in x.items()}
+        rows = np.stack([np.zeros_like(qi), qi], axis=1)
+        s = O.block_scores(prob, hx["iq"], hx["ik"], rows)
+        ids_o = O.select(prob, s, rows)
+        got = host(ids[b, qi]).numpy()
+        res = check_selection(sub, got, ids_o, s, rows=rows)
+        for k in stats:
+            stats[k] += res[k]
+        assert res["fail"] == 0, (name, b, res)
+        ids_fixed[b, qi] = torch.from_numpy(ids_o).cuda()
+        o_o, l_o = O.attend(prob, hx["q"], hx["k"], hx["v"], ids_o, rows)
+        ora[b] = (o_o, l_o)
+        print(f"[{name}] b={b}: oracle done, selection {res}", flush=True)
+    print(f"[{name}] selection over {len(batches)}x{len(qi)} queries x {wl.h_kv} groups: {stats}", flush=True)
+    if wl.hot_frac > 0:
+        hot, _ = inputs.hot_blocks(wl)
+        is_hot = torch.zeros(wl.nblk, dtype=torch.bool, device="cuda")
+        is_hot[hot.cuda()] = True
+        valid = ids >= 0
+        frac = (is_hot[ids.clamp(min=0).long()] & valid).sum().item() / valid.sum().item()
+        print(f"[{name}] fraction of picks on the {len(hot)} hot blocks: {frac:.3f}", flush=True)
+    for sched in scheds:
+        ps = api.problem_of(wl, sched=sched)
+        o2, l2 = api.sparse_attention(ps, x["q"], x["k"], x["v"], ids_fixed)
+        torch.cuda.synchronize()
+        for b in batches:
+            o_o, l_o = ora[b]
+            mx, rl = assert_attention(wl.dtype, to_f64(o2[b, qi]), o_o, host(l2[b, qi]).numpy(), l_o,
+                                      what=f"{name}/{sched}/b{b}")
+            print(f"[{name}] attention {sched} b={b}: max-abs {mx:.2e} rel-L2 {rl:.2e}", flush=True)
+        del o2, l2
+    del x, ids, out, lse, ids_fixed
+    gc.collect()
+    torch.cuda.empty_cache()
+    return stats
+
+
+def test_tiny_f32_4k():
+    run_workload("tiny_f32_4k", 4096, scheds=("auto", "kv_outer", "q_outer"))
+
+
+def test_prefill_32k():
+    run_workload("prefill_32k", 256, scheds=("auto", "q_outer"))
+
+
+def test_skewed_prefill_128k():
+    run_workload("skewed_prefill_128k", 128)
+
+
+def test_chunk_16k_at_1m():
+    run_workload("chunk_16k_at_1m", 24, scheds=("kv_outer", "q_outer"))
+
+
+def test_decode_16x1m():
+    run_workload("decode_16x1m", 1, batches=[0, 7, 15], scheds=("auto", "kv_outer"))
