@@ -31,7 +31,7 @@ METRIC = "MSA fwd effective TFLOP/s (selected tokens) & decode µs/token @1M ctx
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 matrix
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+PROFILES = os.path.join(ROOT, "profiles")
 
 
 def selected_tokens(wl, ids):
@@ -49,6 +49,25 @@ def selected_tokens(wl, ids):
 def attention_flops(wl, ids):
     G = wl.h_q // wl.h_kv
     return 4.0 * wl.d * G * selected_tokens(wl, ids)
+
+
+def attention_bytes(wl, ids):
+    """Algorithmic HBM bytes of the KV-outer attention and of the combine, per
+    launch over the whole problem: every selected (b, i, g, block) moves the
+    group's G query rows in and G partial rows (bf16/fp32 output + fp32 lse)
+    out; each selected key block is read once per (b, g); the combine reads
+    every partial, the block ids and writes the output and lse."""
+    e = 2 if wl.dtype == "bf16" else 4
+    G = wl.h_q // wl.h_kv
+    valid = ids >= 0
+    nnz = int(valid.sum().item())
+    flat = (torch.arange(wl.batch * wl.h_kv, device=ids.device).view(wl.batch, 1, wl.h_kv, 1) * wl.nblk
+            + ids.clamp(min=0).long())
+    uniq = int(torch.unique(flat[valid]).numel())
+    part_row = wl.d * e + 4
+    kv = nnz * G * wl.d * e + nnz * G * part_row + uniq * wl.block_size * wl.d * e * 2 + nnz * 4
+    comb = nnz * G * part_row + ids.numel() * 4 + wl.batch * wl.n_q * wl.h_q * (wl.d * e + 4)
+    return {"attn_kvouter": kv, "combine": comb, "selected_group_blocks": nnz}
 
 
 def index_flops(wl):
@@ -88,11 +107,10 @@ def measured_traffic(kernel, workload):
     """HBM bytes per launch from the committed rocprofv3 counter runs, if they
     were taken on the current kernel source (else None)."""
     try:
-        data = json.load(open(TRAFFIC_FILE))
+        rec = json.load(open(os.path.join(PROFILES, f"{kernel}_{workload}_traffic.json")))
     except (OSError, ValueError):
         return None
-    rec = data.get(workload, {}).get(kernel)
-    if not rec or rec.get("source_hash") != source_hash(rec.get("sources", [])):
+    if rec.get("source_hash") != source_hash(rec.get("sources", [])):
         return None
     return rec.get("bytes_per_launch")
 
@@ -139,8 +157,10 @@ def run_prefill(args):
     torch.cuda.synchronize()
     fl_attn = attention_flops(wl, ids)
     fl_idx = index_flops(wl)
+    nbytes = attention_bytes(wl, ids)
     ms, wall_ms, kern = time_steps(step, args.steps, args.warmup)
-    res = dict(wl=wl, x=x, ms=ms, wall_ms=wall_ms, kern=kern, fl_attn=fl_attn, fl_idx=fl_idx, ws=ws.numel())
+    res = dict(wl=wl, x=x, ms=ms, wall_ms=wall_ms, kern=kern, fl_attn=fl_attn, fl_idx=fl_idx, ws=ws.numel(),
+               bytes=nbytes)
     del ws, out, lse
     return res
 
@@ -185,7 +205,9 @@ def main():
     ap.add_argument("--sched", default="auto", choices=["auto", "kv_outer", "q_outer"])
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=1024)
+    ap.add_argument("--cpu-sample", type=int, default=8192)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (reference for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the MSA forward path here is a single-GPU build "
@@ -193,13 +215,29 @@ def main():
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
 
+    if args.calib_copy_mib:
+        src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     r = run_prefill(args)
     wl, kern = r["wl"], r["kern"]
     value = r["fl_attn"] / r["ms"] / 1e9  # TFLOP/s
     peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
     dom = max(kern, key=lambda k: kern[k][0] * kern[k][1])
-    # algorithmic work of the dominant kernel per launch
-    if dom.startswith("attn_"):
+    # Algorithmic work of the dominant kernel per launch.  The KV-outer kernel
+    # moves (Q rows + partials) ~ 2*(2D+4)*G bytes per selected (query, group,
+    # block) against 4*D*G*128 flops: ~127 flop/B at d=128, below the MI355X
+    # balance of ~312 flop/B, so its roof is HBM; the index kernel's is MFMA.
+    bytes_kv = r["bytes"]["attn_kvouter"]
+    if dom == "attn_kvouter":
+        achieved = bytes_kv / kern[dom][1] / kern[dom][0] / 1e6
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    elif dom == "combine":
+        achieved = r["bytes"]["combine"] / kern[dom][1] / kern[dom][0] / 1e6
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    elif dom.startswith("attn_"):
         achieved = r["fl_attn"] / kern[dom][1] / kern[dom][0] / 1e9
         roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s"}
     elif dom.startswith("index_tile"):
@@ -208,6 +246,7 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": None, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["kernel"] = dom
+    roof["algorithmic_bytes_per_launch"] = bytes_kv if dom == "attn_kvouter" else None
     roof["frac"] = roof["achieved"] / roof["peak"] if roof["achieved"] else None
     roof["traffic"] = measured_traffic(dom, wl.name)
     line = {
@@ -220,6 +259,11 @@ def main():
         "roofline": roof,
         "attention_tflops_per_step": r["fl_attn"] / 1e12, "index_tflops_per_step": r["fl_idx"] / 1e12,
         "index_TFLOPs": None, "wall_ms_per_step": r["wall_ms"],
+        "attn_kvouter_TFLOPs": (r["fl_attn"] / kern["attn_kvouter"][0] / 1e9) if "attn_kvouter" in kern else None,
+        "attn_kvouter_GBs": (r["bytes"]["attn_kvouter"] / kern["attn_kvouter"][0] / 1e6)
+        if "attn_kvouter" in kern else None,
+        "combine_GBs": (r["bytes"]["combine"] / kern["combine"][0] / 1e6) if "combine" in kern else None,
+        "algorithmic_bytes": r["bytes"],
         "kernels_ms": {k: round(v[0], 4) for k, v in kern.items()},
         "kernel_launches_per_step": {k: v[1] for k, v in kern.items()},
         "workspace_bytes": r["ws"],

@@ -47,52 +47,86 @@ struct KvLds {
   static constexpr int BYTES = KBYTES + D * VPITCH;
 };
 
-// Stage K_j and V_j^T of one (b, g) into LDS.  256 threads.  Rows past n_k are
-// zero-filled (they are masked anyway).
+// Staging of K_j and V_j^T of one (b, g) into LDS by 256 threads, split into
+// a global-load phase (into registers) and an LDS-store phase so that callers
+// can overlap other loads with it.  Rows past n_k are zero-filled (they are
+// masked anyway).
+template <typename T, int D>
+struct KvStage {
+  using L = KvLds<T, D>;
+  static constexpr int CPR = D * (int)sizeof(T) / 16;  // 16-byte chunks per K row
+  static constexpr int KCH = kBk * CPR;
+  static constexpr int KLD = (KCH + 255) / 256;
+  static constexpr int DCH = D / 8;         // 8-element chunks per V row
+  static constexpr int KG = 256 / DCH;      // groups of 4 keys per pass
+  static constexpr int PASSES = kBk / (4 * KG);
+  u32x4 kr[KLD];
+  frag_t<T> vr[PASSES][4];
+
+  __device__ __forceinline__ void load(const T* kbase, const T* vbase, int64_t tok_stride, int j, int n_k, int tid) {
+#pragma unroll
+    for (int u = 0; u < KLD; ++u) {
+      const int c = tid + u * 256;
+      const int row = c / CPR, col = c % CPR;
+      const int64_t t = (int64_t)j * kBk + row;
+      kr[u] = u32x4{};
+      if (c < KCH && t < n_k)
+        kr[u] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(kbase + t * tok_stride) + col * 16);
+    }
+    const int dch = tid % DCH, kg = tid / DCH;
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t t = (int64_t)j * kBk + (ps * KG + kg) * 4 + r;
+        vr[ps][r] = t < n_k ? load8(vbase + t * tok_stride + dch * 8) : zero_frag<T>();
+      }
+  }
+
+  // V^T rows get four consecutive keys per store.
+  __device__ __forceinline__ void store(char* lds, int tid) const {
+#pragma unroll
+    for (int u = 0; u < KLD; ++u) {
+      const int c = tid + u * 256;
+      if (c < KCH) *reinterpret_cast<u32x4*>(lds + (c / CPR) * L::KPITCH + (c % CPR) * 16) = kr[u];
+    }
+    char* vt = lds + L::KBYTES;
+    const int dch = tid % DCH, kg = tid / DCH;
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps) {
+      const int key0 = (ps * KG + kg) * 4;
+      if constexpr (sizeof(T) == 2) {
+        // 2x2 transposes of 16-bit halves with byte permutes (v_perm_b32).
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          uint32_t x0 = __builtin_bit_cast(u32x4, vr[ps][0])[w], x1 = __builtin_bit_cast(u32x4, vr[ps][1])[w];
+          uint32_t x2 = __builtin_bit_cast(u32x4, vr[ps][2])[w], x3 = __builtin_bit_cast(u32x4, vr[ps][3])[w];
+          const uint2 lo = make_uint2(__builtin_amdgcn_perm(x1, x0, 0x05040100u), __builtin_amdgcn_perm(x3, x2, 0x05040100u));
+          const uint2 hi = make_uint2(__builtin_amdgcn_perm(x1, x0, 0x07060302u), __builtin_amdgcn_perm(x3, x2, 0x07060302u));
+          *reinterpret_cast<uint2*>(vt + (dch * 8 + 2 * w) * L::VPITCH + key0 * 2) = lo;
+          *reinterpret_cast<uint2*>(vt + (dch * 8 + 2 * w + 1) * L::VPITCH + key0 * 2) = hi;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          typename Pack4<T>::type w;
+          w[0] = vr[ps][0][e];
+          w[1] = vr[ps][1][e];
+          w[2] = vr[ps][2][e];
+          w[3] = vr[ps][3][e];
+          *reinterpret_cast<typename Pack4<T>::type*>(vt + (dch * 8 + e) * L::VPITCH + key0 * (int)sizeof(T)) = w;
+        }
+      }
+    }
+  }
+};
+
 template <typename T, int D>
 __device__ __forceinline__ void stage_kv(char* lds, const T* kbase, const T* vbase, int64_t tok_stride, int j,
                                          int n_k, int tid) {
-  using L = KvLds<T, D>;
-  // K: 16-byte chunks, row-major copy.
-  constexpr int CPR = D * (int)sizeof(T) / 16;
-  constexpr int KCH = kBk * CPR;
-#pragma unroll
-  for (int u = 0; u < (KCH + 255) / 256; ++u) {
-    const int c = tid + u * 256;
-    if (c < KCH) {
-      const int row = c / CPR, col = c % CPR;
-      const int64_t t = (int64_t)j * kBk + row;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (t < n_k) v = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(kbase + t * tok_stride) + col * 16);
-      *reinterpret_cast<uint4*>(lds + row * L::KPITCH + col * 16) = v;
-    }
-  }
-  // V^T: each thread takes 8 d-values of 4 consecutive keys and writes four
-  // keys per transposed row at once.
-  constexpr int DCH = D / 8;             // 8-element chunks per key row
-  constexpr int KG = 256 / DCH;          // key groups of 4 per pass
-  constexpr int PASSES = kBk / (4 * KG);
-  char* vt = lds + L::KBYTES;
-  const int dch = tid % DCH, kg = tid / DCH;
-#pragma unroll
-  for (int ps = 0; ps < PASSES; ++ps) {
-    const int key0 = (ps * KG + kg) * 4;
-    frag_t<T> x[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t t = (int64_t)j * kBk + key0 + r;
-      x[r] = t < n_k ? load8(vbase + t * tok_stride + dch * 8) : zero_frag<T>();
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      typename Pack4<T>::type w;
-      w[0] = x[0][e];
-      w[1] = x[1][e];
-      w[2] = x[2][e];
-      w[3] = x[3][e];
-      *reinterpret_cast<typename Pack4<T>::type*>(vt + (dch * 8 + e) * L::VPITCH + key0 * (int)sizeof(T)) = w;
-    }
-  }
+  KvStage<T, D> st;
+  st.load(kbase, vbase, tok_stride, j, n_k, tid);
+  st.store(lds, tid);
 }
 
 // A fragment of V^T for k-step (mt, a): row d, keys 32mt+16a+4h+[0..3] and +8.
@@ -129,10 +163,10 @@ __device__ __forceinline__ void block_tile(const char* lds, const frag_t<T> (&qf
   f32x16 s[4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
-    s[mt] = f32x16{};
     const T* arow = reinterpret_cast<const T*>(lds + (mt * 32 + (lane & 31)) * L::KPITCH) + 8 * half;
+    s[mt] = mma0(load8(arow), qf[0]);
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) mma(load8(arow + 16 * ks), qf[ks], s[mt]);
+    for (int ks = 1; ks < D / 16; ++ks) mma(load8(arow + 16 * ks), qf[ks], s[mt]);
   }
   __builtin_amdgcn_sched_barrier(0);
   if (need_mask) {
@@ -146,7 +180,7 @@ __device__ __forceinline__ void block_tile(const char* lds, const frag_t<T> (&qf
   }
   float mx = -__builtin_huge_valf();
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) mx = fmaxf(mx, max16(s[mt]));
+  for (int mt = 0; mt < 4; ++mt) mx = max16(s[mt], mx);
   mx = fmaxf(mx, xor_shfl(mx, 32));
   const float mref = mx == -__builtin_huge_valf() ? 0.f : mx * c_log2;
   float sum = 0.f;
@@ -161,8 +195,6 @@ __device__ __forceinline__ void block_tile(const char* lds, const frag_t<T> (&qf
   sum += xor_shfl(sum, 32);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16{};
-#pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
@@ -170,7 +202,11 @@ __device__ __forceinline__ void block_tile(const char* lds, const frag_t<T> (&qf
 #pragma unroll
       for (int e = 0; e < 8; ++e) pb[e] = from_f32<T>(s[mt][8 * a + e]);
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) mma(vt_frag<T, D>(lds, 32 * dt + (lane & 31), mt, a, half), pb, o[dt]);
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const frag_t<T> va = vt_frag<T, D>(lds, 32 * dt + (lane & 31), mt, a, half);
+        if (mt == 0 && a == 0) o[dt] = mma0(va, pb);
+        else mma(va, pb, o[dt]);
+      }
     }
   m = mx == -__builtin_huge_valf() ? -__builtin_huge_valf() : mref;
   l = sum;
@@ -181,22 +217,27 @@ struct TileRows {
   bool valid;
   int qq, slot, h;
 };
-__device__ __forceinline__ TileRows tile_rows(const int32_t* ent, int tile, int nrows, int G, int topk, int g) {
-  const int r = tile * 32 + (threadIdx.x & 31);
+// e = qq*topk + slot is split with a multiply by ceil(2^40/topk): exact for
+// 0 <= e < 2^31 and topk <= 32 (the rounding error stays below 2^-9 < 1/topk).
+__device__ __forceinline__ TileRows rows_of(int e, bool valid, int r, int gshift, int topk, uint64_t topk_magic,
+                                           int g) {
   TileRows t;
-  t.valid = r < nrows;
-  const int e = t.valid ? ent[r / G] : 0;
-  t.qq = e / topk;
-  t.slot = e % topk;
-  t.h = g * G + r % G;
+  t.valid = valid;
+  t.qq = (int)(((uint64_t)(uint32_t)e * topk_magic) >> 40);
+  t.slot = e - t.qq * topk;
+  t.h = (g << gshift) + (r & ((1 << gshift) - 1));
   return t;
 }
+// A work item holds at most 512 (query, head) rows: 512 / G entries.
+constexpr int kMaxItemEntries = 512;
+// Rows past the item's end read a valid row (entry 0 of the chunk): their
+// results are never stored, so no branch is needed around the loads.
 template <typename T, int D>
 __device__ __forceinline__ void load_q_rows(frag_t<T> (&qf)[D / 16], const T* qbase, const TileRows& t, int b, int Nq,
                                             int Hq, int q0, int half) {
   const T* qrow = qbase + (((int64_t)b * Nq + q0 + t.qq) * Hq + t.h) * D + 8 * half;
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) qf[ks] = t.valid ? load8(qrow + 16 * ks) : zero_frag<T>();
+  for (int ks = 0; ks < D / 16; ++ks) qf[ks] = load8(qrow + 16 * ks);
 }
 // Partial store.  (Non-temporal stores were measured several times slower
 // here: the partial-line writes then miss the L2 write combining.)
@@ -214,8 +255,9 @@ struct KvArgs {
   const int4* items;
   void* part_o;  // [B, nq, Hq, S, D] in the input dtype
   float* part_lse;
-  int Nq, Nk, Hq, Hkv, G, topk, S, q0, nq, items_cap;
+  int Nq, Nk, Hq, Hkv, G, topk, S, q0, nq, items_cap, gshift;
   int64_t q_offset;
+  uint64_t topk_magic;  // ceil(2^40 / topk)
   float c_log2;  // softmax scale * log2(e)
 };
 
@@ -223,6 +265,7 @@ template <typename T, int D>
 __global__ void __launch_bounds__(256, 2) k_attn_kvouter(KvArgs a) {
   using L = KvLds<T, D>;
   __shared__ __attribute__((aligned(16))) char lds[L::BYTES];
+  __shared__ int32_t ent_lds[kMaxItemEntries];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
   const int bg = blockIdx.y, b = bg / a.Hkv, g = bg % a.Hkv;
   // Items of one (b, g) are spread so that each XCD (workgroup id mod 8) runs a
@@ -239,19 +282,39 @@ __global__ void __launch_bounds__(256, 2) k_attn_kvouter(KvArgs a) {
   const int64_t tok_stride = (int64_t)a.Hkv * D;
   const T* kb = static_cast<const T*>(a.k) + (int64_t)b * a.Nk * tok_stride + g * D;
   const T* vb = static_cast<const T*>(a.v) + (int64_t)b * a.Nk * tok_stride + g * D;
-  stage_kv<T, D>(lds, kb, vb, tok_stride, j, a.Nk, tid);
-  __syncthreads();
-
   const int32_t* ent = a.entries + (int64_t)bg * a.nq * a.topk + e0;
+  const int nent = e1 - e0;
   const T* qbase = static_cast<const T*>(a.q);
   const int64_t key0 = (int64_t)j * kBk;
+
+  // Prologue, ordered so that the loads overlap: (1) the entries (this lane's
+  // first row, and the item's list for LDS), (2) K_j / V_j into registers,
+  // (3) the first tile's query rows, then the LDS stores.  Vector-memory
+  // counters retire in order, so each wait only covers the older loads.
+  const int r0 = wave * 32 + (lane & 31);
+  const int e_first = r0 < nrows ? ent[r0 >> a.gshift] : 0;
+  static_assert(kMaxItemEntries == 512, "two entries per thread");
+  const int e_mine0 = tid < nent ? ent[tid] : 0;
+  const int e_mine1 = tid + 256 < nent ? ent[tid + 256] : 0;
+  __builtin_amdgcn_sched_barrier(0);
+  KvStage<T, D> stg;
+  stg.load(kb, vb, tok_stride, j, a.Nk, tid);
+  __builtin_amdgcn_sched_barrier(0);
   // Gathered query rows of tile t: row r = t*32 + lane%32 <-> (entry r/G, head r%G).
-  // The next tile's rows are fetched while the current one computes.
-  TileRows cur = tile_rows(ent, wave, nrows, a.G, a.topk, g);
+  TileRows cur = rows_of(e_first, r0 < nrows, r0, a.gshift, a.topk, a.topk_magic, g);
   frag_t<T> qf[D / 16];
   load_q_rows<T, D>(qf, qbase, cur, b, a.Nq, a.Hq, a.q0, half);
+  __builtin_amdgcn_sched_barrier(0);
+  if (tid < nent) ent_lds[tid] = e_mine0;
+  if (tid + 256 < nent) ent_lds[tid + 256] = e_mine1;
+  stg.store(lds, tid);
+  __syncthreads();
+
+  // The next tile's rows are fetched while the current one computes.
   for (int tile = wave; tile * 32 < nrows; tile += 4) {
-    const TileRows nxt = tile_rows(ent, tile + 4, nrows, a.G, a.topk, g);
+    const int rn = (tile + 4) * 32 + (lane & 31);
+    const int en = ent_lds[min(rn >> a.gshift, kMaxItemEntries - 1)];
+    const TileRows nxt = rows_of(rn < nrows ? en : 0, rn < nrows, rn, a.gshift, a.topk, a.topk_magic, g);
     frag_t<T> qn[D / 16];
     load_q_rows<T, D>(qn, qbase, nxt, b, a.Nq, a.Hq, a.q0, half);
     const int64_t pos = a.q_offset + a.q0 + cur.qq;
@@ -447,7 +510,7 @@ template <> struct Pack8<float> { using type = f32x8; };
 // D/8 lanes per (b, query, head) row, 8 output values per lane: merge the S
 // partials of the row by log-sum-exp weights.  Slots with block id -1
 // (KV-outer) or lse = -inf (empty query-outer split) carry no weight.
-template <typename T, int D>
+template <typename T, int D, int SMAX>
 __global__ void __launch_bounds__(256) k_combine(CombArgs a) {
   constexpr int LPH = D / 8;     // lanes per row
   constexpr int RPW = 64 / LPH;  // rows per wave
@@ -460,11 +523,20 @@ __global__ void __launch_bounds__(256) k_combine(CombArgs a) {
   const int64_t prow = ((int64_t)b * a.nq + qq) * a.Hq + h;
   const int32_t* sel = a.ids + (((int64_t)b * a.Nq + a.q0 + qq) * a.Hkv + g) * a.topk;
   const float* pl = a.part_lse + prow * a.S;
-  float M = -__builtin_huge_valf();
-  for (int s = 0; s < a.S; ++s) {
-    const bool ok = !a.ids_slots || sel[s] >= 0;
-    if (ok) M = fmaxf(M, pl[s]);
+  // All slot statistics are loaded at once (S <= SMAX).
+  float ls[SMAX];
+#pragma unroll
+  for (int s = 0; s < SMAX; ++s) {
+    ls[s] = -__builtin_huge_valf();
+    if (s < a.S) {
+      const int id = a.ids_slots ? sel[s] : 0;
+      const float x = pl[s];
+      if (id >= 0) ls[s] = x;
+    }
   }
+  float M = -__builtin_huge_valf();
+#pragma unroll
+  for (int s = 0; s < SMAX; ++s) M = fmaxf(M, ls[s]);
   const float Mref = M == -__builtin_huge_valf() ? 0.f : M;
   float acc[8];
 #pragma unroll
@@ -472,22 +544,23 @@ __global__ void __launch_bounds__(256) k_combine(CombArgs a) {
   float W = 0.f;
   const T* po = static_cast<const T*>(a.part_o) + prow * a.S * D + sub * 8;
   // Eight slots per round: all their loads are issued before any is used.
-  for (int s0 = 0; s0 < a.S; s0 += 8) {
-    frag_t<T> v[8];
-    float w[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int s = s0 + u;
-      const bool ok = s < a.S && (!a.ids_slots || sel[s] >= 0);
-      const float ls = ok ? pl[s] : -__builtin_huge_valf();
-      w[u] = ls == -__builtin_huge_valf() ? 0.f : exp2_fast((ls - Mref) * kLog2e);
-      v[u] = s < a.S ? load8(po + (int64_t)s * D) : zero_frag<T>();
-    }
+  for (int s0 = 0; s0 < SMAX; s0 += 8) {
+    if (s0 < a.S) {
+      frag_t<T> v[8];
+      float w[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      W += w[u];
+      for (int u = 0; u < 8; ++u) {
+        const int s = s0 + u;
+        w[u] = ls[s] == -__builtin_huge_valf() ? 0.f : exp2_fast((ls[s] - Mref) * kLog2e);
+        v[u] = s < a.S ? load8(po + (int64_t)s * D) : zero_frag<T>();
+      }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = w[u] != 0.f ? fmaf(w[u], to_f32(v[u][e]), acc[e]) : acc[e];
+      for (int u = 0; u < 8; ++u) {
+        W += w[u];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = w[u] != 0.f ? fmaf(w[u], to_f32(v[u][e]), acc[e]) : acc[e];
+      }
     }
   }
   const float inv = W > 0.f ? 1.f / W : 0.f;
@@ -531,6 +604,8 @@ hipError_t launch_attn_kvouter(const Shape& s, const InvertPlan& p, int q0, int 
   a.items_cap = p.items_cap;
   a.q_offset = s.q_offset;
   a.c_log2 = s.scale * kLog2e;
+  a.gshift = __builtin_ctz((unsigned)a.G);
+  a.topk_magic = ((uint64_t)1 << 40) / (uint64_t)s.topk + 1;
   const dim3 grid(p.items_cap, s.B * s.Hkv);
   prof_begin(st, kid);
   if (s.dtype == kBF16) {
@@ -583,6 +658,17 @@ hipError_t launch_attn_qouter(const Shape& s, int q0, int nq, int nsplit, const 
   return e;
 }
 
+template <int SMAX>
+static void combine_dispatch(const Shape& s, dim3 grid, const CombArgs& a, hipStream_t st) {
+  if (s.dtype == kBF16) {
+    if (s.D == 64) hipLaunchKernelGGL((k_combine<bf16_t, 64, SMAX>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((k_combine<bf16_t, 128, SMAX>), grid, dim3(256), 0, st, a);
+  } else {
+    if (s.D == 64) hipLaunchKernelGGL((k_combine<float, 64, SMAX>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((k_combine<float, 128, SMAX>), grid, dim3(256), 0, st, a);
+  }
+}
+
 hipError_t launch_combine(const Shape& s, int q0, int nq, const Partials& part, const int32_t* ids,
                           bool ids_slots, void* out, float* lse, hipStream_t st) {
   static const int kid = prof_register("combine");
@@ -605,13 +691,9 @@ hipError_t launch_combine(const Shape& s, int q0, int nq, const Partials& part, 
   const int rows_per_wg = 4 * (64 / (s.D / 8));
   const dim3 grid((unsigned)((rows + rows_per_wg - 1) / rows_per_wg), s.B);
   prof_begin(st, kid);
-  if (s.dtype == kBF16) {
-    if (s.D == 64) hipLaunchKernelGGL((k_combine<bf16_t, 64>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((k_combine<bf16_t, 128>), grid, dim3(256), 0, st, a);
-  } else {
-    if (s.D == 64) hipLaunchKernelGGL((k_combine<float, 64>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((k_combine<float, 128>), grid, dim3(256), 0, st, a);
-  }
+  if (part.S <= 8) combine_dispatch<8>(s, grid, a, st);
+  else if (part.S <= 16) combine_dispatch<16>(s, grid, a, st);
+  else combine_dispatch<32>(s, grid, a, st);
   const hipError_t e = hipGetLastError();
   prof_end(st, kid);
   return e;

@@ -42,6 +42,17 @@ __device__ __forceinline__ void mma(const f32x8& a, const f32x8& b, f32x16& c) {
   for (int e = 0; e < 8; ++e) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], b[e], c, 0, 0, 0);
 }
 
+// Product with a zero accumulator (no register zeroing needed).
+__device__ __forceinline__ f32x16 mma0(const bf16x8& a, const bf16x8& b) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, f32x16{}, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mma0(const f32x8& a, const f32x8& b) {
+  f32x16 c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[0], b[0], f32x16{}, 0, 0, 0);
+#pragma unroll
+  for (int e = 1; e < 8; ++e) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], b[e], c, 0, 0, 0);
+  return c;
+}
+
 // 8 elements from a 16-byte aligned address (global or LDS).
 __device__ __forceinline__ bf16x8 load8(const bf16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
 __device__ __forceinline__ f32x8 load8(const float* p) {
@@ -58,11 +69,10 @@ __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
 
-__device__ __forceinline__ float max16(const f32x16& v) {
-  float m = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
-  m = fmaxf(m, fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
-  m = fmaxf(m, fmaxf(fmaxf(v[8], v[9]), fmaxf(v[10], v[11])));
-  m = fmaxf(m, fmaxf(fmaxf(v[12], v[13]), fmaxf(v[14], v[15])));
+// Running max over 16 values as a chain of three-input maxima (v_max3_f32).
+__device__ __forceinline__ float max16(const f32x16& v, float m = -__builtin_huge_valf()) {
+#pragma unroll
+  for (int e = 0; e < 16; e += 2) m = fmaxf(fmaxf(m, v[e]), v[e + 1]);
   return m;
 }
 
