@@ -266,6 +266,11 @@ __global__ void __launch_bounds__(256, 2) k_attn_kvouter(KvArgs a) {
   using L = KvLds<T, D>;
   __shared__ __attribute__((aligned(16))) char lds[L::BYTES];
   __shared__ int32_t ent_lds[kMaxItemEntries];
+  constexpr int ROWB = D * (int)sizeof(T);   // bytes of one partial row
+  constexpr int OPITCH = ROWB + 16;          // padded LDS row
+  constexpr int LPR = ROWB / 16;             // lanes per row on the way out
+  constexpr int RPS = 64 / LPR;              // rows per store instruction
+  __shared__ __attribute__((aligned(16))) char obuf[4][8 * OPITCH];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
   const int bg = blockIdx.y, b = bg / a.Hkv, g = bg % a.Hkv;
   // Items of one (b, g) are spread so that each XCD (workgroup id mod 8) runs a
@@ -325,20 +330,36 @@ __global__ void __launch_bounds__(256, 2) k_attn_kvouter(KvArgs a) {
     float m, l;
     f32x16 o[D / 32];
     block_tile<T, D>(lds, qf, a.c_log2, vis, need != 0, m, l, o);
-    if (cur.valid) {
-      const int64_t prow = (((int64_t)b * a.nq + cur.qq) * a.Hq + cur.h) * a.S + cur.slot;
-      T* po = static_cast<T*>(a.part_o) + prow * D;
-      const float inv = 1.f / l;
+    // Partial rows leave through LDS, 8 rows per pass, so that each store
+    // instruction writes four whole rows instead of an 8-byte piece of 32.
+    const int64_t prow = (((int64_t)b * a.nq + cur.qq) * a.Hq + cur.h) * a.S + cur.slot;
+    if (cur.valid && half == 0) a.part_lse[prow] = (m + log2_fast(l)) * kLn2;
+    const float inv = 1.f / l;
+    char* ob = obuf[wave];
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
+    for (int ps = 0; ps < 4; ++ps) {
+      if (((lane & 31) >> 3) == ps) {
+        char* orow = ob + ((lane & 7) * OPITCH);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          typename Pack4<T>::type w;
+        for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr) w[rr] = from_f32<T>(o[dt][4 * i + rr] * inv);
-          store_stream(po + 32 * dt + 8 * i + 4 * half, w);
-        }
-      if (half == 0) a.part_lse[prow] = (m + log2_fast(l)) * kLn2;
+          for (int i = 0; i < 4; ++i) {
+            typename Pack4<T>::type w;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) w[rr] = from_f32<T>(o[dt][4 * i + rr] * inv);
+            *reinterpret_cast<typename Pack4<T>::type*>(orow + (32 * dt + 8 * i + 4 * half) * (int)sizeof(T)) = w;
+          }
+      }
+      // lane -> (row ps*8 + lane/LPR + k*RPS, 16-byte chunk lane%LPR)
+#pragma unroll
+      for (int k = 0; k < 8 / RPS; ++k) {
+        const int rl = lane / LPR + k * RPS;
+        const int src = ps * 8 + rl;
+        const int64_t dst_row = __shfl(prow, src, 64);
+        const int ok = __shfl((int)cur.valid, src, 64);
+        const u32x4 v = *reinterpret_cast<const u32x4*>(ob + rl * OPITCH + (lane % LPR) * 16);
+        if (ok) *reinterpret_cast<u32x4*>(static_cast<char*>(a.part_o) + dst_row * ROWB + (lane % LPR) * 16) = v;
+      }
     }
     cur = nxt;
 #pragma unroll
