@@ -196,6 +196,41 @@ def run_decode(args):
             "kernels_ms": {k: round(v[0], 4) for k, v in kern.items()}}
 
 
+def run_crossover(args, chunks=(256, 512, 1024, 1460, 2048, 4096, 16384)):
+    """KV-outer vs query-outer attention time on the last `c` queries of the
+    1M-token chunked-prefill cache (2 % hot blocks).  reuse = c*k*Bk/Nk is the
+    average number of reads of a KV token, the quantity whose crossover the
+    Fireworks note on KV-stationary attention puts near 2.85."""
+    base = inputs.WORKLOADS["chunk_16k_at_1m"]
+    x = inputs.generate(base, device="cuda")
+    rows = []
+    for c in chunks:
+        wl = base.with_(n_q=c, q_offset=base.n_k - c)
+        q, iq = x["q"][:, -c:].contiguous(), x["iq"][:, -c:].contiguous()
+        p0 = api.problem_of(wl)
+        ids = api.index_topk(p0, iq, x["ik"])
+        torch.cuda.synchronize()
+        fl = attention_flops(wl, ids)
+        rec = {"n_q": c, "reuse": c * wl.topk * wl.block_size / wl.n_k}
+        for sched in ("kv_outer", "q_outer"):
+            p = api.problem_of(wl, sched=sched)
+            ws = api.alloc_workspace(p, api.OP_ATTENTION)
+            out = torch.empty_like(q)
+
+            def step():
+                api.sparse_attention(p, q, x["k"], x["v"], ids, out=out, want_lse=False, ws=ws)
+
+            ms, _, _ = time_steps(step, 5, 2)
+            rec[sched + "_ms"] = ms
+            rec[sched + "_TFLOPs"] = fl / ms / 1e9
+            del ws, out
+        rec["kv_over_q_speedup"] = rec["q_outer_ms"] / rec["kv_outer_ms"]
+        rows.append(rec)
+    del x
+    torch.cuda.empty_cache()
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -206,6 +241,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=8192)
+    ap.add_argument("--crossover", action="store_true",
+                    help="also time both attention schedules on query chunks at the end of a 1M-token cache")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (reference for HBM counters)")
     args = ap.parse_args()
@@ -275,6 +312,8 @@ def main():
         line["cpu_baseline"] = cpu_baseline(wl, r["x"], args.cpu_sample)
     del r
     torch.cuda.empty_cache()
+    if args.crossover:
+        line["crossover"] = run_crossover(args)
     if not args.no_decode:
         line["decode"] = run_decode(args)
     print(json.dumps(line), flush=True)
