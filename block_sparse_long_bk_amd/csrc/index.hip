@@ -63,6 +63,47 @@ __device__ __forceinline__ void tile_lstore(const u32x4 (&stage)[LOADS], char* b
   }
 }
 
+// Key blocks whose rows are 256 bytes (bf16 d_idx = 128, fp32 d_idx = 64) are
+// staged with direct global -> LDS loads (global_load_lds_dwordx4: lane L of
+// a wave writes 16 bytes at the wave's LDS base + 16 L), four blocks deep, no
+// staging registers.  Rows are unpadded; chunk c of row r sits at position
+// c ^ (r % 16), so the 16 rows read by a quarter-wave hit distinct banks.
+constexpr int kDmaBufs = 4;
+constexpr int kDmaRowBytes = 256;
+
+__device__ __forceinline__ void dma_issue_block(char* buf, const char* ikb, int j, int64_t rowb, int wave, int lane) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int slot = wave * 4 + u;  // 1 KB slot = 4 rows
+    const int r = slot * 4 + lane / 16;
+    const int c = (lane & 15) ^ (r & 15);
+    const char* src = ikb + ((int64_t)j * kBk + r) * rowb + c * 16;
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src), buf + slot * 1024, 16, 0, 0);
+  }
+}
+
+// Fragment of 8 elements starting at element e (multiple of 8) of row r of a
+// swizzled 256-byte-row buffer.
+template <typename T>
+__device__ __forceinline__ frag_t<T> dma_frag(const char* buf, int r, int e) {
+  const int c = e * (int)sizeof(T) / 16;
+  if constexpr (sizeof(T) == 2) {
+    return *reinterpret_cast<const bf16x8*>(buf + r * kDmaRowBytes + ((c ^ (r & 15)) << 4));
+  } else {
+    const f32x4 lo = *reinterpret_cast<const f32x4*>(buf + r * kDmaRowBytes + ((c ^ (r & 15)) << 4));
+    const f32x4 hi = *reinterpret_cast<const f32x4*>(buf + r * kDmaRowBytes + (((c + 1) ^ (r & 15)) << 4));
+    return f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+}
+
+// s_waitcnt immediate: wait until at most n vector-memory operations of this
+// wave are outstanding (expcnt and lgkmcnt left at their maximum).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 template <typename T, int DI, int NT, int KMAX, bool WRITE_S, bool TOPK>
 __global__ void __launch_bounds__(kTileWaves * 64) k_index_tile(TileArgs a) {
   constexpr int WAVES = kTileWaves;
@@ -74,7 +115,10 @@ __global__ void __launch_bounds__(kTileWaves * 64) k_index_tile(TileArgs a) {
   constexpr int CHUNKS = kBk * CPR;
   constexpr int NTHR = WAVES * 64;
   constexpr int LOADS = (CHUNKS + NTHR - 1) / NTHR;
-  __shared__ __attribute__((aligned(16))) char lds[2][kBk * PITCH];
+  constexpr bool DMA = ROW_BYTES == kDmaRowBytes && WAVES == 8;  // 8 waves x 4 loads = one block
+  constexpr int NBUF = DMA ? kDmaBufs : 2;
+  constexpr int BUFB = DMA ? kBk * kDmaRowBytes : kBk * PITCH;
+  __shared__ __attribute__((aligned(16))) char lds[NBUF][BUFB];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
   const int g = blockIdx.x % a.Hkv;
@@ -108,29 +152,56 @@ __global__ void __launch_bounds__(kTileWaves * 64) k_index_tile(TileArgs a) {
 
   if (j_end > 0) {
     u32x4 stage[LOADS];
-    tile_gload<LOADS, CPR, CHUNKS, NTHR>(stage, ikb, 0, krow * (int64_t)sizeof(T), tid);
-    tile_lstore<LOADS, CPR, CHUNKS, NTHR, PITCH>(stage, lds[0], tid);
-    __syncthreads();
+    if constexpr (DMA) {
+#pragma unroll
+      for (int sb = 0; sb < NBUF - 1; ++sb)
+        if (sb < j_end) dma_issue_block(lds[sb], ikb, sb, krow * (int64_t)sizeof(T), wave, lane);
+    } else {
+      tile_gload<LOADS, CPR, CHUNKS, NTHR>(stage, ikb, 0, krow * (int64_t)sizeof(T), tid);
+      tile_lstore<LOADS, CPR, CHUNKS, NTHR, PITCH>(stage, lds[0], tid);
+      __syncthreads();
+    }
     for (int j = 0; j < j_end; ++j) {
-      const int cur = j & 1;
-      if (j + 1 < j_end) tile_gload<LOADS, CPR, CHUNKS, NTHR>(stage, ikb, j + 1, krow * (int64_t)sizeof(T), tid);
+      const int cur = j % NBUF;
+      if constexpr (DMA) {
+        // Block j has landed once at most the loads of the later blocks in
+        // flight remain; then every wave's share is visible after the barrier.
+        if (!WRITE_S && j + NBUF - 2 < j_end) wait_vmcnt<4 * (NBUF - 2)>();
+        else wait_vmcnt<0>();
+        __syncthreads();
+        if (j + NBUF - 1 < j_end)
+          dma_issue_block(lds[(j + NBUF - 1) % NBUF], ikb, j + NBUF - 1, krow * (int64_t)sizeof(T), wave, lane);
+      } else {
+        if (j + 1 < j_end) tile_gload<LOADS, CPR, CHUNKS, NTHR>(stage, ikb, j + 1, krow * (int64_t)sizeof(T), tid);
+      }
       float run[NT];
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) run[nt] = -__builtin_huge_valf();
+      // The key fragments of M-tile mt+1 are read from LDS while mt multiplies.
+      const char* bufc = lds[cur];
+      const int arow = lane & 31;
+      auto frag = [&](int mt, int ks) -> frag_t<T> {
+        if constexpr (DMA) return dma_frag<T>(bufc, mt * 32 + arow, 16 * ks + 8 * half);
+        else return load8(reinterpret_cast<const T*>(bufc + (mt * 32 + arow) * PITCH) + 8 * half + 16 * ks);
+      };
+      frag_t<T> A[2][KSTEPS];
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) A[0][ks] = frag(0, ks);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
+        if (mt + 1 < 4) {
+#pragma unroll
+          for (int ks = 0; ks < KSTEPS; ++ks) A[(mt + 1) & 1][ks] = frag(mt + 1, ks);
+        }
         f32x16 acc[NT];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x16{};
-        const T* arow = reinterpret_cast<const T*>(&lds[cur][(mt * 32 + (lane & 31)) * PITCH]) + 8 * half;
+        for (int nt = 0; nt < NT; ++nt) acc[nt] = mma0(A[mt & 1][0], bq[nt][0]);
 #pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) {
-          const frag_t<T> A = load8(arow + 16 * ks);
+        for (int ks = 1; ks < KSTEPS; ++ks)
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt) mma(A, bq[nt][ks], acc[nt]);
-        }
+          for (int nt = 0; nt < NT; ++nt) mma(A[mt & 1][ks], bq[nt][ks], acc[nt]);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) run[nt] = fmaxf(run[nt], max16(acc[nt]));
+        for (int nt = 0; nt < NT; ++nt) run[nt] = max16(acc[nt], run[nt]);
       }
       // Each half of the wave saw 64 of the 128 keys; swap halves so that lane l
       // ends with the full block max of query q0 + wave*NT*32 + l.
@@ -145,8 +216,10 @@ __global__ void __launch_bounds__(kTileWaves * 64) k_index_tile(TileArgs a) {
         if (TOPK) list.offer(own, j);
         if (WRITE_S) a.scores[(((int64_t)b * a.Hkv + g) * a.Nq + q_own) * a.nblk + j] = own;
       }
-      if (j + 1 < j_end) tile_lstore<LOADS, CPR, CHUNKS, NTHR, PITCH>(stage, lds[cur ^ 1], tid);
-      __syncthreads();
+      if constexpr (!DMA) {
+        if (j + 1 < j_end) tile_lstore<LOADS, CPR, CHUNKS, NTHR, PITCH>(stage, lds[(j + 1) & 1], tid);
+        __syncthreads();
+      }
     }
   }
   if (TOPK && own_valid) {
