@@ -12,7 +12,7 @@
 // attention), which is exact up to rounding order.
 //
 //  * k_attn_kvouter -- KV-stationary (the paper's KV-outer path, abstract and
-//    "Key Contributions").  One workgroup per work item (block j, up to 512
+//    "Key Contributions").  One workgroup per work item (block j, up to 1024
 //    (query, head) rows that chose j).  K_j (row-major) and V_j (transposed) are
 //    staged once in LDS; 32-row tiles of the gathered queries stream through
 //        S^T = K_j Q^T      (MFMA: A = K rows from LDS, B = Q rows from HBM)
@@ -45,6 +45,14 @@ struct KvLds {
   static constexpr int VPITCH = kBk * (int)sizeof(T) + (sizeof(T) == 2 ? 8 : 16);
   static constexpr int KBYTES = kBk * KPITCH;
   static constexpr int BYTES = KBYTES + D * VPITCH;
+  // Byte offset of keys [4c, 4c+4) in V^T row d.  For 16-bit types the
+  // 4-key chunks are XOR-swizzled by (d / 32) % 4: the staging stores write
+  // rows 8 apart from neighbouring lanes, which would otherwise share banks;
+  // the MFMA fragment reads take 32 consecutive rows, which share the swizzle.
+  __device__ static __forceinline__ int vt_off(int d, int c) {
+    if constexpr (sizeof(T) == 2) return d * VPITCH + ((c ^ ((d >> 5) & 3)) * 4 * (int)sizeof(T));
+    else return d * VPITCH + c * 4 * (int)sizeof(T);
+  }
 };
 
 // Staging of K_j and V_j^T of one (b, g) into LDS by 256 threads, split into
@@ -103,8 +111,8 @@ struct KvStage {
           uint32_t x2 = __builtin_bit_cast(u32x4, vr[ps][2])[w], x3 = __builtin_bit_cast(u32x4, vr[ps][3])[w];
           const uint2 lo = make_uint2(__builtin_amdgcn_perm(x1, x0, 0x05040100u), __builtin_amdgcn_perm(x3, x2, 0x05040100u));
           const uint2 hi = make_uint2(__builtin_amdgcn_perm(x1, x0, 0x07060302u), __builtin_amdgcn_perm(x3, x2, 0x07060302u));
-          *reinterpret_cast<uint2*>(vt + (dch * 8 + 2 * w) * L::VPITCH + key0 * 2) = lo;
-          *reinterpret_cast<uint2*>(vt + (dch * 8 + 2 * w + 1) * L::VPITCH + key0 * 2) = hi;
+          *reinterpret_cast<uint2*>(vt + L::vt_off(dch * 8 + 2 * w, key0 / 4)) = lo;
+          *reinterpret_cast<uint2*>(vt + L::vt_off(dch * 8 + 2 * w + 1, key0 / 4)) = hi;
         }
       } else {
 #pragma unroll
@@ -114,7 +122,7 @@ struct KvStage {
           w[1] = vr[ps][1][e];
           w[2] = vr[ps][2][e];
           w[3] = vr[ps][3][e];
-          *reinterpret_cast<typename Pack4<T>::type*>(vt + (dch * 8 + e) * L::VPITCH + key0 * (int)sizeof(T)) = w;
+          *reinterpret_cast<typename Pack4<T>::type*>(vt + L::vt_off(dch * 8 + e, key0 / 4)) = w;
         }
       }
     }
@@ -133,10 +141,10 @@ __device__ __forceinline__ void stage_kv(char* lds, const T* kbase, const T* vba
 template <typename T, int D>
 __device__ __forceinline__ frag_t<T> vt_frag(const char* lds, int d, int mt, int a, int half) {
   using L = KvLds<T, D>;
-  const T* row = reinterpret_cast<const T*>(lds + L::KBYTES + d * L::VPITCH);
-  const int k0 = 32 * mt + 16 * a + 4 * half;
-  const typename Pack4<T>::type lo = *reinterpret_cast<const typename Pack4<T>::type*>(row + k0);
-  const typename Pack4<T>::type hi = *reinterpret_cast<const typename Pack4<T>::type*>(row + k0 + 8);
+  const char* vt = lds + L::KBYTES;
+  const int c0 = 8 * mt + 4 * a + half;  // chunk of keys 32mt+16a+4h .. +3
+  const typename Pack4<T>::type lo = *reinterpret_cast<const typename Pack4<T>::type*>(vt + L::vt_off(d, c0));
+  const typename Pack4<T>::type hi = *reinterpret_cast<const typename Pack4<T>::type*>(vt + L::vt_off(d, c0 + 2));
   frag_t<T> f;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -228,8 +236,8 @@ __device__ __forceinline__ TileRows rows_of(int e, bool valid, int r, int gshift
   t.h = (g << gshift) + (r & ((1 << gshift) - 1));
   return t;
 }
-// A work item holds at most 512 (query, head) rows: 512 / G entries.
-constexpr int kMaxItemEntries = 512;
+// A work item holds at most min(kItemRows / G, kItemEntries) entries.
+constexpr int kMaxItemEntries = kItemEntries;
 // Rows past the item's end read a valid row (entry 0 of the chunk): their
 // results are never stored, so no branch is needed around the loads.
 template <typename T, int D>
@@ -239,11 +247,18 @@ __device__ __forceinline__ void load_q_rows(frag_t<T> (&qf)[D / 16], const T* qb
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) qf[ks] = load8(qrow + 16 * ks);
 }
-// Partial store.  (Non-temporal stores were measured several times slower
-// here: the partial-line writes then miss the L2 write combining.)
-template <typename V>
-__device__ __forceinline__ void store_stream(void* p, const V& v) {
-  *reinterpret_cast<V*>(p) = v;
+// Partial store.  A partial is written once and read back only by the
+// combine.  With NT the store is marked non-temporal, which keeps partials
+// from displacing the query rows that other blocks of the same queries re-read
+// from the caches: measured faster where work items are full (many rows per
+// staged block), slower where most items are small and the staging of K/V
+// dominates, so the launcher chooses.  Every partial store writes whole rows
+// or whole runs of lse values (partial-line non-temporal writes measured
+// several times slower than plain ones).
+template <bool NT, typename V>
+__device__ __forceinline__ void store_partial(V* p, const V& v) {
+  if constexpr (NT) __builtin_nontemporal_store(v, p);
+  else *p = v;
 }
 
 struct KvArgs {
@@ -255,22 +270,85 @@ struct KvArgs {
   const int4* items;
   void* part_o;  // [B, nq, Hq, S, D] in the input dtype
   float* part_lse;
+  void* trash;      // kTrashBytes of scratch for the stores of rows past an item's end
+  float* trash_lse;
   int Nq, Nk, Hq, Hkv, G, topk, S, q0, nq, items_cap, gshift;
   int64_t q_offset;
   uint64_t topk_magic;  // ceil(2^40 / topk)
   float c_log2;  // softmax scale * log2(e)
 };
 
-template <typename T, int D>
-__global__ void __launch_bounds__(256, 2) k_attn_kvouter(KvArgs a) {
-  using L = KvLds<T, D>;
-  __shared__ __attribute__((aligned(16))) char lds[L::BYTES];
-  __shared__ int32_t ent_lds[kMaxItemEntries];
+// One 32-row tile of a KV-outer work item: prefetches the query rows of tile
+// `tile + 4` into (nxt, qn), computes the tile's partials from (cur, qf) and
+// writes them out.  Partial rows leave through LDS (`ob`, this wave's 8-row
+// buffer), 8 rows per pass, so that each store instruction writes four whole
+// rows instead of an 8-byte piece of 32.
+template <typename T, int D, bool NT>
+__device__ __forceinline__ void kv_tile(const KvArgs& a, const char* lds, const int32_t* ent_lds, char* ob, int tile,
+                                        int nrows, int b, int g, int64_t key0, const TileRows& cur,
+                                        const frag_t<T> (&qf)[D / 16], TileRows& nxt, frag_t<T> (&qn)[D / 16]) {
   constexpr int ROWB = D * (int)sizeof(T);   // bytes of one partial row
   constexpr int OPITCH = ROWB + 16;          // padded LDS row
   constexpr int LPR = ROWB / 16;             // lanes per row on the way out
   constexpr int RPS = 64 / LPR;              // rows per store instruction
-  __shared__ __attribute__((aligned(16))) char obuf[4][8 * OPITCH];
+  const int lane = threadIdx.x & 63, half = lane >> 5;
+  const int rn = (tile + 4) * 32 + (lane & 31);
+  const int en = ent_lds[min(rn >> a.gshift, kMaxItemEntries - 1)];
+  nxt = rows_of(rn < nrows ? en : 0, rn < nrows, rn, a.gshift, a.topk, a.topk_magic, g);
+  load_q_rows<T, D>(qn, static_cast<const T*>(a.q), nxt, b, a.Nq, a.Hq, a.q0, half);
+  const int64_t pos = a.q_offset + a.q0 + cur.qq;
+  const int64_t vis_end = min(pos + 1, (int64_t)a.Nk);  // keys t < vis_end are visible
+  const int vis = (int)max((int64_t)0, min((int64_t)kBk, vis_end - key0));
+  // Masking is only needed where the block reaches past a row's position.
+  const int need = __any(cur.valid && vis < kBk);
+  float m, l;
+  f32x16 o[D / 32];
+  block_tile<T, D>(lds, qf, a.c_log2, vis, need != 0, m, l, o);
+  const int64_t prow = (((int64_t)b * a.nq + cur.qq) * a.Hq + cur.h) * a.S + cur.slot;
+  const int64_t lrow = (((int64_t)b * a.nq + cur.qq) * a.S + cur.slot) * a.Hq + cur.h;
+  // Every store below is issued by every lane (rows past the item's end write
+  // to a scratch line instead): with no store under a branch the compiler
+  // counts the outstanding memory operations exactly, and the wait for the
+  // next tile's query rows does not also wait for these stores.  Both halves
+  // of the wave hold the row's m and l, so both write the same lse.
+  store_partial<NT>(cur.valid ? a.part_lse + lrow : a.trash_lse, (m + log2_fast(l)) * kLn2);
+  const float inv = 1.f / l;
+#pragma unroll
+  for (int ps = 0; ps < 4; ++ps) {
+    if (((lane & 31) >> 3) == ps) {
+      char* orow = ob + ((lane & 7) * OPITCH);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          typename Pack4<T>::type w;
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) w[rr] = from_f32<T>(o[dt][4 * i + rr] * inv);
+          *reinterpret_cast<typename Pack4<T>::type*>(orow + (32 * dt + 8 * i + 4 * half) * (int)sizeof(T)) = w;
+        }
+    }
+    wave_lds_sync();  // the rows written above are read by other lanes below
+    // lane -> (row ps*8 + lane/LPR + k*RPS, 16-byte chunk lane%LPR)
+#pragma unroll
+    for (int k = 0; k < 8 / RPS; ++k) {
+      const int rl = lane / LPR + k * RPS;
+      const int src = ps * 8 + rl;
+      const int64_t dst_row = __shfl(prow, src, 64);
+      const int ok = __shfl((int)cur.valid, src, 64);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(ob + rl * OPITCH + (lane % LPR) * 16);
+      char* dst = ok ? static_cast<char*>(a.part_o) + dst_row * ROWB : static_cast<char*>(a.trash);
+      store_partial<NT>(reinterpret_cast<u32x4*>(dst + (lane % LPR) * 16), v);
+    }
+    wave_lds_sync();  // the next pass overwrites the rows just read
+  }
+}
+
+template <typename T, int D, bool NT>
+__global__ void __launch_bounds__(256, 2) k_attn_kvouter(KvArgs a) {
+  using L = KvLds<T, D>;
+  __shared__ __attribute__((aligned(16))) char lds[L::BYTES];
+  __shared__ int32_t ent_lds[kMaxItemEntries];
+  __shared__ __attribute__((aligned(16))) char obuf[4][8 * (D * (int)sizeof(T) + 16)];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
   const int bg = blockIdx.y, b = bg / a.Hkv, g = bg % a.Hkv;
   // Items of one (b, g) are spread so that each XCD (workgroup id mod 8) runs a
@@ -298,9 +376,11 @@ __global__ void __launch_bounds__(256, 2) k_attn_kvouter(KvArgs a) {
   // counters retire in order, so each wait only covers the older loads.
   const int r0 = wave * 32 + (lane & 31);
   const int e_first = r0 < nrows ? ent[r0 >> a.gshift] : 0;
-  static_assert(kMaxItemEntries == 512, "two entries per thread");
-  const int e_mine0 = tid < nent ? ent[tid] : 0;
-  const int e_mine1 = tid + 256 < nent ? ent[tid + 256] : 0;
+  constexpr int EPT = kMaxItemEntries / 256;  // entries per thread
+  static_assert(kMaxItemEntries % 256 == 0, "whole entries per thread");
+  int e_mine[EPT];
+#pragma unroll
+  for (int u = 0; u < EPT; ++u) e_mine[u] = tid + 256 * u < nent ? ent[tid + 256 * u] : 0;
   __builtin_amdgcn_sched_barrier(0);
   KvStage<T, D> stg;
   stg.load(kb, vb, tok_stride, j, a.Nk, tid);
@@ -310,60 +390,27 @@ __global__ void __launch_bounds__(256, 2) k_attn_kvouter(KvArgs a) {
   frag_t<T> qf[D / 16];
   load_q_rows<T, D>(qf, qbase, cur, b, a.Nq, a.Hq, a.q0, half);
   __builtin_amdgcn_sched_barrier(0);
-  if (tid < nent) ent_lds[tid] = e_mine0;
-  if (tid + 256 < nent) ent_lds[tid + 256] = e_mine1;
+#pragma unroll
+  for (int u = 0; u < EPT; ++u)
+    if (tid + 256 * u < nent) ent_lds[tid + 256 * u] = e_mine[u];
   stg.store(lds, tid);
   __syncthreads();
 
-  // The next tile's rows are fetched while the current one computes.
-  for (int tile = wave; tile * 32 < nrows; tile += 4) {
-    const int rn = (tile + 4) * 32 + (lane & 31);
-    const int en = ent_lds[min(rn >> a.gshift, kMaxItemEntries - 1)];
-    const TileRows nxt = rows_of(rn < nrows ? en : 0, rn < nrows, rn, a.gshift, a.topk, a.topk_magic, g);
-    frag_t<T> qn[D / 16];
-    load_q_rows<T, D>(qn, qbase, nxt, b, a.Nq, a.Hq, a.q0, half);
-    const int64_t pos = a.q_offset + a.q0 + cur.qq;
-    const int64_t vis_end = min(pos + 1, (int64_t)a.Nk);  // keys t < vis_end are visible
-    const int vis = (int)max((int64_t)0, min((int64_t)kBk, vis_end - key0));
-    // Masking is only needed where the block reaches past a row's position.
-    const int need = __any(cur.valid && vis < kBk);
-    float m, l;
-    f32x16 o[D / 32];
-    block_tile<T, D>(lds, qf, a.c_log2, vis, need != 0, m, l, o);
-    // Partial rows leave through LDS, 8 rows per pass, so that each store
-    // instruction writes four whole rows instead of an 8-byte piece of 32.
-    const int64_t prow = (((int64_t)b * a.nq + cur.qq) * a.Hq + cur.h) * a.S + cur.slot;
-    if (cur.valid && half == 0) a.part_lse[prow] = (m + log2_fast(l)) * kLn2;
-    const float inv = 1.f / l;
-    char* ob = obuf[wave];
-#pragma unroll
-    for (int ps = 0; ps < 4; ++ps) {
-      if (((lane & 31) >> 3) == ps) {
-        char* orow = ob + ((lane & 7) * OPITCH);
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            typename Pack4<T>::type w;
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) w[rr] = from_f32<T>(o[dt][4 * i + rr] * inv);
-            *reinterpret_cast<typename Pack4<T>::type*>(orow + (32 * dt + 8 * i + 4 * half) * (int)sizeof(T)) = w;
-          }
-      }
-      // lane -> (row ps*8 + lane/LPR + k*RPS, 16-byte chunk lane%LPR)
-#pragma unroll
-      for (int k = 0; k < 8 / RPS; ++k) {
-        const int rl = lane / LPR + k * RPS;
-        const int src = ps * 8 + rl;
-        const int64_t dst_row = __shfl(prow, src, 64);
-        const int ok = __shfl((int)cur.valid, src, 64);
-        const u32x4 v = *reinterpret_cast<const u32x4*>(ob + rl * OPITCH + (lane % LPR) * 16);
-        if (ok) *reinterpret_cast<u32x4*>(static_cast<char*>(a.part_o) + dst_row * ROWB + (lane % LPR) * 16) = v;
-      }
-    }
-    cur = nxt;
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) qf[ks] = qn[ks];
+  // Tiles alternate between two query-fragment buffers: tile t computes from
+  // one while the rows of tile t+4 load into the other.  (A single buffer
+  // refilled by register copies made the wave wait at every copy for all of
+  // its outstanding memory operations, the partial stores included.)
+  // The first tile is peeled so that the loop is entered with the same
+  // outstanding operations (one tile's query loads, then its stores) on both
+  // paths; otherwise the merged count makes the first wait cover the stores.
+  frag_t<T> qg[D / 16];
+  TileRows nx;
+  if (wave * 32 >= nrows) return;
+  kv_tile<T, D, NT>(a, lds, ent_lds, obuf[wave], wave, nrows, b, g, key0, cur, qf, nx, qg);
+  for (int tile = wave + 4; tile * 32 < nrows; tile += 8) {
+    kv_tile<T, D, NT>(a, lds, ent_lds, obuf[wave], tile, nrows, b, g, key0, nx, qg, cur, qf);
+    if ((tile + 4) * 32 >= nrows) break;
+    kv_tile<T, D, NT>(a, lds, ent_lds, obuf[wave], tile + 4, nrows, b, g, key0, cur, qf, nx, qg);
   }
 }
 
@@ -503,6 +550,7 @@ __global__ void __launch_bounds__(256, 2) k_attn_qouter(QoArgs a) {
       if (dg == 0 && a.lse) a.lse[((int64_t)b * a.Nq + qglob) * a.Hq + h2] = lse_v;
     } else {
       const int64_t prow = (((int64_t)b * a.nq + qq) * a.Hq + h2) * a.nsplit + split;
+      const int64_t lrow = (((int64_t)b * a.nq + qq) * a.nsplit + split) * a.Hq + h2;
       T* po = static_cast<T*>(a.part_o) + prow * D;
       for (int d = dg * DPG; d < (dg + 1) * DPG; ++d) {
         float acc = 0.f;
@@ -510,7 +558,7 @@ __global__ void __launch_bounds__(256, 2) k_attn_qouter(QoArgs a) {
         for (int w = 0; w < 4; ++w) acc += wgt[w] * ob[(w * D + d) * 32 + c2];
         po[d] = from_f32<T>(acc * inv);
       }
-      if (dg == 0) a.part_lse[prow] = lse_v;
+      if (dg == 0) a.part_lse[lrow] = lse_v;
     }
   }
 }
@@ -543,7 +591,7 @@ __global__ void __launch_bounds__(256) k_combine(CombArgs a) {
   const int qq = (int)(row / a.Hq), h = (int)(row % a.Hq), g = h / a.G;
   const int64_t prow = ((int64_t)b * a.nq + qq) * a.Hq + h;
   const int32_t* sel = a.ids + (((int64_t)b * a.Nq + a.q0 + qq) * a.Hkv + g) * a.topk;
-  const float* pl = a.part_lse + prow * a.S;
+  const float* pl = a.part_lse + ((int64_t)b * a.nq + qq) * a.S * a.Hq + h;
   // All slot statistics are loaded at once (S <= SMAX).
   float ls[SMAX];
 #pragma unroll
@@ -551,7 +599,7 @@ __global__ void __launch_bounds__(256) k_combine(CombArgs a) {
     ls[s] = -__builtin_huge_valf();
     if (s < a.S) {
       const int id = a.ids_slots ? sel[s] : 0;
-      const float x = pl[s];
+      const float x = pl[(int64_t)s * a.Hq];
       if (id >= 0) ls[s] = x;
     }
   }
@@ -565,6 +613,7 @@ __global__ void __launch_bounds__(256) k_combine(CombArgs a) {
   float W = 0.f;
   const T* po = static_cast<const T*>(a.part_o) + prow * a.S * D + sub * 8;
   // Eight slots per round: all their loads are issued before any is used.
+  // Partials are read exactly once, so the loads are non-temporal.
 #pragma unroll
   for (int s0 = 0; s0 < SMAX; s0 += 8) {
     if (s0 < a.S) {
@@ -574,7 +623,8 @@ __global__ void __launch_bounds__(256) k_combine(CombArgs a) {
       for (int u = 0; u < 8; ++u) {
         const int s = s0 + u;
         w[u] = ls[s] == -__builtin_huge_valf() ? 0.f : exp2_fast((ls[s] - Mref) * kLog2e);
-        v[u] = s < a.S ? load8(po + (int64_t)s * D) : zero_frag<T>();
+        v[u] = s < a.S ? __builtin_nontemporal_load(reinterpret_cast<const frag_t<T>*>(po + (int64_t)s * D))
+                       : zero_frag<T>();
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -599,6 +649,12 @@ __global__ void __launch_bounds__(256) k_combine(CombArgs a) {
     a.lse[((int64_t)b * a.Nq + a.q0 + qq) * a.Hq + h] = W > 0.f ? M + log2_fast(W) * kLn2 : -__builtin_huge_valf();
 }
 
+template <typename T, int D>
+void kvouter_launch(bool nt, dim3 grid, hipStream_t st, const KvArgs& a) {
+  if (nt) hipLaunchKernelGGL((k_attn_kvouter<T, D, true>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((k_attn_kvouter<T, D, false>), grid, dim3(256), 0, st, a);
+}
+
 }  // namespace
 
 hipError_t launch_attn_kvouter(const Shape& s, const InvertPlan& p, int q0, int nq, const void* q, const void* k,
@@ -613,6 +669,8 @@ hipError_t launch_attn_kvouter(const Shape& s, const InvertPlan& p, int q0, int 
   a.items = inv.items;
   a.part_o = part.o;
   a.part_lse = part.lse;
+  a.trash = part.trash;
+  a.trash_lse = reinterpret_cast<float*>(static_cast<char*>(part.trash) + kTrashBytes - 16);
   a.Nq = s.Nq;
   a.Nk = s.Nk;
   a.Hq = s.Hq;
@@ -628,13 +686,16 @@ hipError_t launch_attn_kvouter(const Shape& s, const InvertPlan& p, int q0, int 
   a.gshift = __builtin_ctz((unsigned)a.G);
   a.topk_magic = ((uint64_t)1 << 40) / (uint64_t)s.topk + 1;
   const dim3 grid(p.items_cap, s.B * s.Hkv);
+  // Non-temporal partial stores pay off when the average selected block
+  // carries at least a full work item of rows.
+  const bool nt = (double)nq * s.topk * a.G >= (double)kItemRows * s.nblk;
   prof_begin(st, kid);
   if (s.dtype == kBF16) {
-    if (s.D == 64) hipLaunchKernelGGL((k_attn_kvouter<bf16_t, 64>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((k_attn_kvouter<bf16_t, 128>), grid, dim3(256), 0, st, a);
+    if (s.D == 64) kvouter_launch<bf16_t, 64>(nt, grid, st, a);
+    else kvouter_launch<bf16_t, 128>(nt, grid, st, a);
   } else {
-    if (s.D == 64) hipLaunchKernelGGL((k_attn_kvouter<float, 64>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((k_attn_kvouter<float, 128>), grid, dim3(256), 0, st, a);
+    if (s.D == 64) kvouter_launch<float, 64>(nt, grid, st, a);
+    else kvouter_launch<float, 128>(nt, grid, st, a);
   }
   const hipError_t e = hipGetLastError();
   prof_end(st, kid);

@@ -157,6 +157,7 @@ __global__ void __launch_bounds__(64) k_inv_scatter(InvArgs a) {
         ent[pos] = (qbeg + t) * a.topk + lane;
       }
     }
+    wave_lds_sync();  // the next step may read a cursor another lane just advanced
   }
 }
 
@@ -187,7 +188,7 @@ InvertPlan invert_plan(const Shape& s, int nq_chunk) {
   p.nq_chunk = nq_chunk;
   p.n_tiles = (nq_chunk + kInvTile - 1) / kInvTile;
   const int G = s.Hq / s.Hkv;
-  p.qi = 512 / G;
+  p.qi = kItemRows / G < kItemEntries ? kItemRows / G : kItemEntries;
   const int64_t cap = ((int64_t)nq_chunk * s.topk + p.qi - 1) / p.qi + s.nblk;
   p.items_cap = (int)((cap + 7) / 8 * 8);
   return p;

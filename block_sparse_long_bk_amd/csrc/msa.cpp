@@ -101,7 +101,7 @@ int qouter_splits(const msa::Shape& s) {
 size_t elem_bytes(const msa::Shape& s) { return s.dtype == msa::kBF16 ? 2 : 4; }
 
 struct KvLayout {
-  size_t offsets, entries, item_count, items, inv_scratch, part_o, part_lse, total;
+  size_t offsets, entries, item_count, items, inv_scratch, part_o, part_lse, trash, total;
 };
 
 KvLayout kv_layout(const msa::Shape& s, int nc) {
@@ -123,6 +123,8 @@ KvLayout kv_layout(const msa::Shape& s, int nc) {
   off += align_up((size_t)s.B * nc * s.Hq * s.topk * s.D * elem_bytes(s));
   L.part_lse = off;
   off += align_up((size_t)s.B * nc * s.Hq * s.topk * 4);
+  L.trash = off;
+  off += align_up(msa::kTrashBytes);
   L.total = off;
   return L;
 }
@@ -190,6 +192,7 @@ msa_status_t run_attention(const msa_problem_t* p, const msa::Shape& s, const vo
     part.o = w + L.part_o;
     part.lse = reinterpret_cast<float*>(w + L.part_lse);
     part.S = s.topk;
+    part.trash = w + L.trash;
     for (int q0 = 0; q0 < s.Nq && e == hipSuccess; q0 += nc) {
       const int nq = std::min(nc, s.Nq - q0);
       e = msa::launch_invert(s, plan, ids, q0, nq, inv, w + L.inv_scratch, st);
@@ -202,6 +205,7 @@ msa_status_t run_attention(const msa_problem_t* p, const msa::Shape& s, const vo
     part.o = w;
     part.lse = reinterpret_cast<float*>(w + (ns > 1 ? align_up((size_t)s.B * nc * s.Hq * ns * s.D * elem_bytes(s)) : 0));
     part.S = ns;
+    part.trash = nullptr;
     for (int q0 = 0; q0 < s.Nq && e == hipSuccess; q0 += nc) {
       const int nq = std::min(nc, s.Nq - q0);
       e = msa::launch_attn_qouter(s, q0, nq, ns, q, k, v, ids, out, lse, part, st);

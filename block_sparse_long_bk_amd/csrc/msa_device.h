@@ -76,6 +76,17 @@ __device__ __forceinline__ float max16(const f32x16& v, float m = -__builtin_hug
   return m;
 }
 
+// Lanes of one wave that exchange data through LDS without a workgroup
+// barrier must separate the writes from the reads with this: the wave runs in
+// lockstep and LDS accesses of one wave complete in order, but without a fence
+// the compiler may treat another lane's write as invisible and move or forward
+// the read (a wavefront-scope fence costs nothing in hardware).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 __device__ __forceinline__ float xor_shfl(float v, int mask) { return __shfl_xor(v, mask, kWave); }
 __device__ __forceinline__ int xor_shfl(int v, int mask) { return __shfl_xor(v, mask, kWave); }
 

@@ -45,6 +45,10 @@ struct InvertPlan {
   int qi;            // queries per work item
 };
 constexpr int kInvTile = 256;
+// A KV-outer work item holds at most kItemRows (query, head) rows and at most
+// kItemEntries (query, slot) entries (the entries are staged in LDS).
+constexpr int kItemRows = 2048;
+constexpr int kItemEntries = 1024;
 InvertPlan invert_plan(const Shape& s, int nq_chunk);
 size_t invert_ws_bytes(const Shape& s, const InvertPlan& p);
 // Builds offsets/entries (and work items) for queries [q0, q0 + nq) of every
@@ -61,12 +65,16 @@ hipError_t launch_invert(const Shape& s, const InvertPlan& p, const int32_t* ids
 
 // Main Branch -----------------------------------------------------------------
 // Partial results per (b, i, h, slot): normalised output o (D values in the
-// input dtype) and the log-sum-exp (fp32) of the slot's scaled logits.
+// input dtype) and the log-sum-exp (fp32) of the slot's scaled logits.  The
+// lse of one (query, slot) is contiguous over heads, so the G heads of a group
+// write one run.
 struct Partials {
   void* o;     // [B, nq, Hq, S, D]
-  float* lse;  // [B, nq, Hq, S]
+  float* lse;  // [B, nq, S, Hq]
   int S;       // slots per (query, head)
+  void* trash; // kTrashBytes written (never read) by KV-outer for padding rows
 };
+constexpr int kTrashBytes = 1024;
 hipError_t launch_attn_kvouter(const Shape& s, const InvertPlan& p, int q0, int nq, const void* q, const void* k,
                                const void* v, const InvertOut& inv, Partials part, hipStream_t st);
 // Query-outer: each workgroup handles (b, i, g, split); nsplit == 1 writes out/lse
