@@ -313,6 +313,15 @@ __device__ __forceinline__ void kv_tile(const KvArgs& a, const char* lds, const 
   // of the wave hold the row's m and l, so both write the same lse.
   store_partial<NT>(cur.valid ? a.part_lse + lrow : a.trash_lse, (m + log2_fast(l)) * kLn2);
   const float inv = 1.f / l;
+  // The normalised row in the output type, converted once (the passes below
+  // only pick which lanes write it).
+  typename Pack4<T>::type ow[D / 32][4];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) ow[dt][i][rr] = from_f32<T>(o[dt][4 * i + rr] * inv);
 #pragma unroll
   for (int ps = 0; ps < 4; ++ps) {
     if (((lane & 31) >> 3) == ps) {
@@ -320,12 +329,8 @@ __device__ __forceinline__ void kv_tile(const KvArgs& a, const char* lds, const 
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          typename Pack4<T>::type w;
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr) w[rr] = from_f32<T>(o[dt][4 * i + rr] * inv);
-          *reinterpret_cast<typename Pack4<T>::type*>(orow + (32 * dt + 8 * i + 4 * half) * (int)sizeof(T)) = w;
-        }
+        for (int i = 0; i < 4; ++i)
+          *reinterpret_cast<typename Pack4<T>::type*>(orow + (32 * dt + 8 * i + 4 * half) * (int)sizeof(T)) = ow[dt][i];
     }
     wave_lds_sync();  // the rows written above are read by other lanes below
     // lane -> (row ps*8 + lane/LPR + k*RPS, 16-byte chunk lane%LPR)
