@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_PKG, "libmsa.so")
 MSA_OK, MSA_ERR_INVALID_ARG, MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE, MSA_ERR_HIP = 0, -1, -2, -3, -4
 F32, BF16 = 0, 1
 SCHED_AUTO, SCHED_KV_OUTER, SCHED_Q_OUTER = 0, 1, 2
-OP_INDEX_TOPK, OP_ATTENTION, OP_FORWARD = 0, 1, 2
+OP_INDEX_TOPK, OP_ATTENTION, OP_FORWARD, OP_INVERT = 0, 1, 2, 3
 _SCHED = {"auto": SCHED_AUTO, "kv_outer": SCHED_KV_OUTER, "q_outer": SCHED_Q_OUTER}
 
 
@@ -186,7 +186,7 @@ def invert(p, ids, ws=None):
     offsets = torch.empty((p.batch, p.h_kv, nblk(p) + 1), dtype=torch.int32, device=ids.device)
     entries = torch.empty((p.batch, p.h_kv, p.n_q * p.topk), dtype=torch.int32, device=ids.device)
     if ws is None:
-        ws = alloc_workspace(p, OP_ATTENTION, ids.device)
+        ws = alloc_workspace(p, OP_INVERT, ids.device)
     wp, wn = _ws(ws)
     _check(_lib().msa_invert(ctypes.byref(p), _ptr(ids), _ptr(offsets), _ptr(entries), wp, wn, _stream()),
            "msa_invert")

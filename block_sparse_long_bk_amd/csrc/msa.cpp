@@ -318,9 +318,12 @@ msa_status_t msa_validate(const msa_problem_t* prob) { return validate(prob); }
 msa_status_t msa_workspace_size(const msa_problem_t* prob, int op, size_t* bytes, size_t* min_bytes) {
   msa_status_t rc = validate(prob);
   if (rc != MSA_OK) return rc;
-  if (!bytes || op < MSA_OP_INDEX_TOPK || op > MSA_OP_FORWARD) return MSA_ERR_INVALID_ARG;
+  if (!bytes || op < MSA_OP_INDEX_TOPK || op > MSA_OP_INVERT) return MSA_ERR_INVALID_ARG;
   const msa::Shape s = shape_of(prob);
   size_t full = 0, least = 0;
+  if (op == MSA_OP_INVERT) {
+    full = least = msa::invert_ws_bytes(s, msa::invert_plan(s, s.Nq));
+  }
   if (op == MSA_OP_INDEX_TOPK || op == MSA_OP_FORWARD) {
     full = std::max(full, index_bytes(s));
     least = std::max(least, index_bytes(s));

@@ -83,7 +83,7 @@ typedef struct {
   int32_t sched;         /* msa_sched_t */
 } msa_problem_t;
 
-typedef enum { MSA_OP_INDEX_TOPK = 0, MSA_OP_ATTENTION = 1, MSA_OP_FORWARD = 2 } msa_op_t;
+typedef enum { MSA_OP_INDEX_TOPK = 0, MSA_OP_ATTENTION = 1, MSA_OP_FORWARD = 2, MSA_OP_INVERT = 3 } msa_op_t;
 
 /* Human-readable name of a status code (static storage). */
 const char* msa_status_string(msa_status_t status);
@@ -124,7 +124,7 @@ msa_status_t msa_index_topk(const msa_problem_t* prob, const void* idx_q, const 
  * (query, slot) pairs that chose each block) and entries [B, Hkv, Nq*topk]
  * (int32 i*topk + slot, grouped by block, ascending within a block; entries
  * past offsets[nblk] are unspecified).  Deterministic.  Needs the
- * MSA_OP_ATTENTION workspace. */
+ * MSA_OP_INVERT workspace (the whole problem in one pass). */
 msa_status_t msa_invert(const msa_problem_t* prob, const int32_t* block_ids, int32_t* offsets,
                         int32_t* entries, void* ws, size_t ws_bytes, void* stream);
 

@@ -101,3 +101,8 @@ def test_workspace_sizes():
     fwd, _ = api.workspace_size(dec, api.OP_FORWARD)
     att, _ = api.workspace_size(dec, api.OP_ATTENTION)
     assert fwd == max(full, att)
+    # the inversion alone is sized for the whole problem, whatever the schedule
+    inv, inv_least = api.workspace_size(dec, api.OP_INVERT)
+    assert inv == inv_least > 0
+    inv_pre, _ = api.workspace_size(pre, api.OP_INVERT)
+    assert inv_pre >= 8 * 256 * 4  # at least one count per (group, block)

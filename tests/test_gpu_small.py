@@ -32,6 +32,9 @@ CASES = {
     "bf16_g32": dict(dtype="bf16", n_q=500, n_k=500, h_q=32, h_kv=1, d=64, d_idx=32, topk=3),
     "bf16_hot": dict(dtype="bf16", n_q=2048, n_k=2048, h_q=16, h_kv=2, d=128, d_idx=128, topk=6, hot_frac=0.1),
     "f32_sharp_offset": dict(n_q=333, n_k=1500, q_offset=1111, h_q=8, h_kv=2, d=128, d_idx=128, topk=5, sharp=True),
+    # more than 2048 candidate blocks and few rows: the workgroup-per-row Top-k
+    "bf16_long_decode": dict(dtype="bf16", batch=2, n_q=1, n_k=2100 * 128 + 77, q_offset=2100 * 128 + 76, h_q=8,
+                             h_kv=2, d=64, d_idx=32, topk=16),
 }
 
 _cache = {}
@@ -90,6 +93,26 @@ def test_topk_of_same_scores_is_exact(name):
     S64 = host(S).numpy().astype(np.float64).transpose(0, 2, 1, 3).reshape(wl.batch * wl.n_q, wl.h_kv, -1)
     want = O.select(O.problem_of(wl), S64)
     got = host(ids).numpy().reshape(wl.batch * wl.n_q, wl.h_kv, wl.topk)
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("n_q,n_k,topk", [(40, 40 * 128, 9), (3, 3000 * 128, 16), (2, 2500 * 128 + 5, 32)])
+def test_topk_planted_ties(n_q, n_k, topk):
+    """Scores drawn from three values, so nearly every row is decided by the
+    lowest-id rule; both Top-k kernels (wave per row, workgroup per row for
+    long rows) must equal the oracle exactly."""
+    wl = inputs.small("ties", n_q=n_q, n_k=n_k, q_offset=n_k - n_q, h_q=4, h_kv=2, topk=topk)
+    p = api.problem_of(wl)
+    nb = (n_k + 127) // 128
+    rng = np.random.default_rng(7 + n_q)
+    S = rng.integers(0, 3, size=(1, wl.h_kv, n_q, nb)).astype(np.float32)
+    ids = api.topk_from_scores(p, torch.from_numpy(S).cuda())
+    torch.cuda.synchronize()
+    S64 = S.astype(np.float64).transpose(0, 2, 1, 3).reshape(n_q, wl.h_kv, nb)
+    L = (np.arange(n_q) + wl.q_offset) // 128
+    S64 = np.where(np.arange(nb)[None, None, :] >= L[:, None, None], -np.inf, S64)  # only j < L is read
+    want = O.select(O.problem_of(wl), S64)
+    got = host(ids).numpy().reshape(n_q, wl.h_kv, wl.topk)
     assert np.array_equal(got, want)
 
 
