@@ -176,7 +176,6 @@ __device__ __forceinline__ void block_tile(const char* lds, const frag_t<T> (&qf
 #pragma unroll
     for (int ks = 1; ks < D / 16; ++ks) mma(load8(arow + 16 * ks), qf[ks], s[mt]);
   }
-  __builtin_amdgcn_sched_barrier(0);
   if (need_mask) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
@@ -201,7 +200,6 @@ __device__ __forceinline__ void block_tile(const char* lds, const frag_t<T> (&qf
       sum += p;
     }
   sum += xor_shfl(sum, 32);
-  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
