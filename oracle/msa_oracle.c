@@ -261,3 +261,68 @@ int mo_attend(const mo_problem* p, const void* q, const void* k, const void* v, 
   }
   return 0;
 }
+
+/* ---- MXFP8: OCP Microscaling Formats v1.0 (E4M3 elements, E8M0 scales) ---- */
+
+double mo_e4m3_value(uint8_t code) {
+  const int sign = code >> 7, e = (code >> 3) & 15, m = code & 7;
+  if (e == 15 && m == 7) return NAN;
+  /* exponent field 0: subnormal m/8 * 2^(1-7); otherwise (1 + m/8) * 2^(e-7) */
+  const double mag = e == 0 ? ldexp((double)m / 8.0, -6) : ldexp(1.0 + (double)m / 8.0, e - 7);
+  return sign ? -mag : mag;
+}
+
+uint8_t mo_e4m3_encode(double y) {
+  const uint8_t sign = signbit(y) ? 0x80 : 0x00;
+  const double a = fabs(y);
+  if (a >= 448.0) return sign | 0x7E; /* saturate at the largest finite value */
+  if (a < ldexp(1.0, -6)) {
+    /* subnormal range: multiples of 2^-9; rounding up to 8 lands on 2^-6 */
+    const double m = nearbyint(ldexp(a, 9)); /* round half to even */
+    return sign | (uint8_t)m;
+  }
+  int ex;
+  frexp(a, &ex); /* a = f * 2^ex, f in [0.5, 1) */
+  int e = ex - 1;  /* a in [2^e, 2^(e+1)) */
+  double q = nearbyint(ldexp(a, 3 - e)); /* in [8, 16]: 1.mmm in eighths */
+  if (q == 16.0) {
+    q = 8.0;
+    e += 1;
+  }
+  return sign | (uint8_t)(((e + 7) << 3) | ((int)q - 8));
+}
+
+int mo_mxfp8_quantize(const void* src, int dtype, int64_t n_rows, int32_t row_len, uint8_t* codes,
+                      uint8_t* scales) {
+  if (!src || !codes || !scales || n_rows < 0 || row_len <= 0 || row_len % 32) return -1;
+  if (dtype != MO_F32 && dtype != MO_BF16 && dtype != MO_F64) return -6;
+  const int64_t nblocks = n_rows * (row_len / 32);
+#pragma omp parallel for schedule(static)
+  for (int64_t blk = 0; blk < nblocks; ++blk) {
+    const int64_t base = blk * 32;
+    double amax = 0.0;
+    for (int c = 0; c < 32; ++c) {
+      const double a = fabs(widen(src, dtype, base + c));
+      if (a > amax) amax = a;
+    }
+    int e = -127;
+    if (amax > 0.0) {
+      int ex;
+      frexp(amax, &ex);
+      e = (ex - 1) - 8; /* floor(log2(amax)) - emax(E4M3) */
+      if (e < -127) e = -127;
+      if (e > 127) e = 127;
+    }
+    scales[blk] = (uint8_t)(e + 127);
+    for (int c = 0; c < 32; ++c) codes[base + c] = mo_e4m3_encode(ldexp(widen(src, dtype, base + c), -e));
+  }
+  return 0;
+}
+
+int mo_mxfp8_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t n_rows, int32_t row_len, double* out) {
+  if (!codes || !scales || !out || n_rows < 0 || row_len <= 0 || row_len % 32) return -1;
+  const int64_t n = n_rows * row_len;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) out[i] = ldexp(mo_e4m3_value(codes[i]), (int)scales[i / 32] - 127);
+  return 0;
+}

@@ -76,6 +76,27 @@ int mo_attend(const mo_problem* p, const void* q, const void* k, const void* v, 
  * covering every query (no row subset). */
 int mo_invert(const mo_problem* p, const int32_t* ids, int32_t* offsets, int32_t* entries);
 
+/* MXFP8 index-key caches (OCP Microscaling Formats v1.0, section 6: blocks of
+ * 32 elements share one E8M0 power-of-two scale X = 2^(s - 127); elements are
+ * OCP FP8 E4M3, i.e. bias 7, no infinities, S.1111.111 = NaN, largest finite
+ * 448).  The MiniMax pages name MXFP8 for the long-context cache (zhichai.net
+ * write-up, section 9, decode KV-cache); the spec fixes the rest.
+ *
+ * Value of one E4M3 code (NaN for the two NaN codes). */
+double mo_e4m3_value(uint8_t code);
+/* The E4M3 code nearest to y, ties to the even code, magnitudes above 448
+ * saturating to +-448 (the spec's conversion of a scaled element); -0 keeps
+ * its sign bit. */
+uint8_t mo_e4m3_encode(double y);
+/* Quantise rows of row_len elements (a multiple of 32) block by block:
+ * shared exponent e = floor(log2(max |v|)) - 8 (8 = the largest exponent of
+ * E4M3), clamped to [-127, 127] (e = -127 for an all-zero block); codes =
+ * encode(v / 2^e), scales = e + 127.  src holds n_rows*row_len elements of
+ * `dtype`; codes: n_rows*row_len bytes; scales: n_rows*row_len/32 bytes. */
+int mo_mxfp8_quantize(const void* src, int dtype, int64_t n_rows, int32_t row_len, uint8_t* codes, uint8_t* scales);
+/* out[r*row_len + c] = value(codes[...]) * 2^(scales[r*row_len/32 + c/32] - 127). */
+int mo_mxfp8_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t n_rows, int32_t row_len, double* out);
+
 /* Number of OpenMP threads the routines above use. */
 int mo_num_threads(void);
 

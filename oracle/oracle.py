@@ -84,6 +84,38 @@ class Oracle:
     def num_threads(self):
         return self.L.mo_num_threads()
 
+    # MXFP8 (OCP Microscaling Formats: 32-element blocks, E8M0 scale, E4M3 codes).
+    def e4m3_value(self, code):
+        return self.L.mo_e4m3_value(int(code) & 0xFF)
+
+    def e4m3_encode(self, y):
+        return self.L.mo_e4m3_encode(float(y))
+
+    def mx_quantize(self, x):
+        """(codes uint8 [..., n], scales uint8 [..., n/32]) of x (last axis a multiple of 32)."""
+        x, dt = _host(x)
+        n = x.shape[-1]
+        assert n % 32 == 0
+        rows = x.size // n
+        codes = np.empty(x.shape, dtype=np.uint8)
+        scales = np.empty(x.shape[:-1] + (n // 32,), dtype=np.uint8)
+        rc = self.L.mo_mxfp8_quantize(_ptr(x), dt, rows, n, _ptr(codes), _ptr(scales))
+        if rc:
+            raise ValueError(f"mo_mxfp8_quantize: invalid argument ({rc})")
+        return codes, scales
+
+    def mx_dequantize(self, codes, scales):
+        """fp64 values of an MXFP8 array (exact)."""
+        codes = np.ascontiguousarray(codes, dtype=np.uint8)
+        scales = np.ascontiguousarray(scales, dtype=np.uint8)
+        n = codes.shape[-1]
+        assert scales.shape == codes.shape[:-1] + (n // 32,)
+        out = np.empty(codes.shape, dtype=np.float64)
+        rc = self.L.mo_mxfp8_dequantize(_ptr(codes), _ptr(scales), codes.size // n, n, _ptr(out))
+        if rc:
+            raise ValueError(f"mo_mxfp8_dequantize: invalid argument ({rc})")
+        return out
+
 
 _default = None
 
@@ -118,6 +150,14 @@ def num_threads():
     return default().num_threads()
 
 
+def mx_quantize(x):
+    return default().mx_quantize(x)
+
+
+def mx_dequantize(codes, scales):
+    return default().mx_dequantize(codes, scales)
+
+
 def load(path):
     L = ctypes.CDLL(path)
     P = ctypes.POINTER(Problem)
@@ -129,6 +169,14 @@ def load(path):
     for f in (L.mo_block_scores, L.mo_select, L.mo_attend, L.mo_invert):
         f.restype = ctypes.c_int
     L.mo_num_threads.restype = ctypes.c_int
+    L.mo_e4m3_value.argtypes = [ctypes.c_uint8]
+    L.mo_e4m3_value.restype = ctypes.c_double
+    L.mo_e4m3_encode.argtypes = [ctypes.c_double]
+    L.mo_e4m3_encode.restype = ctypes.c_uint8
+    L.mo_mxfp8_quantize.argtypes = [vp, ctypes.c_int, ctypes.c_int64, ctypes.c_int32, vp, vp]
+    L.mo_mxfp8_dequantize.argtypes = [vp, vp, ctypes.c_int64, ctypes.c_int32, vp]
+    L.mo_mxfp8_quantize.restype = ctypes.c_int
+    L.mo_mxfp8_dequantize.restype = ctypes.c_int
     return L
 
 

@@ -297,9 +297,93 @@ def pin_causal_diagonal(orc):
         assert lse[0, 0] == 800.0
 
 
+# ---- MXFP8 index-key caches (OCP Microscaling Formats v1.0; OCP 8-bit floating
+# point E4M3).  torch's float8_e4m3fn is an independent implementation of the
+# element format; the shared-exponent rule and the saturation are the MX
+# spec's and are checked on hand-computed blocks.
+
+def _torch_e4m3_codes(y):
+    return torch.from_numpy(np.asarray(y, dtype=np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def pin_e4m3_decode_table(orc):
+    """Every code decodes as torch's float8_e4m3fn does; published anchors."""
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    got = np.array([orc.e4m3_value(c) for c in range(256)])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan) and nan.sum() == 2  # S.1111.111 only
+    assert np.array_equal(got[~nan], ref[~nan])
+    anchors = {0x38: 1.0, 0x7E: 448.0, 0x08: 2.0 ** -6, 0x01: 2.0 ** -9, 0xC0: -2.0, 0x00: 0.0}
+    for c, v in anchors.items():
+        assert got[c] == v, (hex(c), got[c])
+
+
+def pin_e4m3_encode_rne(orc):
+    """Nearest code, ties to the even code: equal to torch's conversion on every
+    representable value, every midpoint between neighbours (the ties), and
+    random values; magnitudes above 448 saturate (the MX conversion)."""
+    vals = torch.arange(0, 0x7F, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()  # 0 .. 448
+    mids = (vals[1:] + vals[:-1]) / 2
+    rng = np.random.default_rng(11)
+    rand = rng.uniform(0, 448, 2000)
+    tiny = rng.uniform(0, 2.0 ** -6, 500)
+    ys = np.concatenate([vals, mids, rand, tiny, [2.0 ** -10, 3 * 2.0 ** -10, 2.0 ** -10 * 1.0001]])
+    ys = np.concatenate([ys, -ys])
+    got = np.array([orc.e4m3_encode(y) for y in ys], dtype=np.uint8)
+    assert np.array_equal(got, _torch_e4m3_codes(ys))
+    for y in (448.5, 464.0, 480.0, 1e6, 1e300):
+        assert orc.e4m3_encode(y) == 0x7E and orc.e4m3_encode(-y) == 0xFE, y
+    assert orc.e4m3_encode(-0.0) == 0x80
+
+
+def pin_mx_shared_exponent(orc):
+    """Hand-computed blocks: scale = floor(log2 max|v|) - 8 (+127 bias), clamped;
+    elements = E4M3(v / 2^scale), the block maximum saturating when its scaled
+    value passes 448."""
+    def q(block):
+        c, sc = orc.mx_quantize(np.asarray(block, dtype=np.float64).reshape(1, 32))
+        return c[0], int(sc[0, 0])
+    c, sc = q(np.ones(32))                       # 1 = 2^0 -> X = 2^-8, 1/X = 256 = 2^8
+    assert sc == 119 and np.all(c == 0x78)
+    blk = np.zeros(32); blk[3] = 56.0; blk[4] = -7.0  # log2 56 = 5.8 -> X = 2^-3: 448 and -56 = -1.75 * 2^5
+    c, sc = q(blk)
+    assert sc == 124 and c[3] == 0x7E and c[4] == 0xE6 and np.all(np.delete(c, [3, 4]) == 0)
+    blk = np.full(32, 1.9)                      # X = 2^-8: 1.9 * 256 = 486.4 saturates to 448
+    c, sc = q(blk)
+    assert sc == 119 and np.all(c == 0x7E)
+    c, sc = q(np.zeros(32))                      # all zero: smallest scale, zero codes
+    assert sc == 0 and np.all(c == 0)
+    c, sc = q(np.full(32, 2.0 ** -130))          # exponent clamped at -127: 2^-130 * 2^127 = 2^-3
+    assert sc == 0 and np.all(c == 0x20)
+    c, sc = q(np.full(32, 2.0 ** 200))           # exponent clamped at 127: saturates
+    assert sc == 254 and np.all(c == 0x7E)
+    # two blocks per row are independent
+    row = np.concatenate([np.full(32, 0.5), np.full(32, 8.0)]).reshape(1, 64)
+    c, sc = orc.mx_quantize(row)
+    assert list(sc[0]) == [127 - 9, 127 - 5] and np.all(c == 0x78)
+
+
+def pin_mx_roundtrip(orc):
+    """Dequantised values are the block scale times a code value, exactly, and
+    agree with torch's element conversion of v / X for every element below the
+    saturation point."""
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((64, 128)) * np.exp(rng.uniform(-8, 8, (64, 1)))
+    c, sc = orc.mx_quantize(x)
+    d = orc.mx_dequantize(c, sc)
+    X = np.repeat(2.0 ** (sc.astype(np.float64) - 127), 32, axis=1)
+    y = x / X
+    ok = np.abs(y) <= 448
+    ref = torch.from_numpy(y[ok]).to(torch.float8_e4m3fn).double().numpy() * X[ok]
+    assert np.array_equal(d[ok], ref)
+    assert np.all(np.abs(d[~ok]) == 448 * X[~ok])
+    assert (~ok).sum() > 0  # the saturating case does occur on Gaussian blocks
+
+
 PINS = [pin_golden_worked_example, pin_maxpool_closed_form, pin_scores_ignore_future_and_token_order,
         pin_topk_bruteforce, pin_topk_special_cases, pin_exp_free, pin_dense_equals_sdpa,
-        pin_sparse_equals_masked_sdpa, pin_value_invariants, pin_causal_diagonal]
+        pin_sparse_equals_masked_sdpa, pin_value_invariants, pin_causal_diagonal,
+        pin_e4m3_decode_table, pin_e4m3_encode_rne, pin_mx_shared_exponent, pin_mx_roundtrip]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -384,6 +468,13 @@ MUTANTS = {
     # catch: candidate blocks lie wholly before the query, so it never fires.)
     "scores_include_local_block": ("for (int64_t j = 0; j < L; ++j) {\n      double best",
                                    "for (int64_t j = 0; j <= L && j < nblk; ++j) {\n      double best"),
+    "mx_truncates": ("double q = nearbyint(ldexp(a, 3 - e));", "double q = floor(ldexp(a, 3 - e));"),
+    "mx_ties_away": ("const double m = nearbyint(ldexp(a, 9));", "const double m = round(ldexp(a, 9));"),
+    "mx_emax_7": ("e = (ex - 1) - 8;", "e = (ex - 1) - 7;"),
+    "mx_no_saturation": ("if (a >= 448.0) return sign | 0x7E;", "if (a >= 480.0) return sign | 0x7F;"),
+    "mx_scale_not_clamped": ("if (e < -127) e = -127;", ""),
+    "mx_exponent_sign": ("out[i] = ldexp(mo_e4m3_value(codes[i]), (int)scales[i / 32] - 127);",
+                         "out[i] = ldexp(mo_e4m3_value(codes[i]), 127 - (int)scales[i / 32]);"),
 }
 
 
