@@ -17,6 +17,8 @@ MSA_OK, MSA_ERR_INVALID_ARG, MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE, MSA_ERR_HIP
 F32, BF16 = 0, 1
 SCHED_AUTO, SCHED_KV_OUTER, SCHED_Q_OUTER = 0, 1, 2
 OP_INDEX_TOPK, OP_ATTENTION, OP_FORWARD, OP_INVERT = 0, 1, 2, 3
+IDX_PLAIN, IDX_MXFP8 = 0, 1
+_IDXF = {"plain": IDX_PLAIN, "mxfp8": IDX_MXFP8}
 _SCHED = {"auto": SCHED_AUTO, "kv_outer": SCHED_KV_OUTER, "q_outer": SCHED_Q_OUTER}
 
 
@@ -27,7 +29,7 @@ class Problem(ctypes.Structure):
         ("h_q", ctypes.c_int32), ("h_kv", ctypes.c_int32), ("d", ctypes.c_int32),
         ("d_idx", ctypes.c_int32), ("block_size", ctypes.c_int32), ("topk", ctypes.c_int32),
         ("dtype", ctypes.c_int32), ("q_offset", ctypes.c_int64), ("softmax_scale", ctypes.c_float),
-        ("sched", ctypes.c_int32),
+        ("sched", ctypes.c_int32), ("idx_format", ctypes.c_int32),
     ]
 
 
@@ -44,7 +46,7 @@ _L = None
 
 EXPORTS = ["msa_status_string", "msa_last_hip_error", "msa_validate", "msa_workspace_size", "msa_block_scores",
            "msa_topk_from_scores", "msa_index_topk", "msa_invert", "msa_sparse_attention", "msa_forward",
-           "msa_profile_enable", "msa_profile_reset", "msa_profile_count", "msa_profile_read"]
+           "msa_mxfp8_quantize", "msa_profile_enable", "msa_profile_reset", "msa_profile_count", "msa_profile_read"]
 
 
 def _lib():
@@ -67,6 +69,7 @@ def _lib():
         L.msa_invert.argtypes = [P, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.msa_sparse_attention.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.msa_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.msa_mxfp8_quantize.argtypes = [vp, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, vp, vp, vp]
         L.msa_profile_enable.argtypes = [ctypes.c_int]
         L.msa_profile_count.restype = ctypes.c_int
         L.msa_profile_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
@@ -84,10 +87,11 @@ def lib():
 
 
 def problem(batch, n_q, n_k, h_q, h_kv, d, d_idx, topk, dtype="bf16", q_offset=0, block_size=128,
-            softmax_scale=0.0, sched="auto"):
+            softmax_scale=0.0, sched="auto", idx_format="plain"):
     return Problem(batch, n_q, n_k, h_q, h_kv, d, d_idx, block_size, topk,
                    BF16 if dtype in ("bf16", torch.bfloat16) else F32, q_offset, softmax_scale,
-                   _SCHED[sched] if isinstance(sched, str) else int(sched))
+                   _SCHED[sched] if isinstance(sched, str) else int(sched),
+                   _IDXF[idx_format] if isinstance(idx_format, str) else int(idx_format))
 
 
 def problem_of(wl, sched="auto", **kw):
@@ -127,6 +131,32 @@ def _tdtype(p):
     return torch.bfloat16 if p.dtype == BF16 else torch.float32
 
 
+def _expect_ik(p, ik):
+    """idx_k in the problem's dtype, or an MXFP8 cache (codes then scales, uint8)."""
+    if p.idx_format == IDX_MXFP8:
+        n = p.batch * p.n_k * p.h_kv * p.d_idx
+        _expect(ik, (n + n // 32,), torch.uint8, "idx_k (MXFP8 codes + scales)")
+    else:
+        _expect(ik, (p.batch, p.n_k, p.h_kv, p.d_idx), _tdtype(p), "idx_k")
+
+
+def mxfp8_quantize(x, out=None):
+    """MXFP8 cache of x (cuda bf16/fp32, last axis a multiple of 32): one uint8
+    tensor holding the E4M3 codes of every element followed by the E8M0 scale
+    of every 32-element block -- the idx_k layout of an IDX_MXFP8 problem."""
+    if x.dtype not in (torch.bfloat16, torch.float32) or not x.is_contiguous() or x.device.type != "cuda":
+        raise ValueError("mxfp8_quantize: expected a contiguous cuda bf16/fp32 tensor")
+    n, row = x.numel(), x.shape[-1]
+    if out is None:
+        out = torch.empty(n + n // 32, dtype=torch.uint8, device=x.device)
+    _expect(out, (n + n // 32,), torch.uint8, "out")
+    base = out.data_ptr()
+    _check(_lib().msa_mxfp8_quantize(_ptr(x), BF16 if x.dtype == torch.bfloat16 else F32, n // row, row,
+                                     ctypes.c_void_p(base), ctypes.c_void_p(base + n), _stream()),
+           "msa_mxfp8_quantize")
+    return out
+
+
 def validate(p):
     return _lib().msa_validate(ctypes.byref(p))
 
@@ -152,7 +182,7 @@ def _ws(ws):
 def block_scores(p, iq, ik, scores=None):
     dt = _tdtype(p)
     _expect(iq, (p.batch, p.n_q, p.h_kv, p.d_idx), dt, "idx_q")
-    _expect(ik, (p.batch, p.n_k, p.h_kv, p.d_idx), dt, "idx_k")
+    _expect_ik(p, ik)
     if scores is None:
         scores = torch.empty((p.batch, p.h_kv, p.n_q, nblk(p)), dtype=torch.float32, device=iq.device)
     _check(_lib().msa_block_scores(ctypes.byref(p), _ptr(iq), _ptr(ik), _ptr(scores), _stream()), "msa_block_scores")
@@ -170,7 +200,7 @@ def topk_from_scores(p, scores, ids=None):
 def index_topk(p, iq, ik, ids=None, ws=None):
     dt = _tdtype(p)
     _expect(iq, (p.batch, p.n_q, p.h_kv, p.d_idx), dt, "idx_q")
-    _expect(ik, (p.batch, p.n_k, p.h_kv, p.d_idx), dt, "idx_k")
+    _expect_ik(p, ik)
     if ids is None:
         ids = torch.empty((p.batch, p.n_q, p.h_kv, p.topk), dtype=torch.int32, device=iq.device)
     if ws is None:
@@ -217,7 +247,7 @@ def forward(p, q, k, v, iq, ik, ids=None, out=None, lse=None, want_lse=True, ws=
     _expect(k, (p.batch, p.n_k, p.h_kv, p.d), dt, "k")
     _expect(v, (p.batch, p.n_k, p.h_kv, p.d), dt, "v")
     _expect(iq, (p.batch, p.n_q, p.h_kv, p.d_idx), dt, "idx_q")
-    _expect(ik, (p.batch, p.n_k, p.h_kv, p.d_idx), dt, "idx_k")
+    _expect_ik(p, ik)
     if ids is None:
         ids = torch.empty((p.batch, p.n_q, p.h_kv, p.topk), dtype=torch.int32, device=q.device)
     if out is None:

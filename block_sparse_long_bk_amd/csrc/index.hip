@@ -29,7 +29,8 @@ namespace {
 
 struct TileArgs {
   const void* iq;
-  const void* ik;
+  const void* ik;          // keys in the dtype, or MXFP8 codes
+  const uint8_t* iks;      // MXFP8 scales (one per 32 key elements), else null
   int32_t* ids;
   float* scores;
   int Nq, Nk, Hkv, topk, nblk, n_tiles;
@@ -59,6 +60,52 @@ __device__ __forceinline__ void tile_lstore(const u32x4 (&stage)[LOADS], char* b
     if (c < CHUNKS) {
       const int row = c / CPR, col = c % CPR;
       *reinterpret_cast<u32x4*>(buf + row * PITCH + col * 16) = stage[u];
+    }
+  }
+}
+
+// MXFP8 keys: 16-byte chunks of codes (16 elements, inside one 32-element
+// scale block) and their scale byte are loaded, decoded exactly and stored to
+// LDS in the dtype layout the MFMA path reads (each element times 2^(s-127) is
+// representable in the dtype: E4M3 carries 3 mantissa bits).
+template <int LOADS, int MCPR, int CHUNKS, int NTHR, int DI>
+__device__ __forceinline__ void mx_gload(u32x4 (&stage)[LOADS], uint32_t (&scl)[LOADS], const uint8_t* codes,
+                                         const uint8_t* scales, int j, int hkv, int tid) {
+#pragma unroll
+  for (int u = 0; u < LOADS; ++u) {
+    const int c = tid + u * NTHR;
+    if (c < CHUNKS) {
+      const int row = c / MCPR, col = c % MCPR;
+      const int64_t r = ((int64_t)j * kBk + row) * hkv;
+      stage[u] = *reinterpret_cast<const u32x4*>(codes + r * DI + col * 16);
+      scl[u] = scales[r * (DI / 32) + col / 2];
+    }
+  }
+}
+template <typename T, int LOADS, int MCPR, int CHUNKS, int NTHR, int PITCH>
+__device__ __forceinline__ void mx_lstore(const u32x4 (&stage)[LOADS], const uint32_t (&scl)[LOADS], char* buf,
+                                          int tid) {
+#pragma unroll
+  for (int u = 0; u < LOADS; ++u) {
+    const int c = tid + u * NTHR;
+    if (c < CHUNKS) {
+      const int row = c / MCPR, col = c % MCPR;
+      float f[16];
+      e4m3_decode16(stage[u], f);
+      const int ex = (int)scl[u] - 127;
+      T* dst = reinterpret_cast<T*>(buf + row * PITCH) + col * 16;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        frag_t<T> o;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = static_cast<T>(__builtin_ldexpf(f[8 * h + e], ex));
+        if constexpr (sizeof(T) == 2) {
+          *reinterpret_cast<frag_t<T>*>(dst + 8 * h) = o;
+        } else {
+          *reinterpret_cast<f32x4*>(dst + 8 * h) = f32x4{o[0], o[1], o[2], o[3]};
+          *reinterpret_cast<f32x4*>(dst + 8 * h + 4) = f32x4{o[4], o[5], o[6], o[7]};
+        }
+      }
     }
   }
 }
@@ -104,7 +151,7 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <typename T, int DI, int NT, int KMAX, bool WRITE_S, bool TOPK>
+template <typename T, int DI, int NT, int KMAX, bool WRITE_S, bool TOPK, bool MX>
 __global__ void __launch_bounds__(kTileWaves * 64) k_index_tile(TileArgs a) {
   constexpr int WAVES = kTileWaves;
   constexpr int TQ = WAVES * NT * 32;  // queries per workgroup
@@ -115,7 +162,10 @@ __global__ void __launch_bounds__(kTileWaves * 64) k_index_tile(TileArgs a) {
   constexpr int CHUNKS = kBk * CPR;
   constexpr int NTHR = WAVES * 64;
   constexpr int LOADS = (CHUNKS + NTHR - 1) / NTHR;
-  constexpr bool DMA = ROW_BYTES == kDmaRowBytes && WAVES == 8;  // 8 waves x 4 loads = one block
+  constexpr bool DMA = !MX && ROW_BYTES == kDmaRowBytes && WAVES == 8;  // 8 waves x 4 loads = one block
+  constexpr int MCPR = DI / 16;  // MXFP8: 16-byte code chunks per key row
+  constexpr int MCHUNKS = kBk * MCPR;
+  constexpr int MLOADS = (MCHUNKS + NTHR - 1) / NTHR;
   constexpr int NBUF = DMA ? kDmaBufs : 2;
   constexpr int BUFB = DMA ? kBk * kDmaRowBytes : kBk * PITCH;
   __shared__ __attribute__((aligned(16))) char lds[NBUF][BUFB];
@@ -131,6 +181,8 @@ __global__ void __launch_bounds__(kTileWaves * 64) k_index_tile(TileArgs a) {
   const T* iq = static_cast<const T*>(a.iq);
   const int64_t krow = (int64_t)a.Hkv * DI;  // elements between consecutive tokens
   const char* ikb = reinterpret_cast<const char*>(static_cast<const T*>(a.ik) + (int64_t)b * a.Nk * krow + g * DI);
+  const uint8_t* ikc = static_cast<const uint8_t*>(a.ik) + ((int64_t)b * a.Nk * a.Hkv + g) * DI;  // MXFP8 codes
+  const uint8_t* iks = a.iks + ((int64_t)b * a.Nk * a.Hkv + g) * (DI / 32);                       // MXFP8 scales
 
   // Index queries of this wave as B operands: column = query, k = d_idx.
   frag_t<T> bq[NT][KSTEPS];
@@ -152,7 +204,13 @@ __global__ void __launch_bounds__(kTileWaves * 64) k_index_tile(TileArgs a) {
 
   if (j_end > 0) {
     u32x4 stage[LOADS];
-    if constexpr (DMA) {
+    u32x4 mstage[MLOADS];
+    uint32_t mscl[MLOADS];
+    if constexpr (MX) {
+      mx_gload<MLOADS, MCPR, MCHUNKS, NTHR, DI>(mstage, mscl, ikc, iks, 0, a.Hkv, tid);
+      mx_lstore<T, MLOADS, MCPR, MCHUNKS, NTHR, PITCH>(mstage, mscl, lds[0], tid);
+      __syncthreads();
+    } else if constexpr (DMA) {
 #pragma unroll
       for (int sb = 0; sb < NBUF - 1; ++sb)
         if (sb < j_end) dma_issue_block(lds[sb], ikb, sb, krow * (int64_t)sizeof(T), wave, lane);
@@ -171,6 +229,8 @@ __global__ void __launch_bounds__(kTileWaves * 64) k_index_tile(TileArgs a) {
         __syncthreads();
         if (j + NBUF - 1 < j_end)
           dma_issue_block(lds[(j + NBUF - 1) % NBUF], ikb, j + NBUF - 1, krow * (int64_t)sizeof(T), wave, lane);
+      } else if constexpr (MX) {
+        if (j + 1 < j_end) mx_gload<MLOADS, MCPR, MCHUNKS, NTHR, DI>(mstage, mscl, ikc, iks, j + 1, a.Hkv, tid);
       } else {
         if (j + 1 < j_end) tile_gload<LOADS, CPR, CHUNKS, NTHR>(stage, ikb, j + 1, krow * (int64_t)sizeof(T), tid);
       }
@@ -216,7 +276,10 @@ __global__ void __launch_bounds__(kTileWaves * 64) k_index_tile(TileArgs a) {
         if (TOPK) list.offer(own, j);
         if (WRITE_S) a.scores[(((int64_t)b * a.Hkv + g) * a.Nq + q_own) * a.nblk + j] = own;
       }
-      if constexpr (!DMA) {
+      if constexpr (MX) {
+        if (j + 1 < j_end) mx_lstore<T, MLOADS, MCPR, MCHUNKS, NTHR, PITCH>(mstage, mscl, lds[(j + 1) & 1], tid);
+        __syncthreads();
+      } else if constexpr (!DMA) {
         if (j + 1 < j_end) tile_lstore<LOADS, CPR, CHUNKS, NTHR, PITCH>(stage, lds[(j + 1) & 1], tid);
         __syncthreads();
       }
@@ -233,7 +296,8 @@ __global__ void __launch_bounds__(kTileWaves * 64) k_index_tile(TileArgs a) {
 
 struct ScanArgs {
   const void* iq;
-  const void* ik;
+  const void* ik;          // keys in the dtype, or MXFP8 codes
+  const uint8_t* iks;      // MXFP8 scales, else null
   float* scores;
   int Nq, Nk, Hkv, nblk, blocks_per_wg, j_end;
   int64_t q_offset;
@@ -243,10 +307,13 @@ constexpr int kScanThreads = 256;
 constexpr int kScanUnroll = 8;
 
 // One workgroup scores `blocks_per_wg` consecutive key blocks of one batch
-// entry for every group and every query (Nq <= NQ).
-template <typename T, int DI, int NQ>
+// entry for every group and every query (Nq <= NQ).  MXFP8 keys: each lane
+// takes a 16-byte chunk of codes (16 elements of one 32-element scale block),
+// decodes it exactly, and scales its partial dot product by 2^(s-127).
+template <typename T, int DI, int NQ, bool MX>
 __global__ void __launch_bounds__(kScanThreads) k_index_scan(ScanArgs a) {
-  constexpr int C = DI / 8;                      // lanes per (token, group) row
+  constexpr int EPL = MX ? 16 : 8;               // key elements per lane
+  constexpr int C = DI / EPL;                    // lanes per (token, group) row
   constexpr int ROWS_IT = kScanThreads / C;      // rows per sweep of the workgroup
   extern __shared__ __attribute__((aligned(16))) float smem[];
   float* qs = smem;                              // [NQ][Hkv][DI] index queries (fp32)
@@ -267,25 +334,50 @@ __global__ void __launch_bounds__(kScanThreads) k_index_scan(ScanArgs a) {
   const int jb = blockIdx.x * a.blocks_per_wg;
   const int je = min(jb + a.blocks_per_wg, a.j_end);
   for (int j = jb; j < je; ++j) {
-    const T* blk = ik + ((int64_t)b * a.Nk + (int64_t)j * kBk) * H * DI;
+    const int64_t row0 = ((int64_t)b * a.Nk + (int64_t)j * kBk) * H;  // first (token, group) row of block j
+    const T* blk = ik + row0 * DI;
+    const uint8_t* blkc = static_cast<const uint8_t*>(a.ik) + row0 * DI;
+    const uint8_t* blks = a.iks + row0 * (DI / 32);
     for (int it0 = 0; it0 < iters; it0 += kScanUnroll) {
       frag_t<T> x[kScanUnroll];
+      u32x4 xc[kScanUnroll];
+      uint32_t xs[kScanUnroll];
 #pragma unroll
       for (int u = 0; u < kScanUnroll; ++u) {
         const int row = (it0 + u) * ROWS_IT + rsub;
-        x[u] = (it0 + u < iters) ? load8(blk + (int64_t)row * DI + c * 8) : zero_frag<T>();
+        if constexpr (MX) {
+          xc[u] = u32x4{};
+          xs[u] = 127;
+          if (it0 + u < iters) {
+            xc[u] = *reinterpret_cast<const u32x4*>(blkc + (int64_t)row * DI + c * 16);
+            xs[u] = blks[(int64_t)row * (DI / 32) + c / 2];
+          }
+        } else {
+          x[u] = (it0 + u < iters) ? load8(blk + (int64_t)row * DI + c * 8) : zero_frag<T>();
+        }
       }
 #pragma unroll
       for (int u = 0; u < kScanUnroll; ++u) {
         const int row = (it0 + u) * ROWS_IT + rsub;
         const int tok = row / H, grp = row % H;
+        float kf[EPL];
+        if constexpr (MX) {
+          float f[16];
+          e4m3_decode16(xc[u], f);
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) kf[e] = f[e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) kf[e] = to_f32(x[u][e]);
+        }
 #pragma unroll
         for (int qi = 0; qi < NQ; ++qi) {
           if (qi < a.Nq) {
-            const float* qv = qs + (qi * H + grp) * DI + c * 8;
+            const float* qv = qs + (qi * H + grp) * DI + c * EPL;
             float acc = 0.f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc = fmaf(to_f32(x[u][e]), qv[e], acc);
+            for (int e = 0; e < EPL; ++e) acc = fmaf(kf[e], qv[e], acc);
+            if constexpr (MX) acc = __builtin_ldexpf(acc, (int)xs[u] - 127);
 #pragma unroll
             for (int m = C / 2; m >= 1; m >>= 1) acc += xor_shfl(acc, m);
             if (c == 0 && it0 + u < iters) dots[(qi * H + grp) * kBk + tok] = acc;
@@ -312,47 +404,63 @@ __global__ void k_fill_neg_inf(float* p, size_t n) {
     p[e] = -__builtin_huge_valf();
 }
 
-template <typename T, int DI, bool WRITE_S, bool TOPK>
+template <typename T, int DI, bool WRITE_S, bool TOPK, bool MX>
 hipError_t tile_dispatch(const Shape& s, const TileArgs& a, dim3 grid, hipStream_t st) {
   constexpr int NT = (DI * (int)sizeof(T) <= 256) ? 2 : 1;
   const int kneed = s.topk - 1;
   if (!TOPK || kneed <= 8) {
-    hipLaunchKernelGGL((k_index_tile<T, DI, NT, 8, WRITE_S, TOPK>), grid, dim3(kTileWaves * 64), 0, st, a);
+    hipLaunchKernelGGL((k_index_tile<T, DI, NT, 8, WRITE_S, TOPK, MX>), grid, dim3(kTileWaves * 64), 0, st, a);
   } else if (kneed <= 16) {
-    hipLaunchKernelGGL((k_index_tile<T, DI, NT, 16, WRITE_S, TOPK>), grid, dim3(kTileWaves * 64), 0, st, a);
+    hipLaunchKernelGGL((k_index_tile<T, DI, NT, 16, WRITE_S, TOPK, MX>), grid, dim3(kTileWaves * 64), 0, st, a);
   } else {
-    hipLaunchKernelGGL((k_index_tile<T, DI, NT, 32, WRITE_S, TOPK>), grid, dim3(kTileWaves * 64), 0, st, a);
+    hipLaunchKernelGGL((k_index_tile<T, DI, NT, 32, WRITE_S, TOPK, MX>), grid, dim3(kTileWaves * 64), 0, st, a);
   }
   return hipGetLastError();
+}
+
+template <typename T, bool WRITE_S, bool TOPK, bool MX>
+hipError_t tile_dispatch_di(const Shape& s, const TileArgs& a, dim3 grid, hipStream_t st) {
+  switch (s.DI) {
+    case 32: return tile_dispatch<T, 32, WRITE_S, TOPK, MX>(s, a, grid, st);
+    case 64: return tile_dispatch<T, 64, WRITE_S, TOPK, MX>(s, a, grid, st);
+    default: return tile_dispatch<T, 128, WRITE_S, TOPK, MX>(s, a, grid, st);
+  }
 }
 
 template <typename T, bool WRITE_S, bool TOPK>
-hipError_t tile_dispatch_di(const Shape& s, const TileArgs& a, dim3 grid, hipStream_t st) {
-  switch (s.DI) {
-    case 32: return tile_dispatch<T, 32, WRITE_S, TOPK>(s, a, grid, st);
-    case 64: return tile_dispatch<T, 64, WRITE_S, TOPK>(s, a, grid, st);
-    default: return tile_dispatch<T, 128, WRITE_S, TOPK>(s, a, grid, st);
-  }
+hipError_t tile_dispatch_fmt(const Shape& s, const TileArgs& a, dim3 grid, hipStream_t st) {
+  return s.idx_mx ? tile_dispatch_di<T, WRITE_S, TOPK, true>(s, a, grid, st)
+                  : tile_dispatch_di<T, WRITE_S, TOPK, false>(s, a, grid, st);
 }
 
-template <typename T, int DI>
+template <typename T, int DI, bool MX>
 hipError_t scan_dispatch(const Shape& s, const ScanArgs& a, dim3 grid, hipStream_t st) {
   const int nq = s.Nq <= 1 ? 1 : s.Nq <= 2 ? 2 : s.Nq <= 4 ? 4 : 8;
   const size_t shm_q = (size_t)nq * s.Hkv * (DI + kBk) * sizeof(float);
-  if (s.Nq <= 1) hipLaunchKernelGGL((k_index_scan<T, DI, 1>), grid, dim3(kScanThreads), shm_q, st, a);
-  else if (s.Nq <= 2) hipLaunchKernelGGL((k_index_scan<T, DI, 2>), grid, dim3(kScanThreads), shm_q, st, a);
-  else if (s.Nq <= 4) hipLaunchKernelGGL((k_index_scan<T, DI, 4>), grid, dim3(kScanThreads), shm_q, st, a);
-  else hipLaunchKernelGGL((k_index_scan<T, DI, 8>), grid, dim3(kScanThreads), shm_q, st, a);
+  if (s.Nq <= 1) hipLaunchKernelGGL((k_index_scan<T, DI, 1, MX>), grid, dim3(kScanThreads), shm_q, st, a);
+  else if (s.Nq <= 2) hipLaunchKernelGGL((k_index_scan<T, DI, 2, MX>), grid, dim3(kScanThreads), shm_q, st, a);
+  else if (s.Nq <= 4) hipLaunchKernelGGL((k_index_scan<T, DI, 4, MX>), grid, dim3(kScanThreads), shm_q, st, a);
+  else hipLaunchKernelGGL((k_index_scan<T, DI, 8, MX>), grid, dim3(kScanThreads), shm_q, st, a);
   return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, bool MX>
 hipError_t scan_dispatch_di(const Shape& s, const ScanArgs& a, dim3 grid, hipStream_t st) {
   switch (s.DI) {
-    case 32: return scan_dispatch<T, 32>(s, a, grid, st);
-    case 64: return scan_dispatch<T, 64>(s, a, grid, st);
-    default: return scan_dispatch<T, 128>(s, a, grid, st);
+    case 32: return scan_dispatch<T, 32, MX>(s, a, grid, st);
+    case 64: return scan_dispatch<T, 64, MX>(s, a, grid, st);
+    default: return scan_dispatch<T, 128, MX>(s, a, grid, st);
   }
+}
+
+template <typename T>
+hipError_t scan_dispatch_fmt(const Shape& s, const ScanArgs& a, dim3 grid, hipStream_t st) {
+  return s.idx_mx ? scan_dispatch_di<T, true>(s, a, grid, st) : scan_dispatch_di<T, false>(s, a, grid, st);
+}
+
+// Scale bytes of an MXFP8 idx_k cache: right after the B*Nk*Hkv*d_idx codes.
+const uint8_t* mx_scales(const Shape& s, const void* ik) {
+  return s.idx_mx ? static_cast<const uint8_t*>(ik) + (size_t)s.B * s.Nk * s.Hkv * s.DI : nullptr;
 }
 
 constexpr int kScanMaxQueries = 8;
@@ -374,6 +482,7 @@ hipError_t launch_index_tile(const Shape& s, const void* iq, const void* ik, int
   TileArgs a;
   a.iq = iq;
   a.ik = ik;
+  a.iks = mx_scales(s, ik);
   a.ids = ids;
   a.scores = scores;
   a.Nq = s.Nq;
@@ -387,9 +496,9 @@ hipError_t launch_index_tile(const Shape& s, const void* iq, const void* ik, int
   prof_begin(st, kid);
   hipError_t e;
   if (s.dtype == kBF16)
-    e = ids ? tile_dispatch_di<bf16_t, false, true>(s, a, grid, st) : tile_dispatch_di<bf16_t, true, false>(s, a, grid, st);
+    e = ids ? tile_dispatch_fmt<bf16_t, false, true>(s, a, grid, st) : tile_dispatch_fmt<bf16_t, true, false>(s, a, grid, st);
   else
-    e = ids ? tile_dispatch_di<float, false, true>(s, a, grid, st) : tile_dispatch_di<float, true, false>(s, a, grid, st);
+    e = ids ? tile_dispatch_fmt<float, false, true>(s, a, grid, st) : tile_dispatch_fmt<float, true, false>(s, a, grid, st);
   prof_end(st, kid);
   return e;
 }
@@ -400,6 +509,7 @@ hipError_t launch_index_scan(const Shape& s, const void* iq, const void* ik, flo
   ScanArgs a;
   a.iq = iq;
   a.ik = ik;
+  a.iks = mx_scales(s, ik);
   a.scores = scores;
   a.Nq = s.Nq;
   a.Nk = s.Nk;
@@ -411,7 +521,7 @@ hipError_t launch_index_scan(const Shape& s, const void* iq, const void* ik, flo
   a.blocks_per_wg = 2;
   const dim3 grid((a.j_end + a.blocks_per_wg - 1) / a.blocks_per_wg, s.B);
   prof_begin(st, kid);
-  const hipError_t e = s.dtype == kBF16 ? scan_dispatch_di<bf16_t>(s, a, grid, st) : scan_dispatch_di<float>(s, a, grid, st);
+  const hipError_t e = s.dtype == kBF16 ? scan_dispatch_fmt<bf16_t>(s, a, grid, st) : scan_dispatch_fmt<float>(s, a, grid, st);
   prof_end(st, kid);
   return e;
 }

@@ -38,6 +38,7 @@ msa_status_t validate(const msa_problem_t* p) {
   if (p->sched != MSA_SCHED_AUTO && p->sched != MSA_SCHED_KV_OUTER && p->sched != MSA_SCHED_Q_OUTER)
     return MSA_ERR_INVALID_ARG;
   if (!std::isfinite(p->softmax_scale)) return MSA_ERR_INVALID_ARG;
+  if (p->idx_format != MSA_IDX_PLAIN && p->idx_format != MSA_IDX_MXFP8) return MSA_ERR_INVALID_ARG;
   // Valid but outside what the kernels are built for.
   if (p->block_size != 128) return MSA_ERR_UNSUPPORTED;
   if (p->d != 64 && p->d != 128) return MSA_ERR_UNSUPPORTED;
@@ -64,6 +65,7 @@ msa::Shape shape_of(const msa_problem_t* p) {
   s.DI = p->d_idx;
   s.topk = p->topk;
   s.dtype = p->dtype == MSA_BF16 ? msa::kBF16 : msa::kF32;
+  s.idx_mx = p->idx_format == MSA_IDX_MXFP8;
   s.q_offset = p->q_offset;
   s.nblk = (p->n_k + 127) / 128;
   s.scale = p->softmax_scale > 0 ? p->softmax_scale : 1.0f / std::sqrt((float)p->d);
@@ -350,6 +352,17 @@ msa_status_t msa_block_scores(const msa_problem_t* prob, const void* idx_q, cons
     if (msa::index_use_tile(s)) e = msa::launch_index_tile(s, idx_q, idx_k, nullptr, scores, st);
     else e = msa::launch_index_scan(s, idx_q, idx_k, scores, st);
   }
+  return e == hipSuccess ? MSA_OK : hip_fail(e);
+}
+
+msa_status_t msa_mxfp8_quantize(const void* src, int32_t src_dtype, int64_t n_rows, int32_t row_len, uint8_t* codes,
+                                uint8_t* scales, void* stream) {
+  if (!src || !codes || !scales || !aligned16(src) || !aligned16(codes)) return MSA_ERR_INVALID_ARG;
+  if (src_dtype != MSA_F32 && src_dtype != MSA_BF16) return MSA_ERR_INVALID_ARG;
+  if (n_rows < 0 || row_len <= 0 || row_len % 32 || n_rows > ((int64_t)1 << 40) / row_len) return MSA_ERR_INVALID_ARG;
+  if (n_rows == 0) return MSA_OK;
+  const hipError_t e = msa::launch_mxfp8_quantize(src, src_dtype == MSA_BF16 ? msa::kBF16 : msa::kF32, n_rows,
+                                                  row_len, codes, scales, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MSA_OK : hip_fail(e);
 }
 

@@ -76,6 +76,21 @@ __device__ __forceinline__ float max16(const f32x16& v, float m = -__builtin_hug
   return m;
 }
 
+// Sixteen OCP E4M3 codes (one 16-byte chunk, little-endian bytes) decoded
+// exactly to fp32 by the hardware conversion (which follows the OCP encoding
+// on gfx950: checked against a reference table of all 256 codes).
+__device__ __forceinline__ void e4m3_decode16(const u32x4& c, float (&out)[16]) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[w], false);
+    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[w], true);
+    out[4 * w + 0] = lo[0];
+    out[4 * w + 1] = lo[1];
+    out[4 * w + 2] = hi[0];
+    out[4 * w + 3] = hi[1];
+  }
+}
+
 // Lanes of one wave that exchange data through LDS without a workgroup
 // barrier must separate the writes from the reads with this: the wave runs in
 // lockstep and LDS accesses of one wave complete in order, but without a fence

@@ -13,6 +13,7 @@ enum DType { kF32 = 0, kBF16 = 1 };
 // Shape of one call after validation (all sizes in elements).
 struct Shape {
   int B, Nq, Nk, Hq, Hkv, D, DI, topk, dtype;
+  bool idx_mx;  // idx_k is an MXFP8 cache: codes, then one scale byte per 32 elements
   int64_t q_offset;
   int nblk;     // ceil(Nk / 128)
   float scale;  // softmax scale (natural-log domain)
@@ -30,6 +31,9 @@ hipError_t launch_index_tile(const Shape& s, const void* iq, const void* ik, int
                              hipStream_t st);
 // Streaming scan for few queries (decode): writes block scores only.
 hipError_t launch_index_scan(const Shape& s, const void* iq, const void* ik, float* scores, hipStream_t st);
+// MXFP8 quantisation of n_rows rows of row_len elements (src in `dtype`).
+hipError_t launch_mxfp8_quantize(const void* src, int dtype, int64_t n_rows, int row_len, uint8_t* codes,
+                                 uint8_t* scales, hipStream_t st);
 // Fill scores with -inf.
 hipError_t launch_fill_neg_inf(float* p, size_t n, hipStream_t st);
 // Top-k over score rows (one wave per (b, g, i) row).

@@ -44,6 +44,17 @@
  * Supported: dtype MSA_BF16 or MSA_F32; block_size 128; d in {64, 128};
  * d_idx in {32, 64, 128}; 1 <= topk <= 32; Hq / Hkv a power of two <= 32;
  * 0 <= q_offset and q_offset + Nq <= Nk.
+ *
+ * Index keys may instead be an MXFP8 cache (idx_format = MSA_IDX_MXFP8; the
+ * MiniMax write-up pairs MSA with MXFP8 caches for long-context decode,
+ * zhichai.net section 9).  Format: OCP Microscaling Formats v1.0 -- blocks of
+ * 32 consecutive elements of a row share one E8M0 scale byte s (value
+ * 2^(s-127)); elements are OCP FP8 E4M3 codes.  Layout: the idx_k pointer
+ * holds the codes [B, Nk, Hkv, d_idx] (uint8) immediately followed by the
+ * scales [B, Nk, Hkv, d_idx/32] (uint8), i.e. the scales start
+ * B*Nk*Hkv*d_idx bytes after idx_k.  idx_q stays in `dtype`; scores are
+ * computed from the exactly decoded keys in fp32.  msa_mxfp8_quantize writes
+ * such a cache.
  */
 #ifndef MSA_H
 #define MSA_H
@@ -75,12 +86,16 @@ typedef enum { MSA_F32 = 0, MSA_BF16 = 1 } msa_dtype_t;
  * (the note quotes 2.85 for its Blackwell kernels) -- and Q_OUTER otherwise. */
 typedef enum { MSA_SCHED_AUTO = 0, MSA_SCHED_KV_OUTER = 1, MSA_SCHED_Q_OUTER = 2 } msa_sched_t;
 
+/* How idx_k is stored: in `dtype` like the other tensors, or as an MXFP8 cache. */
+typedef enum { MSA_IDX_PLAIN = 0, MSA_IDX_MXFP8 = 1 } msa_idx_format_t;
+
 typedef struct {
   int32_t batch, n_q, n_k, h_q, h_kv, d, d_idx, block_size, topk;
   int32_t dtype;         /* msa_dtype_t */
   int64_t q_offset;      /* query i sits at position q_offset + i */
   float softmax_scale;   /* <= 0 means 1/sqrt(d) */
   int32_t sched;         /* msa_sched_t */
+  int32_t idx_format;    /* msa_idx_format_t */
 } msa_problem_t;
 
 typedef enum { MSA_OP_INDEX_TOPK = 0, MSA_OP_ATTENTION = 1, MSA_OP_FORWARD = 2, MSA_OP_INVERT = 3 } msa_op_t;
@@ -140,6 +155,19 @@ msa_status_t msa_sparse_attention(const msa_problem_t* prob, const void* q, cons
 msa_status_t msa_forward(const msa_problem_t* prob, const void* q, const void* k, const void* v,
                          const void* idx_q, const void* idx_k, int32_t* block_ids, void* out, float* lse,
                          void* ws, size_t ws_bytes, void* stream);
+
+/* Quantise n_rows rows of row_len elements (row_len a multiple of 32) of src
+ * (device, `src_dtype` MSA_F32 or MSA_BF16, row-major) to MXFP8 following the
+ * OCP MX v1.0 conversion: per 32-element block, shared exponent
+ * e = floor(log2(max |v|)) - 8 clamped to [-127, 127] (-127 for an all-zero
+ * block), scale byte e + 127, codes = E4M3(v / 2^e) rounded to nearest even
+ * with magnitudes above 448 saturating to 448 (-0 keeps its sign).  codes:
+ * n_rows*row_len bytes; scales: n_rows*row_len/32 bytes (device, caller-owned;
+ * codes 16-byte aligned).  For an idx_k cache pass rows = B*Nk*Hkv,
+ * row_len = d_idx and scales = codes + B*Nk*Hkv*d_idx.  Errors:
+ * MSA_ERR_INVALID_ARG (NULL or misaligned pointer, bad sizes or dtype). */
+msa_status_t msa_mxfp8_quantize(const void* src, int32_t src_dtype, int64_t n_rows, int32_t row_len, uint8_t* codes,
+                                uint8_t* scales, void* stream);
 
 /* Kernel timing for measurement.  While enabled, every kernel launch is
  * bracketed by two hipEvents on its stream (a small overhead per launch).

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def declared_functions():
     src = open(os.path.join(ROOT, "include", "msa.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(msa_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(msa_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_header_declares_the_binding_exports():
@@ -51,6 +51,9 @@ def test_status_strings():
     (dict(topk=0), api.MSA_ERR_INVALID_ARG),
     (dict(softmax_scale=float("nan")), api.MSA_ERR_INVALID_ARG),
     (dict(sched=7), api.MSA_ERR_INVALID_ARG),
+    (dict(idx_format=2), api.MSA_ERR_INVALID_ARG),
+    (dict(idx_format="mxfp8"), api.MSA_OK),
+    (dict(idx_format="mxfp8", dtype="bf16", d=128, d_idx=32, h_q=64, h_kv=8, topk=16), api.MSA_OK),
     (dict(block_size=64), api.MSA_ERR_UNSUPPORTED),
     (dict(d=96), api.MSA_ERR_UNSUPPORTED),
     (dict(d_idx=48), api.MSA_ERR_UNSUPPORTED),
@@ -84,6 +87,14 @@ def test_entry_points_reject_before_any_hip_call():
     big = good(dtype="bf16", n_q=32768, n_k=32768, h_q=64, h_kv=8, d=128, d_idx=128, topk=16, sched="kv_outer")
     assert L.msa_sparse_attention(ctypes.byref(big), x, x, x, x, x, null, x, 1024, null) == api.MSA_ERR_WORKSPACE
     assert L.msa_workspace_size(ctypes.byref(p), 9, ctypes.byref(ctypes.c_size_t()), None) == api.MSA_ERR_INVALID_ARG
+    # MXFP8 quantiser: sizes, dtype and pointers are checked before any launch
+    q = L.msa_mxfp8_quantize
+    assert q(x, api.BF16, 4, 48, x, x, null) == api.MSA_ERR_INVALID_ARG   # row length not a multiple of 32
+    assert q(x, 7, 4, 64, x, x, null) == api.MSA_ERR_INVALID_ARG         # unknown dtype
+    assert q(null, api.F32, 4, 64, x, x, null) == api.MSA_ERR_INVALID_ARG
+    assert q(x, api.F32, 4, 64, mis, x, null) == api.MSA_ERR_INVALID_ARG  # codes not 16-byte aligned
+    assert q(x, api.F32, -1, 64, x, x, null) == api.MSA_ERR_INVALID_ARG
+    assert q(x, api.F32, 0, 64, x, x, null) == api.MSA_OK                 # nothing to do
 
 
 def test_workspace_sizes():
