@@ -111,3 +111,33 @@ def test_index_over_mxfp8_cache(name):
     assert_attention(wl.dtype, to_f64(o2).reshape(o_o.shape), o_o, host(l2).numpy().reshape(l_o.shape), l_o,
                      what=f"{name}/attention")
     print(f"{name}: selection {res}")
+
+
+def _dequant_f32(codes, scales, chunk=1 << 16):
+    """Exact key values (fp32 holds every MXFP8 value of a quantised finite
+    cache) without a full fp64 copy of a 1M-token cache."""
+    out = np.empty(codes.shape, dtype=np.float32)
+    for t0 in range(0, codes.shape[1], chunk):
+        out[:, t0:t0 + chunk] = O.mx_dequantize(codes[:, t0:t0 + chunk], scales[:, t0:t0 + chunk])
+    return out
+
+
+def test_decode_16x1m_over_mxfp8_cache():
+    """Full-size decode rows (1M-token cache, 8191 candidate blocks) over an
+    MXFP8 cache built by the oracle, for the first and last sequence."""
+    wl = inputs.WORKLOADS["decode_16x1m"]
+    x = inputs.generate(wl, device="cuda", tensors=("iq", "ik"))
+    sub = wl.with_(batch=1)
+    prob = O.problem_of(sub)
+    for b in (0, wl.batch - 1):
+        codes, scales = O.mx_quantize(host(x["ik"][b:b + 1]))
+        cache = torch.from_numpy(np.concatenate([codes.reshape(-1), scales.reshape(-1)])).cuda()
+        iq = x["iq"][b:b + 1].contiguous()
+        ids = api.index_topk(api.problem_of(sub, idx_format="mxfp8"), iq, cache)
+        torch.cuda.synchronize()
+        s_o = O.block_scores(prob, host(iq).float().numpy(), _dequant_f32(codes, scales))
+        ids_o = O.select(prob, s_o)
+        res = check_selection(sub, host(ids).numpy().reshape(1, wl.h_kv, wl.topk), ids_o, s_o)
+        print(f"decode_16x1m/mxfp8 b={b}: {res}", flush=True)
+        assert res["fail"] == 0, res
+        del cache
