@@ -318,6 +318,7 @@ __global__ void __launch_bounds__(kScanThreads) k_index_scan(ScanArgs a) {
   extern __shared__ __attribute__((aligned(16))) float smem[];
   float* qs = smem;                              // [NQ][Hkv][DI] index queries (fp32)
   float* dots = smem + NQ * a.Hkv * DI;          // [NQ][Hkv][128] token scores of one block
+  uint8_t* sscl = reinterpret_cast<uint8_t*>(dots + NQ * a.Hkv * kBk);  // MXFP8: the block's scale bytes
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = blockIdx.y;
@@ -337,7 +338,19 @@ __global__ void __launch_bounds__(kScanThreads) k_index_scan(ScanArgs a) {
     const int64_t row0 = ((int64_t)b * a.Nk + (int64_t)j * kBk) * H;  // first (token, group) row of block j
     const T* blk = ik + row0 * DI;
     const uint8_t* blkc = static_cast<const uint8_t*>(a.ik) + row0 * DI;
-    const uint8_t* blks = a.iks + row0 * (DI / 32);
+    if constexpr (MX) {
+      // The block's scale bytes (128 * Hkv * DI/32, contiguous) go to LDS with
+      // one 16-byte load per thread instead of a byte load per row and lane.
+      const uint8_t* blks = a.iks + row0 * (DI / 32);
+      const int nbytes = kBk * H * (DI / 32);
+      if ((reinterpret_cast<uintptr_t>(blks) & 15) == 0) {
+        for (int ch = tid; ch < nbytes / 16; ch += kScanThreads)
+          reinterpret_cast<u32x4*>(sscl)[ch] = reinterpret_cast<const u32x4*>(blks)[ch];
+      } else {  // a batch entry whose scales do not start on 16 bytes (odd Nk)
+        for (int i = tid; i < nbytes; i += kScanThreads) sscl[i] = blks[i];
+      }
+      __syncthreads();
+    }
     for (int it0 = 0; it0 < iters; it0 += kScanUnroll) {
       frag_t<T> x[kScanUnroll];
       u32x4 xc[kScanUnroll];
@@ -350,7 +363,7 @@ __global__ void __launch_bounds__(kScanThreads) k_index_scan(ScanArgs a) {
           xs[u] = 127;
           if (it0 + u < iters) {
             xc[u] = *reinterpret_cast<const u32x4*>(blkc + (int64_t)row * DI + c * 16);
-            xs[u] = blks[(int64_t)row * (DI / 32) + c / 2];
+            xs[u] = sscl[row * (DI / 32) + c / 2];
           }
         } else {
           x[u] = (it0 + u < iters) ? load8(blk + (int64_t)row * DI + c * 8) : zero_frag<T>();
@@ -436,7 +449,7 @@ hipError_t tile_dispatch_fmt(const Shape& s, const TileArgs& a, dim3 grid, hipSt
 template <typename T, int DI, bool MX>
 hipError_t scan_dispatch(const Shape& s, const ScanArgs& a, dim3 grid, hipStream_t st) {
   const int nq = s.Nq <= 1 ? 1 : s.Nq <= 2 ? 2 : s.Nq <= 4 ? 4 : 8;
-  const size_t shm_q = (size_t)nq * s.Hkv * (DI + kBk) * sizeof(float);
+  const size_t shm_q = (size_t)nq * s.Hkv * (DI + kBk) * sizeof(float) + (MX ? (size_t)kBk * s.Hkv * (DI / 32) : 0);
   if (s.Nq <= 1) hipLaunchKernelGGL((k_index_scan<T, DI, 1, MX>), grid, dim3(kScanThreads), shm_q, st, a);
   else if (s.Nq <= 2) hipLaunchKernelGGL((k_index_scan<T, DI, 2, MX>), grid, dim3(kScanThreads), shm_q, st, a);
   else if (s.Nq <= 4) hipLaunchKernelGGL((k_index_scan<T, DI, 4, MX>), grid, dim3(kScanThreads), shm_q, st, a);
