@@ -36,14 +36,14 @@ template <typename T> struct Pack4;
 template <> struct Pack4<bf16_t> { using type = bf16x4; };
 template <> struct Pack4<float> { using type = f32x4; };
 
-// LDS geometry of one staged key block: K row-major [128][D], V transposed
-// [D][128].  Pitches are padded so the 32 rows read by a half-wave fall on
-// distinct banks.
-template <typename T, int D>
+// LDS geometry of one staged key block of BK tokens: K row-major [BK][D], V
+// transposed [D][BK].  Pitches are padded so the 32 rows read by a half-wave
+// fall on distinct banks.
+template <typename T, int D, int BK>
 struct KvLds {
   static constexpr int KPITCH = D * (int)sizeof(T) + 16;
-  static constexpr int VPITCH = kBk * (int)sizeof(T) + (sizeof(T) == 2 ? 8 : 16);
-  static constexpr int KBYTES = kBk * KPITCH;
+  static constexpr int VPITCH = BK * (int)sizeof(T) + (sizeof(T) == 2 ? 8 : 16);
+  static constexpr int KBYTES = BK * KPITCH;
   static constexpr int BYTES = KBYTES + D * VPITCH;
   // Byte offset of keys [4c, 4c+4) in V^T row d.  For 16-bit types the
   // 4-key chunks are XOR-swizzled by (d / 32) % 4: the staging stores write
@@ -59,15 +59,15 @@ struct KvLds {
 // a global-load phase (into registers) and an LDS-store phase so that callers
 // can overlap other loads with it.  Rows past n_k are zero-filled (they are
 // masked anyway).
-template <typename T, int D>
+template <typename T, int D, int BK>
 struct KvStage {
-  using L = KvLds<T, D>;
+  using L = KvLds<T, D, BK>;
   static constexpr int CPR = D * (int)sizeof(T) / 16;  // 16-byte chunks per K row
-  static constexpr int KCH = kBk * CPR;
+  static constexpr int KCH = BK * CPR;
   static constexpr int KLD = (KCH + 255) / 256;
   static constexpr int DCH = D / 8;         // 8-element chunks per V row
   static constexpr int KG = 256 / DCH;      // groups of 4 keys per pass
-  static constexpr int PASSES = kBk / (4 * KG);
+  static constexpr int PASSES = (BK + 4 * KG - 1) / (4 * KG);  // the last pass may be partial
   u32x4 kr[KLD];
   frag_t<T> vr[PASSES][4];
 
@@ -76,7 +76,7 @@ struct KvStage {
     for (int u = 0; u < KLD; ++u) {
       const int c = tid + u * 256;
       const int row = c / CPR, col = c % CPR;
-      const int64_t t = (int64_t)j * kBk + row;
+      const int64_t t = (int64_t)j * BK + row;
       kr[u] = u32x4{};
       if (c < KCH && t < n_k)
         kr[u] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(kbase + t * tok_stride) + col * 16);
@@ -86,8 +86,9 @@ struct KvStage {
     for (int ps = 0; ps < PASSES; ++ps)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int64_t t = (int64_t)j * kBk + (ps * KG + kg) * 4 + r;
-        vr[ps][r] = t < n_k ? load8(vbase + t * tok_stride + dch * 8) : zero_frag<T>();
+        const int key = (ps * KG + kg) * 4 + r;
+        const int64_t t = (int64_t)j * BK + key;
+        vr[ps][r] = key < BK && t < n_k ? load8(vbase + t * tok_stride + dch * 8) : zero_frag<T>();
       }
   }
 
@@ -103,6 +104,7 @@ struct KvStage {
 #pragma unroll
     for (int ps = 0; ps < PASSES; ++ps) {
       const int key0 = (ps * KG + kg) * 4;
+      if (key0 >= BK) continue;  // a partial last pass (blocks smaller than 4 * KG keys)
       if constexpr (sizeof(T) == 2) {
         // 2x2 transposes of 16-bit halves with byte permutes (v_perm_b32).
 #pragma unroll
@@ -129,18 +131,18 @@ struct KvStage {
   }
 };
 
-template <typename T, int D>
+template <typename T, int D, int BK>
 __device__ __forceinline__ void stage_kv(char* lds, const T* kbase, const T* vbase, int64_t tok_stride, int j,
                                          int n_k, int tid) {
-  KvStage<T, D> st;
+  KvStage<T, D, BK> st;
   st.load(kbase, vbase, tok_stride, j, n_k, tid);
   st.store(lds, tid);
 }
 
 // A fragment of V^T for k-step (mt, a): row d, keys 32mt+16a+4h+[0..3] and +8.
-template <typename T, int D>
+template <typename T, int D, int BK>
 __device__ __forceinline__ frag_t<T> vt_frag(const char* lds, int d, int mt, int a, int half) {
-  using L = KvLds<T, D>;
+  using L = KvLds<T, D, BK>;
   const char* vt = lds + L::KBYTES;
   const int c0 = 8 * mt + 4 * a + half;  // chunk of keys 32mt+16a+4h .. +3
   const typename Pack4<T>::type lo = *reinterpret_cast<const typename Pack4<T>::type*>(vt + L::vt_off(d, c0));
@@ -162,15 +164,16 @@ template <> __device__ __forceinline__ float from_f32<float>(float x) { return x
 // O^T = V^T P^T.  Lane (c = lane%32, h = lane/32) ends with the tile row c's
 // block max (log2 domain, already scaled) m, sum l, and its 64 of the D output
 // values in o[dt][e] for d = 32dt + 8(e/4) + 4h + e%4.
-template <typename T, int D>
-// Keys at offsets >= vis (0..128) inside the block are masked when need_mask.
+// Keys at offsets >= vis (0..BK) inside the block are masked when need_mask.
+template <typename T, int D, int BK>
 __device__ __forceinline__ void block_tile(const char* lds, const frag_t<T> (&qf)[D / 16], float c_log2, int vis,
                                            bool need_mask, float& m, float& l, f32x16 (&o)[D / 32]) {
-  using L = KvLds<T, D>;
+  using L = KvLds<T, D, BK>;
+  constexpr int MT = BK / 32;  // 32-key M-tiles per block
   const int lane = threadIdx.x & 63, half = lane >> 5;
-  f32x16 s[4];
+  f32x16 s[MT];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
+  for (int mt = 0; mt < MT; ++mt) {
     const T* arow = reinterpret_cast<const T*>(lds + (mt * 32 + (lane & 31)) * L::KPITCH) + 8 * half;
     s[mt] = mma0(load8(arow), qf[0]);
 #pragma unroll
@@ -178,7 +181,7 @@ __device__ __forceinline__ void block_tile(const char* lds, const frag_t<T> (&qf
   }
   if (need_mask) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int t = 32 * mt + 8 * (e / 4) + 4 * half + (e % 4);
@@ -187,12 +190,12 @@ __device__ __forceinline__ void block_tile(const char* lds, const frag_t<T> (&qf
   }
   float mx = -__builtin_huge_valf();
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) mx = max16(s[mt], mx);
+  for (int mt = 0; mt < MT; ++mt) mx = max16(s[mt], mx);
   mx = fmaxf(mx, xor_shfl(mx, 32));
   const float mref = mx == -__builtin_huge_valf() ? 0.f : mx * c_log2;
   float sum = 0.f;
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const float p = exp2_fast(fmaf(s[mt][e], c_log2, -mref));
@@ -201,7 +204,7 @@ __device__ __forceinline__ void block_tile(const char* lds, const frag_t<T> (&qf
     }
   sum += xor_shfl(sum, 32);
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
       frag_t<T> pb;
@@ -209,7 +212,7 @@ __device__ __forceinline__ void block_tile(const char* lds, const frag_t<T> (&qf
       for (int e = 0; e < 8; ++e) pb[e] = from_f32<T>(s[mt][8 * a + e]);
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        const frag_t<T> va = vt_frag<T, D>(lds, 32 * dt + (lane & 31), mt, a, half);
+        const frag_t<T> va = vt_frag<T, D, BK>(lds, 32 * dt + (lane & 31), mt, a, half);
         if (mt == 0 && a == 0) o[dt] = mma0(va, pb);
         else mma(va, pb, o[dt]);
       }
@@ -281,7 +284,7 @@ struct KvArgs {
 // writes them out.  Partial rows leave through LDS (`ob`, this wave's 8-row
 // buffer), 8 rows per pass, so that each store instruction writes four whole
 // rows instead of an 8-byte piece of 32.
-template <typename T, int D, bool NT>
+template <typename T, int D, bool NT, int BK>
 __device__ __forceinline__ void kv_tile(const KvArgs& a, const char* lds, const int32_t* ent_lds, char* ob, int tile,
                                         int nrows, int b, int g, int64_t key0, const TileRows& cur,
                                         const frag_t<T> (&qf)[D / 16], TileRows& nxt, frag_t<T> (&qn)[D / 16]) {
@@ -296,12 +299,12 @@ __device__ __forceinline__ void kv_tile(const KvArgs& a, const char* lds, const 
   load_q_rows<T, D>(qn, static_cast<const T*>(a.q), nxt, b, a.Nq, a.Hq, a.q0, half);
   const int64_t pos = a.q_offset + a.q0 + cur.qq;
   const int64_t vis_end = min(pos + 1, (int64_t)a.Nk);  // keys t < vis_end are visible
-  const int vis = (int)max((int64_t)0, min((int64_t)kBk, vis_end - key0));
+  const int vis = (int)max((int64_t)0, min((int64_t)BK, vis_end - key0));
   // Masking is only needed where the block reaches past a row's position.
-  const int need = __any(cur.valid && vis < kBk);
+  const int need = __any(cur.valid && vis < BK);
   float m, l;
   f32x16 o[D / 32];
-  block_tile<T, D>(lds, qf, a.c_log2, vis, need != 0, m, l, o);
+  block_tile<T, D, BK>(lds, qf, a.c_log2, vis, need != 0, m, l, o);
   const int64_t prow = (((int64_t)b * a.nq + cur.qq) * a.Hq + cur.h) * a.S + cur.slot;
   const int64_t lrow = (((int64_t)b * a.nq + cur.qq) * a.S + cur.slot) * a.Hq + cur.h;
   // Every store below is issued by every lane (rows past the item's end write
@@ -346,9 +349,9 @@ __device__ __forceinline__ void kv_tile(const KvArgs& a, const char* lds, const 
   }
 }
 
-template <typename T, int D, bool NT>
+template <typename T, int D, bool NT, int BK>
 __global__ void __launch_bounds__(256, 2) k_attn_kvouter(KvArgs a) {
-  using L = KvLds<T, D>;
+  using L = KvLds<T, D, BK>;
   __shared__ __attribute__((aligned(16))) char lds[L::BYTES];
   __shared__ int32_t ent_lds[kMaxItemEntries];
   __shared__ __attribute__((aligned(16))) char obuf[4][8 * (D * (int)sizeof(T) + 16)];
@@ -371,7 +374,7 @@ __global__ void __launch_bounds__(256, 2) k_attn_kvouter(KvArgs a) {
   const int32_t* ent = a.entries + (int64_t)bg * a.nq * a.topk + e0;
   const int nent = e1 - e0;
   const T* qbase = static_cast<const T*>(a.q);
-  const int64_t key0 = (int64_t)j * kBk;
+  const int64_t key0 = (int64_t)j * BK;
 
   // Prologue, ordered so that the loads overlap: (1) the entries (this lane's
   // first row, and the item's list for LDS), (2) K_j / V_j into registers,
@@ -385,7 +388,7 @@ __global__ void __launch_bounds__(256, 2) k_attn_kvouter(KvArgs a) {
 #pragma unroll
   for (int u = 0; u < EPT; ++u) e_mine[u] = tid + 256 * u < nent ? ent[tid + 256 * u] : 0;
   __builtin_amdgcn_sched_barrier(0);
-  KvStage<T, D> stg;
+  KvStage<T, D, BK> stg;
   stg.load(kb, vb, tok_stride, j, a.Nk, tid);
   __builtin_amdgcn_sched_barrier(0);
   // Gathered query rows of tile t: row r = t*32 + lane%32 <-> (entry r/G, head r%G).
@@ -409,11 +412,11 @@ __global__ void __launch_bounds__(256, 2) k_attn_kvouter(KvArgs a) {
   frag_t<T> qg[D / 16];
   TileRows nx;
   if (wave * 32 >= nrows) return;
-  kv_tile<T, D, NT>(a, lds, ent_lds, obuf[wave], wave, nrows, b, g, key0, cur, qf, nx, qg);
+  kv_tile<T, D, NT, BK>(a, lds, ent_lds, obuf[wave], wave, nrows, b, g, key0, cur, qf, nx, qg);
   for (int tile = wave + 4; tile * 32 < nrows; tile += 8) {
-    kv_tile<T, D, NT>(a, lds, ent_lds, obuf[wave], tile, nrows, b, g, key0, nx, qg, cur, qf);
+    kv_tile<T, D, NT, BK>(a, lds, ent_lds, obuf[wave], tile, nrows, b, g, key0, nx, qg, cur, qf);
     if ((tile + 4) * 32 >= nrows) break;
-    kv_tile<T, D, NT>(a, lds, ent_lds, obuf[wave], tile + 4, nrows, b, g, key0, cur, qf, nx, qg);
+    kv_tile<T, D, NT, BK>(a, lds, ent_lds, obuf[wave], tile + 4, nrows, b, g, key0, cur, qf, nx, qg);
   }
 }
 
@@ -432,11 +435,12 @@ struct QoArgs {
 };
 
 // grid: x = nq * Hkv, y = nsplit, z = B.  256 threads; wave w owns keys
-// [32w, 32w + 32) of every block.
-template <typename T, int D>
+// [32w, 32w + 32) of every block (waves past the block's BK / 32 tiles idle).
+template <typename T, int D, int BK>
 __global__ void __launch_bounds__(256, 2) k_attn_qouter(QoArgs a) {
-  using L = KvLds<T, D>;
-  __shared__ __attribute__((aligned(16))) char lds[L::BYTES];
+  using L = KvLds<T, D, BK>;
+  constexpr int MERGE_BYTES = 4 * D * 32 * (int)sizeof(float);  // the final merge reuses the staging area
+  __shared__ __attribute__((aligned(16))) char lds[L::BYTES > MERGE_BYTES ? L::BYTES : MERGE_BYTES];
   __shared__ float stat[4][2][32];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
   const int qq = blockIdx.x / a.Hkv, g = blockIdx.x % a.Hkv;
@@ -469,14 +473,15 @@ __global__ void __launch_bounds__(256, 2) k_attn_qouter(QoArgs a) {
     const int j = sel[s];
     if (j < 0) continue;  // uniform across the workgroup
     __syncthreads();
-    stage_kv<T, D>(lds, kb, vb, tok_stride, j, a.Nk, tid);
+    stage_kv<T, D, BK>(lds, kb, vb, tok_stride, j, a.Nk, tid);
     __syncthreads();
+    if (wave * 32 >= BK) continue;  // no keys for this wave (uniform per wave)
     // wave's 32 keys: S^T tile for M-tile `wave`
     f32x16 sc = f32x16{};
     const T* arow = reinterpret_cast<const T*>(lds + (wave * 32 + c) * L::KPITCH) + 8 * half;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) mma(load8(arow + 16 * ks), qf[ks], sc);
-    const int64_t kbase = (int64_t)j * kBk + wave * 32;
+    const int64_t kbase = (int64_t)j * BK + wave * 32;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int64_t t = kbase + 8 * (e / 4) + 4 * half + (e % 4);
@@ -507,7 +512,7 @@ __global__ void __launch_bounds__(256, 2) k_attn_qouter(QoArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) pb[e] = from_f32<T>(sc[8 * aa + e]);
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) mma(vt_frag<T, D>(lds, 32 * dt + c, wave, aa, half), pb, o[dt]);
+      for (int dt = 0; dt < D / 32; ++dt) mma(vt_frag<T, D, BK>(lds, 32 * dt + c, wave, aa, half), pb, o[dt]);
     }
   }
   // Merge the four waves' states through LDS (reusing the staging area).
@@ -652,10 +657,24 @@ __global__ void __launch_bounds__(256) k_combine(CombArgs a) {
     a.lse[((int64_t)b * a.Nq + a.q0 + qq) * a.Hq + h] = W > 0.f ? M + log2_fast(W) * kLn2 : -__builtin_huge_valf();
 }
 
+template <typename T, int D, int BK>
+void kvouter_launch_bk(bool nt, dim3 grid, hipStream_t st, const KvArgs& a) {
+  if (nt) hipLaunchKernelGGL((k_attn_kvouter<T, D, true, BK>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((k_attn_kvouter<T, D, false, BK>), grid, dim3(256), 0, st, a);
+}
+
 template <typename T, int D>
-void kvouter_launch(bool nt, dim3 grid, hipStream_t st, const KvArgs& a) {
-  if (nt) hipLaunchKernelGGL((k_attn_kvouter<T, D, true>), grid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((k_attn_kvouter<T, D, false>), grid, dim3(256), 0, st, a);
+void kvouter_launch(int bk, bool nt, dim3 grid, hipStream_t st, const KvArgs& a) {
+  if (bk == 32) kvouter_launch_bk<T, D, 32>(nt, grid, st, a);
+  else if (bk == 64) kvouter_launch_bk<T, D, 64>(nt, grid, st, a);
+  else kvouter_launch_bk<T, D, 128>(nt, grid, st, a);
+}
+
+template <typename T, int D>
+void qouter_launch(int bk, dim3 grid, hipStream_t st, const QoArgs& a) {
+  if (bk == 32) hipLaunchKernelGGL((k_attn_qouter<T, D, 32>), grid, dim3(256), 0, st, a);
+  else if (bk == 64) hipLaunchKernelGGL((k_attn_qouter<T, D, 64>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((k_attn_qouter<T, D, 128>), grid, dim3(256), 0, st, a);
 }
 
 }  // namespace
@@ -694,11 +713,11 @@ hipError_t launch_attn_kvouter(const Shape& s, const InvertPlan& p, int q0, int 
   const bool nt = (double)nq * s.topk * a.G >= (double)kItemRows * s.nblk;
   prof_begin(st, kid);
   if (s.dtype == kBF16) {
-    if (s.D == 64) kvouter_launch<bf16_t, 64>(nt, grid, st, a);
-    else kvouter_launch<bf16_t, 128>(nt, grid, st, a);
+    if (s.D == 64) kvouter_launch<bf16_t, 64>(s.Bk, nt, grid, st, a);
+    else kvouter_launch<bf16_t, 128>(s.Bk, nt, grid, st, a);
   } else {
-    if (s.D == 64) kvouter_launch<float, 64>(nt, grid, st, a);
-    else kvouter_launch<float, 128>(nt, grid, st, a);
+    if (s.D == 64) kvouter_launch<float, 64>(s.Bk, nt, grid, st, a);
+    else kvouter_launch<float, 128>(s.Bk, nt, grid, st, a);
   }
   const hipError_t e = hipGetLastError();
   prof_end(st, kid);
@@ -732,11 +751,11 @@ hipError_t launch_attn_qouter(const Shape& s, int q0, int nq, int nsplit, const 
   const dim3 grid(nq * s.Hkv, nsplit, s.B);
   prof_begin(st, kid);
   if (s.dtype == kBF16) {
-    if (s.D == 64) hipLaunchKernelGGL((k_attn_qouter<bf16_t, 64>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((k_attn_qouter<bf16_t, 128>), grid, dim3(256), 0, st, a);
+    if (s.D == 64) qouter_launch<bf16_t, 64>(s.Bk, grid, st, a);
+    else qouter_launch<bf16_t, 128>(s.Bk, grid, st, a);
   } else {
-    if (s.D == 64) hipLaunchKernelGGL((k_attn_qouter<float, 64>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((k_attn_qouter<float, 128>), grid, dim3(256), 0, st, a);
+    if (s.D == 64) qouter_launch<float, 64>(s.Bk, grid, st, a);
+    else qouter_launch<float, 128>(s.Bk, grid, st, a);
   }
   const hipError_t e = hipGetLastError();
   prof_end(st, kid);

@@ -33,7 +33,7 @@ struct TileArgs {
   const uint8_t* iks;      // MXFP8 scales (one per 32 key elements), else null
   int32_t* ids;
   float* scores;
-  int Nq, Nk, Hkv, topk, nblk, n_tiles;
+  int Nq, Nk, Hkv, topk, nblk, n_tiles, bk;
   int64_t q_offset;
 };
 
@@ -41,14 +41,19 @@ constexpr int kTileWaves = 8;
 
 // Global -> registers -> LDS staging of one 128-token key block (16-byte
 // chunks; CPR chunks per token row, row stride `rowb` bytes in HBM).
+// Chunk j covers tokens [128 j, 128 j + 128); tokens past n_k (only in the last
+// chunk, and only when blocks are smaller than a chunk) re-read token n_k - 1:
+// they belong to the last, partial block, which is never a candidate.
 template <int LOADS, int CPR, int CHUNKS, int NTHR>
-__device__ __forceinline__ void tile_gload(u32x4 (&stage)[LOADS], const char* base, int j, int64_t rowb, int tid) {
+__device__ __forceinline__ void tile_gload(u32x4 (&stage)[LOADS], const char* base, int j, int64_t rowb, int nk,
+                                           int tid) {
 #pragma unroll
   for (int u = 0; u < LOADS; ++u) {
     const int c = tid + u * NTHR;
     if (c < CHUNKS) {
       const int row = c / CPR, col = c % CPR;
-      stage[u] = *reinterpret_cast<const u32x4*>(base + ((int64_t)j * kBk + row) * rowb + col * 16);
+      const int64_t t = min((int64_t)j * kChunk + row, (int64_t)nk - 1);
+      stage[u] = *reinterpret_cast<const u32x4*>(base + t * rowb + col * 16);
     }
   }
 }
@@ -70,13 +75,13 @@ __device__ __forceinline__ void tile_lstore(const u32x4 (&stage)[LOADS], char* b
 // representable in the dtype: E4M3 carries 3 mantissa bits).
 template <int LOADS, int MCPR, int CHUNKS, int NTHR, int DI>
 __device__ __forceinline__ void mx_gload(u32x4 (&stage)[LOADS], uint32_t (&scl)[LOADS], const uint8_t* codes,
-                                         const uint8_t* scales, int j, int hkv, int tid) {
+                                         const uint8_t* scales, int j, int hkv, int nk, int tid) {
 #pragma unroll
   for (int u = 0; u < LOADS; ++u) {
     const int c = tid + u * NTHR;
     if (c < CHUNKS) {
       const int row = c / MCPR, col = c % MCPR;
-      const int64_t r = ((int64_t)j * kBk + row) * hkv;
+      const int64_t r = min((int64_t)j * kChunk + row, (int64_t)nk - 1) * hkv;
       stage[u] = *reinterpret_cast<const u32x4*>(codes + r * DI + col * 16);
       scl[u] = scales[r * (DI / 32) + col / 2];
     }
@@ -118,13 +123,14 @@ __device__ __forceinline__ void mx_lstore(const u32x4 (&stage)[LOADS], const uin
 constexpr int kDmaBufs = 4;
 constexpr int kDmaRowBytes = 256;
 
-__device__ __forceinline__ void dma_issue_block(char* buf, const char* ikb, int j, int64_t rowb, int wave, int lane) {
+__device__ __forceinline__ void dma_issue_block(char* buf, const char* ikb, int j, int64_t rowb, int nk, int wave,
+                                                int lane) {
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int slot = wave * 4 + u;  // 1 KB slot = 4 rows
     const int r = slot * 4 + lane / 16;
     const int c = (lane & 15) ^ (r & 15);
-    const char* src = ikb + ((int64_t)j * kBk + r) * rowb + c * 16;
+    const char* src = ikb + min((int64_t)j * kChunk + r, (int64_t)nk - 1) * rowb + c * 16;
     __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src), buf + slot * 1024, 16, 0, 0);
   }
 }
@@ -159,15 +165,15 @@ __global__ void __launch_bounds__(kTileWaves * 64) k_index_tile(TileArgs a) {
   constexpr int PITCH = ROW_BYTES + 16;  // padded LDS row: conflict-free 16-byte reads
   constexpr int KSTEPS = DI / 16;
   constexpr int CPR = ROW_BYTES / 16;  // 16-byte chunks per key row
-  constexpr int CHUNKS = kBk * CPR;
+  constexpr int CHUNKS = kChunk * CPR;
   constexpr int NTHR = WAVES * 64;
   constexpr int LOADS = (CHUNKS + NTHR - 1) / NTHR;
   constexpr bool DMA = !MX && ROW_BYTES == kDmaRowBytes && WAVES == 8;  // 8 waves x 4 loads = one block
   constexpr int MCPR = DI / 16;  // MXFP8: 16-byte code chunks per key row
-  constexpr int MCHUNKS = kBk * MCPR;
+  constexpr int MCHUNKS = kChunk * MCPR;
   constexpr int MLOADS = (MCHUNKS + NTHR - 1) / NTHR;
   constexpr int NBUF = DMA ? kDmaBufs : 2;
-  constexpr int BUFB = DMA ? kBk * kDmaRowBytes : kBk * PITCH;
+  constexpr int BUFB = DMA ? kChunk * kDmaRowBytes : kChunk * PITCH;
   __shared__ __attribute__((aligned(16))) char lds[NBUF][BUFB];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
@@ -176,7 +182,10 @@ __global__ void __launch_bounds__(kTileWaves * 64) k_index_tile(TileArgs a) {
   const int b = blockIdx.y;
   const int q0 = tile * TQ;
   const int q_last = min(q0 + TQ, a.Nq) - 1;
-  const int j_end = (int)((a.q_offset + q_last) / kBk);
+  // Key chunks holding a candidate block of some query of the tile.
+  const int j_end = (int)(((a.q_offset + q_last) / a.bk * a.bk + kChunk - 1) / kChunk);
+  const int bpm = a.bk / 32;              // 32-key M-tiles per block
+  const int bpc = kChunk / a.bk;          // blocks per chunk
 
   const T* iq = static_cast<const T*>(a.iq);
   const int64_t krow = (int64_t)a.Hkv * DI;  // elements between consecutive tokens
@@ -197,7 +206,7 @@ __global__ void __launch_bounds__(kTileWaves * 64) k_index_tile(TileArgs a) {
   // Query owned by this lane after the max-pool exchange.
   const int q_own = q0 + wave * NT * 32 + (NT == 2 ? lane : (lane & 31));
   const bool own_valid = q_own < a.Nq && (NT == 2 || half == 0);
-  const int L_own = own_valid ? (int)((a.q_offset + q_own) / kBk) : 0;
+  const int L_own = own_valid ? (int)((a.q_offset + q_own) / a.bk) : 0;
 
   TopList<KMAX> list;
   list.init();
@@ -207,15 +216,15 @@ __global__ void __launch_bounds__(kTileWaves * 64) k_index_tile(TileArgs a) {
     u32x4 mstage[MLOADS];
     uint32_t mscl[MLOADS];
     if constexpr (MX) {
-      mx_gload<MLOADS, MCPR, MCHUNKS, NTHR, DI>(mstage, mscl, ikc, iks, 0, a.Hkv, tid);
+      mx_gload<MLOADS, MCPR, MCHUNKS, NTHR, DI>(mstage, mscl, ikc, iks, 0, a.Hkv, a.Nk, tid);
       mx_lstore<T, MLOADS, MCPR, MCHUNKS, NTHR, PITCH>(mstage, mscl, lds[0], tid);
       __syncthreads();
     } else if constexpr (DMA) {
 #pragma unroll
       for (int sb = 0; sb < NBUF - 1; ++sb)
-        if (sb < j_end) dma_issue_block(lds[sb], ikb, sb, krow * (int64_t)sizeof(T), wave, lane);
+        if (sb < j_end) dma_issue_block(lds[sb], ikb, sb, krow * (int64_t)sizeof(T), a.Nk, wave, lane);
     } else {
-      tile_gload<LOADS, CPR, CHUNKS, NTHR>(stage, ikb, 0, krow * (int64_t)sizeof(T), tid);
+      tile_gload<LOADS, CPR, CHUNKS, NTHR>(stage, ikb, 0, krow * (int64_t)sizeof(T), a.Nk, tid);
       tile_lstore<LOADS, CPR, CHUNKS, NTHR, PITCH>(stage, lds[0], tid);
       __syncthreads();
     }
@@ -228,11 +237,11 @@ __global__ void __launch_bounds__(kTileWaves * 64) k_index_tile(TileArgs a) {
         else wait_vmcnt<0>();
         __syncthreads();
         if (j + NBUF - 1 < j_end)
-          dma_issue_block(lds[(j + NBUF - 1) % NBUF], ikb, j + NBUF - 1, krow * (int64_t)sizeof(T), wave, lane);
+          dma_issue_block(lds[(j + NBUF - 1) % NBUF], ikb, j + NBUF - 1, krow * (int64_t)sizeof(T), a.Nk, wave, lane);
       } else if constexpr (MX) {
-        if (j + 1 < j_end) mx_gload<MLOADS, MCPR, MCHUNKS, NTHR, DI>(mstage, mscl, ikc, iks, j + 1, a.Hkv, tid);
+        if (j + 1 < j_end) mx_gload<MLOADS, MCPR, MCHUNKS, NTHR, DI>(mstage, mscl, ikc, iks, j + 1, a.Hkv, a.Nk, tid);
       } else {
-        if (j + 1 < j_end) tile_gload<LOADS, CPR, CHUNKS, NTHR>(stage, ikb, j + 1, krow * (int64_t)sizeof(T), tid);
+        if (j + 1 < j_end) tile_gload<LOADS, CPR, CHUNKS, NTHR>(stage, ikb, j + 1, krow * (int64_t)sizeof(T), a.Nk, tid);
       }
       float run[NT];
 #pragma unroll
@@ -262,19 +271,25 @@ __global__ void __launch_bounds__(kTileWaves * 64) k_index_tile(TileArgs a) {
           for (int nt = 0; nt < NT; ++nt) mma(A[mt & 1][ks], bq[nt][ks], acc[nt]);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) run[nt] = max16(acc[nt], run[nt]);
-      }
-      // Each half of the wave saw 64 of the 128 keys; swap halves so that lane l
-      // ends with the full block max of query q0 + wave*NT*32 + l.
-      float own;
-      if (NT == 2) {
-        const float give = half ? run[0] : run[1];
-        own = fmaxf(half ? run[1] : run[0], xor_shfl(give, 32));
-      } else {
-        own = fmaxf(run[0], xor_shfl(run[0], 32));
-      }
-      if (j < L_own) {
-        if (TOPK) list.offer(own, j);
-        if (WRITE_S) a.scores[(((int64_t)b * a.Hkv + g) * a.Nq + q_own) * a.nblk + j] = own;
+        if (((mt + 1) & (bpm - 1)) == 0) {
+          // Last M-tile of a key block.  Each half of the wave saw half of the
+          // block's keys; swap halves so that lane l ends with the full block
+          // max of query q0 + wave*NT*32 + l.
+          float own;
+          if (NT == 2) {
+            const float give = half ? run[0] : run[1];
+            own = fmaxf(half ? run[1] : run[0], xor_shfl(give, 32));
+          } else {
+            own = fmaxf(run[0], xor_shfl(run[0], 32));
+          }
+          const int jb = j * bpc + mt / bpm;  // blocks arrive in increasing order
+          if (jb < L_own) {
+            if (TOPK) list.offer(own, jb);
+            if (WRITE_S) a.scores[(((int64_t)b * a.Hkv + g) * a.Nq + q_own) * a.nblk + jb] = own;
+          }
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) run[nt] = -__builtin_huge_valf();
+        }
       }
       if constexpr (MX) {
         if (j + 1 < j_end) mx_lstore<T, MLOADS, MCPR, MCHUNKS, NTHR, PITCH>(mstage, mscl, lds[(j + 1) & 1], tid);
@@ -299,7 +314,7 @@ struct ScanArgs {
   const void* ik;          // keys in the dtype, or MXFP8 codes
   const uint8_t* iks;      // MXFP8 scales, else null
   float* scores;
-  int Nq, Nk, Hkv, nblk, blocks_per_wg, j_end;
+  int Nq, Nk, Hkv, nblk, blocks_per_wg, j_end, bk;  // j_end, blocks_per_wg: 128-token chunks
   int64_t q_offset;
 };
 
@@ -318,7 +333,7 @@ __global__ void __launch_bounds__(kScanThreads) k_index_scan(ScanArgs a) {
   extern __shared__ __attribute__((aligned(16))) float smem[];
   float* qs = smem;                              // [NQ][Hkv][DI] index queries (fp32)
   float* dots = smem + NQ * a.Hkv * DI;          // [NQ][Hkv][128] token scores of one block
-  uint8_t* sscl = reinterpret_cast<uint8_t*>(dots + NQ * a.Hkv * kBk);  // MXFP8: the block's scale bytes
+  uint8_t* sscl = reinterpret_cast<uint8_t*>(dots + NQ * a.Hkv * kChunk);  // MXFP8: the chunk's scale bytes
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = blockIdx.y;
@@ -330,23 +345,27 @@ __global__ void __launch_bounds__(kScanThreads) k_index_scan(ScanArgs a) {
   __syncthreads();
 
   const int c = tid % C, rsub = tid / C;
-  const int rows = kBk * H;
-  const int iters = rows / ROWS_IT;  // H * DI / 16 (exact: 128*8 divisible by C)
+  const int rows = kChunk * H;
+  const int iters = rows / ROWS_IT;  // exact: 128 * H rows, ROWS_IT divides 128
   const int jb = blockIdx.x * a.blocks_per_wg;
   const int je = min(jb + a.blocks_per_wg, a.j_end);
   for (int j = jb; j < je; ++j) {
-    const int64_t row0 = ((int64_t)b * a.Nk + (int64_t)j * kBk) * H;  // first (token, group) row of block j
+    // Chunk j: tokens [128 j, 128 j + ntok); tokens past n_k (possible in the last
+    // chunk when blocks are smaller than a chunk) are skipped -- they belong to
+    // the last, partial block, which is never a candidate.
+    const int ntok = (int)min((int64_t)kChunk, (int64_t)a.Nk - (int64_t)j * kChunk);
+    const int64_t row0 = ((int64_t)b * a.Nk + (int64_t)j * kChunk) * H;  // first (token, group) row of chunk j
     const T* blk = ik + row0 * DI;
     const uint8_t* blkc = static_cast<const uint8_t*>(a.ik) + row0 * DI;
     if constexpr (MX) {
-      // The block's scale bytes (128 * Hkv * DI/32, contiguous) go to LDS with
+      // The chunk's scale bytes (ntok * Hkv * DI/32, contiguous) go to LDS with
       // one 16-byte load per thread instead of a byte load per row and lane.
       const uint8_t* blks = a.iks + row0 * (DI / 32);
-      const int nbytes = kBk * H * (DI / 32);
-      if ((reinterpret_cast<uintptr_t>(blks) & 15) == 0) {
+      const int nbytes = ntok * H * (DI / 32);
+      if ((reinterpret_cast<uintptr_t>(blks) & 15) == 0 && (nbytes & 15) == 0) {
         for (int ch = tid; ch < nbytes / 16; ch += kScanThreads)
           reinterpret_cast<u32x4*>(sscl)[ch] = reinterpret_cast<const u32x4*>(blks)[ch];
-      } else {  // a batch entry whose scales do not start on 16 bytes (odd Nk)
+      } else {  // scales not on a 16-byte boundary (odd Nk), or a partial chunk
         for (int i = tid; i < nbytes; i += kScanThreads) sscl[i] = blks[i];
       }
       __syncthreads();
@@ -358,15 +377,16 @@ __global__ void __launch_bounds__(kScanThreads) k_index_scan(ScanArgs a) {
 #pragma unroll
       for (int u = 0; u < kScanUnroll; ++u) {
         const int row = (it0 + u) * ROWS_IT + rsub;
+        const bool live = it0 + u < iters && row < ntok * H;
         if constexpr (MX) {
           xc[u] = u32x4{};
           xs[u] = 127;
-          if (it0 + u < iters) {
+          if (live) {
             xc[u] = *reinterpret_cast<const u32x4*>(blkc + (int64_t)row * DI + c * 16);
             xs[u] = sscl[row * (DI / 32) + c / 2];
           }
         } else {
-          x[u] = (it0 + u < iters) ? load8(blk + (int64_t)row * DI + c * 8) : zero_frag<T>();
+          x[u] = live ? load8(blk + (int64_t)row * DI + c * 8) : zero_frag<T>();
         }
       }
 #pragma unroll
@@ -393,20 +413,42 @@ __global__ void __launch_bounds__(kScanThreads) k_index_scan(ScanArgs a) {
             if constexpr (MX) acc = __builtin_ldexpf(acc, (int)xs[u] - 127);
 #pragma unroll
             for (int m = C / 2; m >= 1; m >>= 1) acc += xor_shfl(acc, m);
-            if (c == 0 && it0 + u < iters) dots[(qi * H + grp) * kBk + tok] = acc;
+            if (c == 0 && it0 + u < iters) dots[(qi * H + grp) * kChunk + tok] = acc;
           }
         }
       }
     }
     __syncthreads();
-    // max over the 128 tokens of block j for every (query, group)
+    // max over the Bk tokens of each block of chunk j, for every (query, group):
+    // lane l holds tokens l and 64 + l; blocks of 128 / 64 / 32 tokens are
+    // reduced over 64 / 64 / 32 lanes.
     for (int r = wave; r < a.Nq * H; r += kScanThreads / 64) {
-      float m = fmaxf(dots[r * kBk + lane], dots[r * kBk + 64 + lane]);
+      float m0 = dots[r * kChunk + lane], m1 = dots[r * kChunk + 64 + lane];
+      if (a.bk == kChunk) m0 = m1 = fmaxf(m0, m1);
+      const int span = a.bk == 32 ? 16 : 32;
 #pragma unroll
-      for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, xor_shfl(m, s));
+      for (int s = 32; s >= 1; s >>= 1)
+        if (s <= span) {
+          m0 = fmaxf(m0, xor_shfl(m0, s));
+          m1 = fmaxf(m1, xor_shfl(m1, s));
+        }
       const int qi = r / H, grp = r % H;
-      const int L = (int)((a.q_offset + qi) / kBk);
-      if (lane == 0 && j < L) a.scores[(((int64_t)b * H + grp) * a.Nq + qi) * a.nblk + j] = m;
+      const int L = (int)((a.q_offset + qi) / a.bk);
+      const int bpc = kChunk / a.bk;
+      // lane 0 writes the first block of each half-chunk; for 32-token blocks
+      // lane 32 writes the second one
+      const int sub = a.bk == 32 ? (lane >> 5) : 0;
+      if ((lane & 31) == 0 && (lane == 0 || a.bk == 32)) {
+        float* out = a.scores + (((int64_t)b * H + grp) * a.Nq + qi) * a.nblk;
+        const int jb0 = j * bpc + sub;              // block of tokens 0..63
+        const int jb1 = j * bpc + bpc / 2 + sub;    // block of tokens 64..127
+        if (a.bk == kChunk) {
+          if (jb0 < L) out[jb0] = m0;
+        } else {
+          if (jb0 < L) out[jb0] = m0;
+          if (jb1 < L) out[jb1] = m1;
+        }
+      }
     }
     __syncthreads();
   }
@@ -449,7 +491,7 @@ hipError_t tile_dispatch_fmt(const Shape& s, const TileArgs& a, dim3 grid, hipSt
 template <typename T, int DI, bool MX>
 hipError_t scan_dispatch(const Shape& s, const ScanArgs& a, dim3 grid, hipStream_t st) {
   const int nq = s.Nq <= 1 ? 1 : s.Nq <= 2 ? 2 : s.Nq <= 4 ? 4 : 8;
-  const size_t shm_q = (size_t)nq * s.Hkv * (DI + kBk) * sizeof(float) + (MX ? (size_t)kBk * s.Hkv * (DI / 32) : 0);
+  const size_t shm_q = (size_t)nq * s.Hkv * (DI + kChunk) * sizeof(float) + (MX ? (size_t)kChunk * s.Hkv * (DI / 32) : 0);
   if (s.Nq <= 1) hipLaunchKernelGGL((k_index_scan<T, DI, 1, MX>), grid, dim3(kScanThreads), shm_q, st, a);
   else if (s.Nq <= 2) hipLaunchKernelGGL((k_index_scan<T, DI, 2, MX>), grid, dim3(kScanThreads), shm_q, st, a);
   else if (s.Nq <= 4) hipLaunchKernelGGL((k_index_scan<T, DI, 4, MX>), grid, dim3(kScanThreads), shm_q, st, a);
@@ -504,6 +546,7 @@ hipError_t launch_index_tile(const Shape& s, const void* iq, const void* ik, int
   a.topk = s.topk;
   a.nblk = s.nblk;
   a.n_tiles = (s.Nq + tile_queries(s) - 1) / tile_queries(s);
+  a.bk = s.Bk;
   a.q_offset = s.q_offset;
   const dim3 grid(a.n_tiles * s.Hkv, s.B);
   prof_begin(st, kid);
@@ -529,7 +572,9 @@ hipError_t launch_index_scan(const Shape& s, const void* iq, const void* ik, flo
   a.Hkv = s.Hkv;
   a.nblk = s.nblk;
   a.q_offset = s.q_offset;
-  a.j_end = (int)((s.q_offset + s.Nq - 1) / kBk);  // candidates of the last query
+  a.bk = s.Bk;
+  // chunks holding a candidate block of the last query
+  a.j_end = (int)(((s.q_offset + s.Nq - 1) / s.Bk * s.Bk + kChunk - 1) / kChunk);
   if (a.j_end <= 0) return hipSuccess;
   a.blocks_per_wg = 2;
   const dim3 grid((a.j_end + a.blocks_per_wg - 1) / a.blocks_per_wg, s.B);

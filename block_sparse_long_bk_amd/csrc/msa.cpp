@@ -40,13 +40,13 @@ msa_status_t validate(const msa_problem_t* p) {
   if (!std::isfinite(p->softmax_scale)) return MSA_ERR_INVALID_ARG;
   if (p->idx_format != MSA_IDX_PLAIN && p->idx_format != MSA_IDX_MXFP8) return MSA_ERR_INVALID_ARG;
   // Valid but outside what the kernels are built for.
-  if (p->block_size != 128) return MSA_ERR_UNSUPPORTED;
+  if (p->block_size != 32 && p->block_size != 64 && p->block_size != 128) return MSA_ERR_UNSUPPORTED;
   if (p->d != 64 && p->d != 128) return MSA_ERR_UNSUPPORTED;
   if (p->d_idx != 32 && p->d_idx != 64 && p->d_idx != 128) return MSA_ERR_UNSUPPORTED;
   if (p->topk > 32) return MSA_ERR_UNSUPPORTED;
   const int G = p->h_q / p->h_kv;
   if (!is_pow2(G) || G > 32) return MSA_ERR_UNSUPPORTED;
-  const int64_t nblk = ((int64_t)p->n_k + 127) / 128;
+  const int64_t nblk = ((int64_t)p->n_k + p->block_size - 1) / p->block_size;
   if (nblk > 16384) return MSA_ERR_UNSUPPORTED;
   if ((int64_t)p->n_q * p->topk >= (int64_t)1 << 31) return MSA_ERR_UNSUPPORTED;
   if ((int64_t)p->batch * p->h_kv > 65535 || (int64_t)p->n_q * p->h_kv >= (int64_t)1 << 31)
@@ -67,7 +67,8 @@ msa::Shape shape_of(const msa_problem_t* p) {
   s.dtype = p->dtype == MSA_BF16 ? msa::kBF16 : msa::kF32;
   s.idx_mx = p->idx_format == MSA_IDX_MXFP8;
   s.q_offset = p->q_offset;
-  s.nblk = (p->n_k + 127) / 128;
+  s.Bk = p->block_size;
+  s.nblk = (p->n_k + s.Bk - 1) / s.Bk;
   s.scale = p->softmax_scale > 0 ? p->softmax_scale : 1.0f / std::sqrt((float)p->d);
   return s;
 }

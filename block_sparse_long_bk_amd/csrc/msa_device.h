@@ -23,7 +23,8 @@ typedef __attribute__((__vector_size__(8 * sizeof(float)))) float f32x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
 
-constexpr int kBk = 128;        // key block size (tokens)
+constexpr int kChunk = 128;     // tokens per key chunk the index kernels stage at a time
+constexpr int kMaxBk = 128;     // largest key block size (block sizes 32, 64, 128 divide a chunk)
 constexpr int kWave = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;

@@ -15,7 +15,8 @@ struct Shape {
   int B, Nq, Nk, Hq, Hkv, D, DI, topk, dtype;
   bool idx_mx;  // idx_k is an MXFP8 cache: codes, then one scale byte per 32 elements
   int64_t q_offset;
-  int nblk;     // ceil(Nk / 128)
+  int Bk;       // key block size: 32, 64 or 128
+  int nblk;     // ceil(Nk / Bk)
   float scale;  // softmax scale (natural-log domain)
 };
 

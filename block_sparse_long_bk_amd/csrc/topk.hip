@@ -1,7 +1,7 @@
 // topk.hip -- exp-free Top-k over rows of block scores (gfx950).
 //
 // Selection rule (paper summary page, "Method"; zhichai.net write-up,
-// sections 2 and 4.1): the local block L(i) = floor((q_offset + i)/128) is
+// sections 2 and 4.1): the local block L(i) = floor((q_offset + i)/Bk) is
 // always kept; the other k-1 slots go to the candidate blocks j < L(i) with the
 // highest raw scores -- no exponential, since only the order matters.  Equal
 // scores go to the lower block id.  The row is emitted ascending, -1 padded.
@@ -18,7 +18,8 @@ namespace {
 
 template <int KMAX>
 __global__ void __launch_bounds__(256) k_topk_rows(const float* __restrict__ S, int32_t* __restrict__ ids, int Nq,
-                                                   int Hkv, int nblk, int topk, int64_t q_offset, int64_t nrows) {
+                                                   int Hkv, int nblk, int topk, int64_t q_offset, int bk,
+                                                   int64_t nrows) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= nrows) return;  // whole wave leaves together
@@ -26,7 +27,7 @@ __global__ void __launch_bounds__(256) k_topk_rows(const float* __restrict__ S, 
   const int64_t bg = row / Nq;
   const int g = (int)(bg % Hkv);
   const int64_t b = bg / Hkv;
-  const int L = (int)((q_offset + i) / kBk);
+  const int L = (int)((q_offset + i) / bk);
   const float* Sr = S + row * nblk;
 
   TopList<KMAX> list;
@@ -65,7 +66,8 @@ __global__ void __launch_bounds__(256) k_topk_rows(const float* __restrict__ S, 
 constexpr int kTopkWgThreads = 1024;
 template <int KMAX>
 __global__ void __launch_bounds__(kTopkWgThreads) k_topk_wg(const float* __restrict__ S, int32_t* __restrict__ ids,
-                                                             int Nq, int Hkv, int nblk, int topk, int64_t q_offset) {
+                                                             int Nq, int Hkv, int nblk, int topk, int64_t q_offset,
+                                                             int bk) {
   constexpr int NW = kTopkWgThreads / 64;
   constexpr int CPL = (NW * KMAX + 63) / 64;  // merge candidates per lane of wave 0
   __shared__ float cs[NW * KMAX];
@@ -76,7 +78,7 @@ __global__ void __launch_bounds__(kTopkWgThreads) k_topk_wg(const float* __restr
   const int64_t bg = row / Nq;
   const int g = (int)(bg % Hkv);
   const int64_t b = bg / Hkv;
-  const int L = (int)((q_offset + i) / kBk);
+  const int L = (int)((q_offset + i) / bk);
   const float* Sr = S + row * nblk;
   const int nsel = min(topk - 1, L);
 
@@ -175,17 +177,17 @@ hipError_t launch_topk_rows(const Shape& s, const float* scores, int32_t* ids, h
   if (nrows <= 4096 && s.nblk >= 2048) {
     const dim3 g1((unsigned)nrows);
     if (kneed <= 8)
-      hipLaunchKernelGGL(k_topk_wg<8>, g1, dim3(kTopkWgThreads), 0, st, scores, ids, s.Nq, s.Hkv, s.nblk, s.topk, s.q_offset);
+      hipLaunchKernelGGL(k_topk_wg<8>, g1, dim3(kTopkWgThreads), 0, st, scores, ids, s.Nq, s.Hkv, s.nblk, s.topk, s.q_offset, s.Bk);
     else if (kneed <= 16)
-      hipLaunchKernelGGL(k_topk_wg<16>, g1, dim3(kTopkWgThreads), 0, st, scores, ids, s.Nq, s.Hkv, s.nblk, s.topk, s.q_offset);
+      hipLaunchKernelGGL(k_topk_wg<16>, g1, dim3(kTopkWgThreads), 0, st, scores, ids, s.Nq, s.Hkv, s.nblk, s.topk, s.q_offset, s.Bk);
     else
-      hipLaunchKernelGGL(k_topk_wg<32>, g1, dim3(kTopkWgThreads), 0, st, scores, ids, s.Nq, s.Hkv, s.nblk, s.topk, s.q_offset);
+      hipLaunchKernelGGL(k_topk_wg<32>, g1, dim3(kTopkWgThreads), 0, st, scores, ids, s.Nq, s.Hkv, s.nblk, s.topk, s.q_offset, s.Bk);
   } else if (kneed <= 8) {
-    hipLaunchKernelGGL(k_topk_rows<8>, grid, dim3(256), 0, st, scores, ids, s.Nq, s.Hkv, s.nblk, s.topk, s.q_offset, nrows);
+    hipLaunchKernelGGL(k_topk_rows<8>, grid, dim3(256), 0, st, scores, ids, s.Nq, s.Hkv, s.nblk, s.topk, s.q_offset, s.Bk, nrows);
   } else if (kneed <= 16) {
-    hipLaunchKernelGGL(k_topk_rows<16>, grid, dim3(256), 0, st, scores, ids, s.Nq, s.Hkv, s.nblk, s.topk, s.q_offset, nrows);
+    hipLaunchKernelGGL(k_topk_rows<16>, grid, dim3(256), 0, st, scores, ids, s.Nq, s.Hkv, s.nblk, s.topk, s.q_offset, s.Bk, nrows);
   } else {
-    hipLaunchKernelGGL(k_topk_rows<32>, grid, dim3(256), 0, st, scores, ids, s.Nq, s.Hkv, s.nblk, s.topk, s.q_offset, nrows);
+    hipLaunchKernelGGL(k_topk_rows<32>, grid, dim3(256), 0, st, scores, ids, s.Nq, s.Hkv, s.nblk, s.topk, s.q_offset, s.Bk, nrows);
   }
   const hipError_t e = hipGetLastError();
   prof_end(st, kid);

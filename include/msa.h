@@ -41,7 +41,8 @@
  *   - Results are bitwise reproducible for identical inputs and do not depend
  *     on how the library splits the work (query chunks, workspace size).
  *
- * Supported: dtype MSA_BF16 or MSA_F32; block_size 128; d in {64, 128};
+ * Supported: dtype MSA_BF16 or MSA_F32; block_size in {32, 64, 128} (the
+ * pages use 128 and ablate the smaller sizes); d in {64, 128};
  * d_idx in {32, 64, 128}; 1 <= topk <= 32; Hq / Hkv a power of two <= 32;
  * 0 <= q_offset and q_offset + Nq <= Nk.
  *

@@ -54,7 +54,11 @@ def test_status_strings():
     (dict(idx_format=2), api.MSA_ERR_INVALID_ARG),
     (dict(idx_format="mxfp8"), api.MSA_OK),
     (dict(idx_format="mxfp8", dtype="bf16", d=128, d_idx=32, h_q=64, h_kv=8, topk=16), api.MSA_OK),
-    (dict(block_size=64), api.MSA_ERR_UNSUPPORTED),
+    (dict(block_size=64), api.MSA_OK),
+    (dict(block_size=32), api.MSA_OK),
+    (dict(block_size=96), api.MSA_ERR_UNSUPPORTED),
+    (dict(block_size=256), api.MSA_ERR_UNSUPPORTED),
+    (dict(block_size=32, n_k=1 << 20, n_q=1, q_offset=(1 << 20) - 1), api.MSA_ERR_UNSUPPORTED),  # 32768 blocks
     (dict(d=96), api.MSA_ERR_UNSUPPORTED),
     (dict(d_idx=48), api.MSA_ERR_UNSUPPORTED),
     (dict(topk=33), api.MSA_ERR_UNSUPPORTED),

@@ -65,6 +65,9 @@ MX_CASES = {
     "mx_bf16_decode": dict(dtype="bf16", batch=3, n_q=1, n_k=5000, q_offset=4999, h_q=16, h_kv=2, d=128,
                            d_idx=128, topk=8),
     "mx_f32_few_queries": dict(n_q=5, n_k=3000, q_offset=2995, d_idx=64, topk=4),
+    "mx_bf16_bk64": dict(dtype="bf16", n_q=700, n_k=700, h_q=8, h_kv=2, d=64, d_idx=128, topk=8, block_size=64),
+    "mx_bf16_bk32_decode": dict(dtype="bf16", batch=2, n_q=1, n_k=3001, q_offset=3000, h_q=8, h_kv=2, d=64,
+                                d_idx=64, topk=8, block_size=32),
     "mx_bf16_long_decode": dict(dtype="bf16", batch=2, n_q=1, n_k=2100 * 128 + 77, q_offset=2100 * 128 + 76,
                                 h_q=8, h_kv=2, d=64, d_idx=32, topk=16),
 }

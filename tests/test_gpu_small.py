@@ -32,6 +32,15 @@ CASES = {
     "bf16_g32": dict(dtype="bf16", n_q=500, n_k=500, h_q=32, h_kv=1, d=64, d_idx=32, topk=3),
     "bf16_hot": dict(dtype="bf16", n_q=2048, n_k=2048, h_q=16, h_kv=2, d=128, d_idx=128, topk=6, hot_frac=0.1),
     "f32_sharp_offset": dict(n_q=333, n_k=1500, q_offset=1111, h_q=8, h_kv=2, d=128, d_idx=128, topk=5, sharp=True),
+    # smaller key blocks (the pages' block-size ablation): both index kernels,
+    # both schedules, partial last 128-token chunks
+    "bf16_bk64": dict(dtype="bf16", n_q=1000, n_k=1000, h_q=16, h_kv=4, d=128, d_idx=128, topk=8, block_size=64),
+    "f32_bk32": dict(n_q=700, n_k=700, h_q=8, h_kv=2, d=64, d_idx=32, topk=6, block_size=32),
+    "bf16_bk32_offset": dict(dtype="bf16", n_q=300, n_k=2050, q_offset=1750, h_q=8, h_kv=1, d=128, d_idx=64,
+                             topk=12, block_size=32),
+    "bf16_bk64_decode": dict(dtype="bf16", batch=2, n_q=1, n_k=5001, q_offset=5000, h_q=16, h_kv=2, d=128,
+                             d_idx=128, topk=16, block_size=64),
+    "f32_bk32_few": dict(n_q=5, n_k=3000, q_offset=2995, topk=4, block_size=32),
     # more than 2048 candidate blocks and few rows: the workgroup-per-row Top-k
     "bf16_long_decode": dict(dtype="bf16", batch=2, n_q=1, n_k=2100 * 128 + 77, q_offset=2100 * 128 + 76, h_q=8,
                              h_kv=2, d=64, d_idx=32, topk=16),
