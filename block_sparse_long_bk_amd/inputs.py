@@ -72,6 +72,13 @@ WORKLOADS = {
                              "bf16", 0.0, 1003),
     "chunk_16k_at_1m": Workload("chunk_16k_at_1m", 1, 16384, 1 << 20, (1 << 20) - 16384, 128, 16, 64, 8, 128,
                                 128, "bf16", 0.02, 1004),
+    # The block-size ablation at the prefill shape: 64-token blocks keep the
+    # 2048-token budget (k = 32); 32-token blocks with k = 32 (the largest k
+    # supported) select 1024 tokens.
+    "prefill_32k_bk64": Workload("prefill_32k_bk64", 1, 32768, 32768, 0, 64, 32, 64, 8, 128, 128, "bf16", 0.0,
+                                 1005),
+    "prefill_32k_bk32": Workload("prefill_32k_bk32", 1, 32768, 32768, 0, 32, 32, 64, 8, 128, 128, "bf16", 0.0,
+                                 1006),
 }
 
 

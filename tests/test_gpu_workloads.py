@@ -1,4 +1,4 @@
-"""GPU parity at the full sizes of the five measured workloads, in the launch
+"""GPU parity at the full sizes of the measured workloads (the five configs and the block-size ablation at the prefill shape), in the launch
 configuration bench.py times (msa_forward, AUTO schedule, full workspace).
 
 The oracle evaluates a stratified sample of queries (first, last, block
@@ -105,3 +105,11 @@ def test_chunk_16k_at_1m():
 
 def test_decode_16x1m():
     run_workload("decode_16x1m", 1, batches=[0, 7, 15], scheds=("auto", "kv_outer"))
+
+
+def test_prefill_32k_bk64():
+    run_workload("prefill_32k_bk64", 128, scheds=("auto", "q_outer"))
+
+
+def test_prefill_32k_bk32():
+    run_workload("prefill_32k_bk32", 128)
