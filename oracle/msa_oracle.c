@@ -202,15 +202,68 @@ int mo_invert(const mo_problem* p, const int32_t* ids, int32_t* offsets, int32_t
 }
 
 /* Step 4: exact softmax attention restricted to the selected blocks. */
+/* Query head h belongs to GQA group h / G (contiguous heads per group). */
+static int64_t group_of(const mo_problem* p, int64_t h) { return h / (p->h_q / p->h_kv); }
+
+/* The attention scale: 1/sqrt(d) unless the problem gives one. */
+static double softmax_scale(const mo_problem* p) {
+  const int64_t D = p->d;
+  return p->softmax_scale > 0 ? p->softmax_scale : 1.0 / sqrt((double)D);
+}
+
+/* T: the visible tokens (t <= pos, t < n_k) of the blocks listed in sel
+ * (topk entries, -1 ignored), in list order.  Returns |T|. */
+static int64_t visible_tokens(const mo_problem* p, const int32_t* sel, int64_t pos, int64_t* tok) {
+  const int64_t Bk = p->block_size, nblk = num_blocks(p);
+  int64_t n = 0;
+  for (int64_t s = 0; s < p->topk; ++s) {
+    const int64_t j = sel[s];
+    if (j < 0 || j >= nblk) continue;
+    for (int64_t t = j * Bk; t < (j + 1) * Bk; ++t)
+      if (t <= pos && t < p->n_k) tok[n++] = t;
+  }
+  return n;
+}
+
+/* Softmax attention of query head h of (b, i) over the tokens tok[0..n):
+ * x[a] = probability of token a, o = output row; returns the log-sum-exp of
+ * the scaled logits (-inf when n == 0, o then 0). */
+static double attend_row(const mo_problem* p, const void* q, const void* k, const void* v, int dtype, int64_t b,
+                         int64_t i, int64_t h, const int64_t* tok, int64_t n, double* x, double* o) {
+  const int64_t Hq = p->h_q, Hkv = p->h_kv, D = p->d, g = group_of(p, h);
+  const double scale = softmax_scale(p);
+  const int64_t qbase = ((b * p->n_q + i) * Hq + h) * D;
+  double m = -INFINITY;
+  for (int64_t a = 0; a < n; ++a) {
+    const int64_t kbase = ((b * p->n_k + tok[a]) * Hkv + g) * D;
+    double s = 0.0;
+    for (int64_t c = 0; c < D; ++c) s += widen(q, dtype, qbase + c) * widen(k, dtype, kbase + c);
+    x[a] = scale * s;
+    if (x[a] > m) m = x[a];
+  }
+  double l = 0.0;
+  for (int64_t a = 0; a < n; ++a) {
+    x[a] = exp(x[a] - m);
+    l += x[a];
+  }
+  for (int64_t c = 0; c < D; ++c) o[c] = 0.0;
+  for (int64_t a = 0; a < n; ++a) {
+    const int64_t vbase = ((b * p->n_k + tok[a]) * Hkv + g) * D;
+    for (int64_t c = 0; c < D; ++c) o[c] += x[a] * widen(v, dtype, vbase + c);
+  }
+  for (int64_t c = 0; c < D; ++c) o[c] /= l;
+  for (int64_t a = 0; a < n; ++a) x[a] /= l;
+  return m + log(l);
+}
+
 int mo_attend(const mo_problem* p, const void* q, const void* k, const void* v, int dtype,
               const int32_t* ids, const int64_t* rows, int64_t n_rows, double* out, double* lse) {
   int rc = check_problem(p, dtype);
   if (rc) return rc;
   if ((rc = check_rows(p, rows, n_rows))) return rc;
   if (!q || !k || !v || !ids || !out) return -1;
-  const int64_t Hq = p->h_q, Hkv = p->h_kv, G = Hq / Hkv, D = p->d, K = p->topk, Bk = p->block_size;
+  const int64_t Hq = p->h_q, Hkv = p->h_kv, D = p->d, K = p->topk, Bk = p->block_size;
   const int64_t nblk = num_blocks(p);
-  const double scale = p->softmax_scale > 0 ? p->softmax_scale : 1.0 / sqrt((double)D);
 
 #pragma omp parallel
   {
@@ -220,44 +273,74 @@ int mo_attend(const mo_problem* p, const void* q, const void* k, const void* v, 
     int64_t* tok = (int64_t*)malloc(sizeof(int64_t) * (size_t)cap);
 #pragma omp for schedule(dynamic, 4)
     for (int64_t rh = 0; rh < n_rows * Hq; ++rh) {
-      const int64_t r = rh / Hq, h = rh % Hq, g = h / G;
+      const int64_t r = rh / Hq, h = rh % Hq, g = group_of(p, h);
       int64_t b, i;
       row_of(p, rows, r, &b, &i);
       const int64_t pos = p->q_offset + i;
       const int32_t* sel = ids + (r * Hkv + g) * K;
-      /* T: visible tokens of the selected blocks. */
-      int64_t n = 0;
-      for (int64_t s = 0; s < K; ++s) {
-        const int64_t j = sel[s];
-        if (j < 0 || j >= nblk) continue;
-        for (int64_t t = j * Bk; t < (j + 1) * Bk; ++t)
-          if (t <= pos && t < p->n_k) tok[n++] = t;
-      }
-      const int64_t qbase = ((b * p->n_q + i) * Hq + h) * D;
-      double m = -INFINITY;
-      for (int64_t a = 0; a < n; ++a) {
-        const int64_t kbase = ((b * p->n_k + tok[a]) * Hkv + g) * D;
-        double s = 0.0;
-        for (int64_t c = 0; c < D; ++c) s += widen(q, dtype, qbase + c) * widen(k, dtype, kbase + c);
-        x[a] = scale * s;
-        if (x[a] > m) m = x[a];
-      }
-      double l = 0.0;
-      for (int64_t a = 0; a < n; ++a) {
-        x[a] = exp(x[a] - m);
-        l += x[a];
-      }
-      double* o = out + rh * D;
-      for (int64_t c = 0; c < D; ++c) o[c] = 0.0;
-      for (int64_t a = 0; a < n; ++a) {
-        const int64_t vbase = ((b * p->n_k + tok[a]) * Hkv + g) * D;
-        for (int64_t c = 0; c < D; ++c) o[c] += x[a] * widen(v, dtype, vbase + c);
-      }
-      for (int64_t c = 0; c < D; ++c) o[c] /= l;
-      if (lse) lse[rh] = m + log(l);
+      const int64_t n = visible_tokens(p, sel, pos, tok);
+      const double row_lse = attend_row(p, q, k, v, dtype, b, i, h, tok, n, x, out + rh * D);
+      if (lse) lse[rh] = row_lse;
     }
     free(x);
     free(tok);
+  }
+  return 0;
+}
+
+/* Chain rule through the softmax attention of mo_attend, written out per
+ * (b, i, h).  Each OpenMP thread owns whole (b, g) groups, so the dk / dv sums
+ * over queries are formed by one thread in query order. */
+int mo_attend_backward(const mo_problem* p, const void* q, const void* k, const void* v, const void* dout,
+                       int dtype, const int32_t* ids, double* dq, double* dk, double* dv) {
+  int rc = check_problem(p, dtype);
+  if (rc) return rc;
+  if (!q || !k || !v || !dout || !ids || !dq || !dk || !dv) return -1;
+  const int64_t Hq = p->h_q, Hkv = p->h_kv, G = Hq / Hkv, D = p->d, K = p->topk, Bk = p->block_size;
+  const int64_t nblk = num_blocks(p);
+  const double scale = softmax_scale(p);
+  memset(dk, 0, sizeof(double) * (size_t)(p->batch * p->n_k * Hkv * D));
+  memset(dv, 0, sizeof(double) * (size_t)(p->batch * p->n_k * Hkv * D));
+
+#pragma omp parallel
+  {
+    const int64_t cap = (K < nblk ? K : nblk) * Bk;
+    double* x = (double*)malloc(sizeof(double) * (size_t)cap);
+    int64_t* tok = (int64_t*)malloc(sizeof(int64_t) * (size_t)cap);
+    double* o = (double*)malloc(sizeof(double) * (size_t)D);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t bg = 0; bg < p->batch * Hkv; ++bg) {
+      const int64_t b = bg / Hkv, g = bg % Hkv;
+      for (int64_t i = 0; i < p->n_q; ++i) {
+        const int64_t pos = p->q_offset + i;
+        const int32_t* sel = ids + ((b * p->n_q + i) * Hkv + g) * K;
+        const int64_t n = visible_tokens(p, sel, pos, tok);
+        for (int64_t h = g * G; h < (g + 1) * G; ++h) {
+          const int64_t qbase = ((b * p->n_q + i) * Hq + h) * D;
+          double* dqr = dq + qbase;
+          for (int64_t c = 0; c < D; ++c) dqr[c] = 0.0;
+          if (n == 0) continue;
+          attend_row(p, q, k, v, dtype, b, i, h, tok, n, x, o); /* x = P, o = O */
+          double dot_do_o = 0.0;
+          for (int64_t c = 0; c < D; ++c) dot_do_o += widen(dout, dtype, qbase + c) * o[c];
+          /* backward */
+          for (int64_t a = 0; a < n; ++a) {
+            const int64_t kvbase = ((b * p->n_k + tok[a]) * Hkv + g) * D;
+            double dp = 0.0;
+            for (int64_t c = 0; c < D; ++c) dp += widen(dout, dtype, qbase + c) * widen(v, dtype, kvbase + c);
+            const double ds = x[a] * (dp - dot_do_o);
+            for (int64_t c = 0; c < D; ++c) {
+              dqr[c] += scale * ds * widen(k, dtype, kvbase + c);
+              dk[kvbase + c] += scale * ds * widen(q, dtype, qbase + c);
+              dv[kvbase + c] += x[a] * widen(dout, dtype, qbase + c);
+            }
+          }
+        }
+      }
+    }
+    free(x);
+    free(tok);
+    free(o);
   }
   return 0;
 }

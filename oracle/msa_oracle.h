@@ -67,6 +67,19 @@ int mo_select(const mo_problem* p, const double* scores, const int64_t* rows, in
 int mo_attend(const mo_problem* p, const void* q, const void* k, const void* v, int dtype,
               const int32_t* ids, const int64_t* rows, int64_t n_rows, double* out, double* lse);
 
+/* Gradients of the attention step for a fixed selection: given the upstream
+ * gradient dout = dL/dO (same layout and dtype as q), returns dq = dL/dq,
+ * dk = dL/dk, dv = dL/dv of L through O of mo_attend (the selection itself is
+ * not differentiable; the pages train the index branch separately).  For each
+ * (b, i, h) over its visible selected tokens T:
+ *   P = softmax(x), x_t = scale <q, k_t>;  O = sum_t P_t v_t;
+ *   dP_t = <dout, v_t>;  dS_t = P_t (dP_t - <dout, O>);
+ *   dq += scale sum_t dS_t k_t;  dk_t += scale dS_t q;  dv_t += P_t dout.
+ * Covers every query (ids [B, Nq, h_kv, topk]); dq [B, Nq, h_q, d],
+ * dk, dv [B, Nk, h_kv, d], all fp64 (tokens no query attends get zeros). */
+int mo_attend_backward(const mo_problem* p, const void* q, const void* k, const void* v, const void* dout,
+                       int dtype, const int32_t* ids, double* dq, double* dk, double* dv);
+
 /* Block -> query lists (the bookkeeping a KV-outer schedule needs; the paper
  * summary's "Key Contributions" name KV-outer attention): for each (b, g),
  * offsets[(b*h_kv+g)*(nblk+1) + j] = number of (i, slot) pairs with

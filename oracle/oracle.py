@@ -74,6 +74,25 @@ class Oracle:
             raise ValueError(f"mo_attend: invalid argument ({rc})")
         return out, lse
 
+    def attend_backward(self, prob, q, k, v, dout, ids):
+        """fp64 (dq [B, Nq, h_q, d], dk [B, Nk, h_kv, d], dv [B, Nk, h_kv, d]) of the
+        attention step for upstream gradient dout and the fixed selection ids."""
+        q, d1 = _host(q)
+        k, d2 = _host(k)
+        v, d3 = _host(v)
+        dout, d4 = _host(dout)
+        assert d1 == d2 == d3 == d4
+        ids = np.ascontiguousarray(np.asarray(ids, dtype=np.int32))
+        assert ids.size == prob.batch * prob.n_q * prob.h_kv * prob.topk
+        dq = np.empty((prob.batch, prob.n_q, prob.h_q, prob.d), dtype=np.float64)
+        dk = np.empty((prob.batch, prob.n_k, prob.h_kv, prob.d), dtype=np.float64)
+        dv = np.empty_like(dk)
+        rc = self.L.mo_attend_backward(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), d1, _ptr(ids),
+                                       _ptr(dq), _ptr(dk), _ptr(dv))
+        if rc:
+            raise ValueError(f"mo_attend_backward: invalid argument ({rc})")
+        return dq, dk, dv
+
     def forward(self, prob, q, k, v, iq, ik, rows=None):
         """Select then attend; returns (ids, out, lse, scores)."""
         s = self.block_scores(prob, iq, ik, rows)
@@ -150,6 +169,10 @@ def num_threads():
     return default().num_threads()
 
 
+def attend_backward(prob, q, k, v, dout, ids):
+    return default().attend_backward(prob, q, k, v, dout, ids)
+
+
 def mx_quantize(x):
     return default().mx_quantize(x)
 
@@ -166,7 +189,8 @@ def load(path):
     L.mo_select.argtypes = [P, vp, vp, ctypes.c_int64, vp]
     L.mo_attend.argtypes = [P, vp, vp, vp, ctypes.c_int, vp, vp, ctypes.c_int64, vp, vp]
     L.mo_invert.argtypes = [P, vp, vp, vp]
-    for f in (L.mo_block_scores, L.mo_select, L.mo_attend, L.mo_invert):
+    L.mo_attend_backward.argtypes = [P, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp, vp]
+    for f in (L.mo_block_scores, L.mo_select, L.mo_attend, L.mo_invert, L.mo_attend_backward):
         f.restype = ctypes.c_int
     L.mo_num_threads.restype = ctypes.c_int
     L.mo_e4m3_value.argtypes = [ctypes.c_uint8]

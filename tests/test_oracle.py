@@ -297,6 +297,77 @@ def pin_causal_diagonal(orc):
         assert lse[0, 0] == 800.0
 
 
+# ---- Backward of the attention step (chain rule through the softmax): checked
+# against torch autograd of the masked-SDPA special case and against central
+# finite differences of the oracle's own forward.
+
+def _selection_mask(prob, ids):
+    B, N, Hkv, K, Bk = prob.batch, prob.n_q, prob.h_kv, prob.topk, prob.block_size
+    allowed = np.zeros((B, N, Hkv, prob.n_k), dtype=bool)
+    idr = ids.reshape(B, N, Hkv, K)
+    for b in range(B):
+        for i in range(N):
+            for g in range(Hkv):
+                for j in idr[b, i, g]:
+                    if j >= 0:
+                        allowed[b, i, g, j * Bk:(j + 1) * Bk] = True
+    return allowed & _causal_allowed(prob)
+
+
+def pin_backward_equals_autograd(orc):
+    """dq, dk, dv of L = sum(O * dout) equal torch autograd through fp64 SDPA
+    with the selection as a boolean mask (GQA heads share k, v)."""
+    rng = np.random.default_rng(23)
+    B, N, Hq, Hkv, d, di, Bk, K = 2, 36, 4, 2, 8, 4, 4, 3
+    prob = O.make_problem(B, N, N, Hq, Hkv, d, di, Bk, K, q_offset=0)
+    x = _inputs(rng, B, N, N, Hq, Hkv, d, di)
+    x["q"] *= 2.0  # sharper softmax
+    dout = rng.standard_normal((B, N, Hq, d))
+    ids, _, _, _ = orc.forward(prob, x["q"], x["k"], x["v"], x["iq"], x["ik"])
+    dq, dk, dv = orc.attend_backward(prob, x["q"], x["k"], x["v"], dout, ids)
+    allowed = _selection_mask(prob, ids)
+    G = Hq // Hkv
+    qt = torch.tensor(x["q"], requires_grad=True)
+    kt = torch.tensor(x["k"], requires_grad=True)
+    vt = torch.tensor(x["v"], requires_grad=True)
+    qh = qt.permute(0, 2, 1, 3)
+    kh = kt.permute(0, 2, 1, 3).repeat_interleave(G, dim=1)
+    vh = vt.permute(0, 2, 1, 3).repeat_interleave(G, dim=1)
+    m = torch.from_numpy(allowed).permute(0, 2, 1, 3).repeat_interleave(G, dim=1)
+    o = torch.nn.functional.scaled_dot_product_attention(qh, kh, vh, attn_mask=m, scale=1.0 / math.sqrt(d))
+    (o.permute(0, 2, 1, 3) * torch.from_numpy(dout)).sum().backward()
+    np.testing.assert_allclose(dq, qt.grad.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dk, kt.grad.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dv, vt.grad.numpy(), rtol=0, atol=1e-12)
+    assert np.abs(dk).max() > 1e-3 and np.abs(dq).max() > 1e-3  # not trivially zero
+
+
+def pin_backward_finite_differences(orc):
+    """Central differences of L = sum(O * dout) through the oracle's forward
+    (mo_attend) match the analytic gradients, including with q_offset > 0."""
+    rng = np.random.default_rng(29)
+    B, Nq, Nk, Hq, Hkv, d, di, Bk, K = 1, 6, 14, 2, 1, 4, 4, 4, 2
+    prob = O.make_problem(B, Nq, Nk, Hq, Hkv, d, di, Bk, K, q_offset=Nk - Nq)
+    x = _inputs(rng, B, Nq, Nk, Hq, Hkv, d, di)
+    dout = rng.standard_normal((B, Nq, Hq, d))
+    ids, _, _, _ = orc.forward(prob, x["q"], x["k"], x["v"], x["iq"], x["ik"])
+    dq, dk, dv = orc.attend_backward(prob, x["q"], x["k"], x["v"], dout, ids)
+
+    def loss(q, k, v):
+        o, _ = orc.attend(prob, q, k, v, ids)
+        return float((o.reshape(dout.shape) * dout).sum())
+
+    eps = 1e-6
+    for name, grad in (("q", dq), ("k", dk), ("v", dv)):
+        for idx in [tuple(rng.integers(0, n) for n in grad.shape) for _ in range(12)]:
+            xp = {k_: v_.copy() for k_, v_ in x.items()}
+            xm = {k_: v_.copy() for k_, v_ in x.items()}
+            xp[name][idx] += eps
+            xm[name][idx] -= eps
+            fd = (loss(xp["q"], xp["k"], xp["v"]) - loss(xm["q"], xm["k"], xm["v"])) / (2 * eps)
+            assert abs(fd - grad[idx]) < 1e-7, (name, idx, fd, grad[idx])
+
+
 # ---- MXFP8 index-key caches (OCP Microscaling Formats v1.0; OCP 8-bit floating
 # point E4M3).  torch's float8_e4m3fn is an independent implementation of the
 # element format; the shared-exponent rule and the saturation are the MX
@@ -383,7 +454,8 @@ def pin_mx_roundtrip(orc):
 PINS = [pin_golden_worked_example, pin_maxpool_closed_form, pin_scores_ignore_future_and_token_order,
         pin_topk_bruteforce, pin_topk_special_cases, pin_exp_free, pin_dense_equals_sdpa,
         pin_sparse_equals_masked_sdpa, pin_value_invariants, pin_causal_diagonal,
-        pin_e4m3_decode_table, pin_e4m3_encode_rne, pin_mx_shared_exponent, pin_mx_roundtrip]
+        pin_e4m3_decode_table, pin_e4m3_encode_rne, pin_mx_shared_exponent, pin_mx_roundtrip,
+        pin_backward_equals_autograd, pin_backward_finite_differences]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -460,7 +532,7 @@ MUTANTS = {
     "sum_pooling": ("if (s > best) best = s;", "best = (best == -INFINITY ? 0.0 : best) + s;"),
     "min_pooling": ("if (s > best) best = s;", "if (s < best || best == -INFINITY) best = s;"),
     "scale_one_over_d": ("1.0 / sqrt((double)D)", "1.0 / (double)D"),
-    "strided_group_map": ("g = h / G;", "g = h % Hkv;"),
+    "strided_group_map": ("return h / (p->h_q / p->h_kv);", "return h % p->h_kv;"),
     "k_excludes_local": ("for (int64_t m = 0; m < K - 1; ++m) chosen[n++] = cand[m].j;",
                          "for (int64_t m = 0; m < K && m < L; ++m) chosen[n++] = cand[m].j;"),
     "values_from_keys": ("o[c] += x[a] * widen(v, dtype, vbase + c);", "o[c] += x[a] * widen(k, dtype, vbase + c);"),
@@ -468,6 +540,13 @@ MUTANTS = {
     # catch: candidate blocks lie wholly before the query, so it never fires.)
     "scores_include_local_block": ("for (int64_t j = 0; j < L; ++j) {\n      double best",
                                    "for (int64_t j = 0; j <= L && j < nblk; ++j) {\n      double best"),
+    "bwd_drops_rowsum": ("const double ds = x[a] * (dp - dot_do_o);", "const double ds = x[a] * dp;"),
+    "bwd_dk_unscaled": ("dk[kvbase + c] += scale * ds * widen(q, dtype, qbase + c);",
+                        "dk[kvbase + c] += ds * widen(q, dtype, qbase + c);"),
+    "bwd_dv_from_scores": ("dv[kvbase + c] += x[a] * widen(dout, dtype, qbase + c);",
+                           "dv[kvbase + c] += ds * widen(dout, dtype, qbase + c);"),
+    "bwd_dq_from_values": ("dqr[c] += scale * ds * widen(k, dtype, kvbase + c);",
+                           "dqr[c] += scale * ds * widen(v, dtype, kvbase + c);"),
     "mx_truncates": ("double q = nearbyint(ldexp(a, 3 - e));", "double q = floor(ldexp(a, 3 - e));"),
     "mx_ties_away": ("const double m = nearbyint(ldexp(a, 9));", "const double m = round(ldexp(a, 9));"),
     "mx_emax_7": ("e = (ex - 1) - 8;", "e = (ex - 1) - 7;"),
