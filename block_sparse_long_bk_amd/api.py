@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_PKG, "libmsa.so")
 MSA_OK, MSA_ERR_INVALID_ARG, MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE, MSA_ERR_HIP = 0, -1, -2, -3, -4
 F32, BF16 = 0, 1
 SCHED_AUTO, SCHED_KV_OUTER, SCHED_Q_OUTER = 0, 1, 2
-OP_INDEX_TOPK, OP_ATTENTION, OP_FORWARD, OP_INVERT = 0, 1, 2, 3
+OP_INDEX_TOPK, OP_ATTENTION, OP_FORWARD, OP_INVERT, OP_BACKWARD = 0, 1, 2, 3, 4
 IDX_PLAIN, IDX_MXFP8 = 0, 1
 _IDXF = {"plain": IDX_PLAIN, "mxfp8": IDX_MXFP8}
 _SCHED = {"auto": SCHED_AUTO, "kv_outer": SCHED_KV_OUTER, "q_outer": SCHED_Q_OUTER}
@@ -46,7 +46,8 @@ _L = None
 
 EXPORTS = ["msa_status_string", "msa_last_hip_error", "msa_validate", "msa_workspace_size", "msa_block_scores",
            "msa_topk_from_scores", "msa_index_topk", "msa_invert", "msa_sparse_attention", "msa_forward",
-           "msa_mxfp8_quantize", "msa_profile_enable", "msa_profile_reset", "msa_profile_count", "msa_profile_read"]
+           "msa_sparse_attention_backward", "msa_mxfp8_quantize", "msa_profile_enable", "msa_profile_reset",
+           "msa_profile_count", "msa_profile_read"]
 
 
 def _lib():
@@ -69,6 +70,7 @@ def _lib():
         L.msa_invert.argtypes = [P, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.msa_sparse_attention.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.msa_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.msa_sparse_attention_backward.argtypes = [P] + [vp] * 10 + [vp, ctypes.c_size_t, vp]
         L.msa_mxfp8_quantize.argtypes = [vp, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, vp, vp, vp]
         L.msa_profile_enable.argtypes = [ctypes.c_int]
         L.msa_profile_count.restype = ctypes.c_int
@@ -239,6 +241,32 @@ def sparse_attention(p, q, k, v, ids, out=None, lse=None, want_lse=True, ws=None
     _check(_lib().msa_sparse_attention(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(ids), _ptr(out), _ptr(lse),
                                        wp, wn, _stream()), "msa_sparse_attention")
     return out, lse
+
+
+def sparse_attention_backward(p, q, k, v, out, lse, dout, ids, dq=None, dk=None, dv=None, ws=None):
+    """Gradients (dq, dk, dv) of the Main Branch for the fixed selection ids,
+    given the forward's out and lse and the upstream gradient dout."""
+    dt = _tdtype(p)
+    _expect(q, (p.batch, p.n_q, p.h_q, p.d), dt, "q")
+    _expect(k, (p.batch, p.n_k, p.h_kv, p.d), dt, "k")
+    _expect(v, (p.batch, p.n_k, p.h_kv, p.d), dt, "v")
+    _expect(out, (p.batch, p.n_q, p.h_q, p.d), dt, "out")
+    _expect(dout, (p.batch, p.n_q, p.h_q, p.d), dt, "dout")
+    _expect(lse, (p.batch, p.n_q, p.h_q), torch.float32, "lse")
+    _expect(ids, (p.batch, p.n_q, p.h_kv, p.topk), torch.int32, "block_ids")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _expect(dq, tuple(q.shape), dt, "dq")
+    _expect(dk, tuple(k.shape), dt, "dk")
+    _expect(dv, tuple(v.shape), dt, "dv")
+    if ws is None:
+        ws = alloc_workspace(p, OP_BACKWARD, q.device)
+    wp, wn = _ws(ws)
+    _check(_lib().msa_sparse_attention_backward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                                _ptr(dout), _ptr(ids), _ptr(dq), _ptr(dk), _ptr(dv), wp, wn,
+                                                _stream()), "msa_sparse_attention_backward")
+    return dq, dk, dv
 
 
 def forward(p, q, k, v, iq, ik, ids=None, out=None, lse=None, want_lse=True, ws=None):

@@ -1,0 +1,183 @@
+// attn_common.h -- device helpers shared by the Main Branch kernels (forward
+// attention in attention.hip, gradients in backward.hip): LDS staging of one
+// key block (rows and transposed rows), MFMA fragment reads of the transposed
+// block, the gathered query rows of a KV-outer work item, partial stores.
+#pragma once
+
+#include "msa_device.h"
+#include "msa_internal.h"
+
+namespace msa {
+namespace {
+
+template <typename T> struct Pack4;
+template <> struct Pack4<bf16_t> { using type = bf16x4; };
+template <> struct Pack4<float> { using type = f32x4; };
+
+// LDS geometry of one staged key block of BK tokens: K row-major [BK][D], V
+// transposed [D][BK].  Pitches are padded so the 32 rows read by a half-wave
+// fall on distinct banks.
+template <typename T, int D, int BK>
+struct KvLds {
+  static constexpr int KPITCH = D * (int)sizeof(T) + 16;
+  static constexpr int VPITCH = BK * (int)sizeof(T) + (sizeof(T) == 2 ? 8 : 16);
+  static constexpr int KBYTES = BK * KPITCH;
+  static constexpr int BYTES = KBYTES + D * VPITCH;
+  // Byte offset of keys [4c, 4c+4) in V^T row d.  For 16-bit types the
+  // 4-key chunks are XOR-swizzled by (d / 32) % 4: the staging stores write
+  // rows 8 apart from neighbouring lanes, which would otherwise share banks;
+  // the MFMA fragment reads take 32 consecutive rows, which share the swizzle.
+  __device__ static __forceinline__ int vt_off(int d, int c) {
+    if constexpr (sizeof(T) == 2) return d * VPITCH + ((c ^ ((d >> 5) & 3)) * 4 * (int)sizeof(T));
+    else return d * VPITCH + c * 4 * (int)sizeof(T);
+  }
+};
+
+// Staging of K_j and V_j^T of one (b, g) into LDS by 256 threads, split into
+// a global-load phase (into registers) and an LDS-store phase so that callers
+// can overlap other loads with it.  Rows past n_k are zero-filled (they are
+// masked anyway).
+template <typename T, int D, int BK>
+struct KvStage {
+  using L = KvLds<T, D, BK>;
+  static constexpr int CPR = D * (int)sizeof(T) / 16;  // 16-byte chunks per K row
+  static constexpr int KCH = BK * CPR;
+  static constexpr int KLD = (KCH + 255) / 256;
+  static constexpr int DCH = D / 8;         // 8-element chunks per V row
+  static constexpr int KG = 256 / DCH;      // groups of 4 keys per pass
+  static constexpr int PASSES = (BK + 4 * KG - 1) / (4 * KG);  // the last pass may be partial
+  u32x4 kr[KLD];
+  frag_t<T> vr[PASSES][4];
+
+  __device__ __forceinline__ void load(const T* kbase, const T* vbase, int64_t tok_stride, int j, int n_k, int tid) {
+#pragma unroll
+    for (int u = 0; u < KLD; ++u) {
+      const int c = tid + u * 256;
+      const int row = c / CPR, col = c % CPR;
+      const int64_t t = (int64_t)j * BK + row;
+      kr[u] = u32x4{};
+      if (c < KCH && t < n_k)
+        kr[u] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(kbase + t * tok_stride) + col * 16);
+    }
+    const int dch = tid % DCH, kg = tid / DCH;
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = (ps * KG + kg) * 4 + r;
+        const int64_t t = (int64_t)j * BK + key;
+        vr[ps][r] = key < BK && t < n_k ? load8(vbase + t * tok_stride + dch * 8) : zero_frag<T>();
+      }
+  }
+
+  // V^T rows get four consecutive keys per store.
+  __device__ __forceinline__ void store(char* lds, int tid) const {
+#pragma unroll
+    for (int u = 0; u < KLD; ++u) {
+      const int c = tid + u * 256;
+      if (c < KCH) *reinterpret_cast<u32x4*>(lds + (c / CPR) * L::KPITCH + (c % CPR) * 16) = kr[u];
+    }
+    char* vt = lds + L::KBYTES;
+    const int dch = tid % DCH, kg = tid / DCH;
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps) {
+      const int key0 = (ps * KG + kg) * 4;
+      if (key0 >= BK) continue;  // a partial last pass (blocks smaller than 4 * KG keys)
+      if constexpr (sizeof(T) == 2) {
+        // 2x2 transposes of 16-bit halves with byte permutes (v_perm_b32).
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          uint32_t x0 = __builtin_bit_cast(u32x4, vr[ps][0])[w], x1 = __builtin_bit_cast(u32x4, vr[ps][1])[w];
+          uint32_t x2 = __builtin_bit_cast(u32x4, vr[ps][2])[w], x3 = __builtin_bit_cast(u32x4, vr[ps][3])[w];
+          const uint2 lo = make_uint2(__builtin_amdgcn_perm(x1, x0, 0x05040100u), __builtin_amdgcn_perm(x3, x2, 0x05040100u));
+          const uint2 hi = make_uint2(__builtin_amdgcn_perm(x1, x0, 0x07060302u), __builtin_amdgcn_perm(x3, x2, 0x07060302u));
+          *reinterpret_cast<uint2*>(vt + L::vt_off(dch * 8 + 2 * w, key0 / 4)) = lo;
+          *reinterpret_cast<uint2*>(vt + L::vt_off(dch * 8 + 2 * w + 1, key0 / 4)) = hi;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          typename Pack4<T>::type w;
+          w[0] = vr[ps][0][e];
+          w[1] = vr[ps][1][e];
+          w[2] = vr[ps][2][e];
+          w[3] = vr[ps][3][e];
+          *reinterpret_cast<typename Pack4<T>::type*>(vt + L::vt_off(dch * 8 + e, key0 / 4)) = w;
+        }
+      }
+    }
+  }
+};
+
+template <typename T, int D, int BK>
+__device__ __forceinline__ void stage_kv(char* lds, const T* kbase, const T* vbase, int64_t tok_stride, int j,
+                                         int n_k, int tid) {
+  KvStage<T, D, BK> st;
+  st.load(kbase, vbase, tok_stride, j, n_k, tid);
+  st.store(lds, tid);
+}
+
+// A fragment of V^T for k-step (mt, a): row d, keys 32mt+16a+4h+[0..3] and +8.
+template <typename T, int D, int BK>
+__device__ __forceinline__ frag_t<T> vt_frag(const char* lds, int d, int mt, int a, int half) {
+  using L = KvLds<T, D, BK>;
+  const char* vt = lds + L::KBYTES;
+  const int c0 = 8 * mt + 4 * a + half;  // chunk of keys 32mt+16a+4h .. +3
+  const typename Pack4<T>::type lo = *reinterpret_cast<const typename Pack4<T>::type*>(vt + L::vt_off(d, c0));
+  const typename Pack4<T>::type hi = *reinterpret_cast<const typename Pack4<T>::type*>(vt + L::vt_off(d, c0 + 2));
+  frag_t<T> f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f[e] = lo[e];
+    f[4 + e] = hi[e];
+  }
+  return f;
+}
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) { return static_cast<bf16_t>(x); }
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+
+// Query rows of one 32-row tile of a KV-outer work item.
+struct TileRows {
+  bool valid;
+  int qq, slot, h;
+};
+// e = qq*topk + slot is split with a multiply by ceil(2^40/topk): exact for
+// 0 <= e < 2^31 and topk <= 32 (the rounding error stays below 2^-9 < 1/topk).
+__device__ __forceinline__ TileRows rows_of(int e, bool valid, int r, int gshift, int topk, uint64_t topk_magic,
+                                           int g) {
+  TileRows t;
+  t.valid = valid;
+  t.qq = (int)(((uint64_t)(uint32_t)e * topk_magic) >> 40);
+  t.slot = e - t.qq * topk;
+  t.h = (g << gshift) + (r & ((1 << gshift) - 1));
+  return t;
+}
+// A work item holds at most min(kItemRows / G, kItemEntries) entries.
+constexpr int kMaxItemEntries = kItemEntries;
+// Rows past the item's end read a valid row (entry 0 of the chunk): their
+// results are never stored, so no branch is needed around the loads.
+template <typename T, int D>
+__device__ __forceinline__ void load_q_rows(frag_t<T> (&qf)[D / 16], const T* qbase, const TileRows& t, int b, int Nq,
+                                            int Hq, int q0, int half) {
+  const T* qrow = qbase + (((int64_t)b * Nq + q0 + t.qq) * Hq + t.h) * D + 8 * half;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) qf[ks] = load8(qrow + 16 * ks);
+}
+// Partial store.  A partial is written once and read back only by the
+// combine.  With NT the store is marked non-temporal, which keeps partials
+// from displacing the query rows that other blocks of the same queries re-read
+// from the caches: measured faster where work items are full (many rows per
+// staged block), slower where most items are small and the staging of K/V
+// dominates, so the launcher chooses.  Every partial store writes whole rows
+// or whole runs of lse values (partial-line non-temporal writes measured
+// several times slower than plain ones).
+template <bool NT, typename V>
+__device__ __forceinline__ void store_partial(V* p, const V& v) {
+  if constexpr (NT) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+
+}  // namespace
+}  // namespace msa

@@ -132,6 +132,39 @@ KvLayout kv_layout(const msa::Shape& s, int nc) {
   return L;
 }
 
+// Backward workspace: D rows, the inversion of the whole problem, dq partials,
+// per-item dk/dv partials and a scratch line.
+struct BwdLayout {
+  size_t drow, offsets, entries, item_count, items, inv_scratch, dq_part, dkv_part, trash, total;
+};
+
+BwdLayout bwd_layout(const msa::Shape& s) {
+  const msa::InvertPlan p = msa::invert_plan(s, s.Nq);
+  const size_t BG = (size_t)s.B * s.Hkv, rows = (size_t)s.B * s.Nq * s.Hq;
+  BwdLayout L;
+  size_t off = 0;
+  L.drow = off;
+  off += align_up(rows * 4);
+  L.offsets = off;
+  off += align_up(BG * (s.nblk + 1) * 4);
+  L.entries = off;
+  off += align_up(BG * (size_t)s.Nq * s.topk * 4);
+  L.item_count = off;
+  off += align_up(BG * 4);
+  L.items = off;
+  off += align_up(BG * (size_t)p.items_cap * 16);
+  L.inv_scratch = off;
+  off += align_up(msa::invert_ws_bytes(s, p));
+  L.dq_part = off;
+  off += align_up(rows * s.topk * s.D * 4);
+  L.dkv_part = off;
+  off += align_up(msa::bwd_dkv_bytes(s, p));
+  L.trash = off;
+  off += align_up(msa::kTrashBytes);
+  L.total = off;
+  return L;
+}
+
 size_t qo_bytes(const msa::Shape& s, int nc, int nsplit) {
   if (nsplit <= 1) return 0;
   return align_up((size_t)s.B * nc * s.Hq * nsplit * s.D * elem_bytes(s)) + align_up((size_t)s.B * nc * s.Hq * nsplit * 4);
@@ -321,11 +354,14 @@ msa_status_t msa_validate(const msa_problem_t* prob) { return validate(prob); }
 msa_status_t msa_workspace_size(const msa_problem_t* prob, int op, size_t* bytes, size_t* min_bytes) {
   msa_status_t rc = validate(prob);
   if (rc != MSA_OK) return rc;
-  if (!bytes || op < MSA_OP_INDEX_TOPK || op > MSA_OP_INVERT) return MSA_ERR_INVALID_ARG;
+  if (!bytes || op < MSA_OP_INDEX_TOPK || op > MSA_OP_BACKWARD) return MSA_ERR_INVALID_ARG;
   const msa::Shape s = shape_of(prob);
   size_t full = 0, least = 0;
   if (op == MSA_OP_INVERT) {
     full = least = msa::invert_ws_bytes(s, msa::invert_plan(s, s.Nq));
+  }
+  if (op == MSA_OP_BACKWARD) {
+    full = least = bwd_layout(s).total;
   }
   if (op == MSA_OP_INDEX_TOPK || op == MSA_OP_FORWARD) {
     full = std::max(full, index_bytes(s));
@@ -353,6 +389,36 @@ msa_status_t msa_block_scores(const msa_problem_t* prob, const void* idx_q, cons
     if (msa::index_use_tile(s)) e = msa::launch_index_tile(s, idx_q, idx_k, nullptr, scores, st);
     else e = msa::launch_index_scan(s, idx_q, idx_k, scores, st);
   }
+  return e == hipSuccess ? MSA_OK : hip_fail(e);
+}
+
+msa_status_t msa_sparse_attention_backward(const msa_problem_t* prob, const void* q, const void* k, const void* v,
+                                           const void* out, const float* lse, const void* dout,
+                                           const int32_t* block_ids, void* dq, void* dk, void* dv, void* ws,
+                                           size_t ws_bytes, void* stream) {
+  msa_status_t rc = validate(prob);
+  if (rc != MSA_OK) return rc;
+  const void* ptrs[] = {q, k, v, out, lse, dout, block_ids, dq, dk, dv, ws};
+  for (const void* x : ptrs)
+    if (!x || !aligned16(x)) return MSA_ERR_INVALID_ARG;
+  const msa::Shape s = shape_of(prob);
+  const BwdLayout L = bwd_layout(s);
+  if (ws_bytes < L.total) return MSA_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  float* drow = reinterpret_cast<float*>(w + L.drow);
+  const msa::InvertPlan plan = msa::invert_plan(s, s.Nq);
+  msa::InvertOut inv;
+  inv.offsets = reinterpret_cast<int32_t*>(w + L.offsets);
+  inv.entries = reinterpret_cast<int32_t*>(w + L.entries);
+  inv.item_count = reinterpret_cast<int32_t*>(w + L.item_count);
+  inv.items = reinterpret_cast<int4*>(w + L.items);
+  hipError_t e = msa::launch_bwd_rowdot(s, out, dout, drow, st);
+  if (e == hipSuccess) e = msa::launch_invert(s, plan, block_ids, 0, s.Nq, inv, w + L.inv_scratch, st);
+  if (e == hipSuccess)
+    e = msa::launch_bwd_attention(s, plan, q, k, v, dout, lse, drow, block_ids, inv,
+                                  reinterpret_cast<float*>(w + L.dq_part), reinterpret_cast<float*>(w + L.dkv_part),
+                                  w + L.trash, dq, dk, dv, st);
   return e == hipSuccess ? MSA_OK : hip_fail(e);
 }
 

@@ -26,7 +26,7 @@ import torch
 CHUNK = 65536
 
 # Tensor ids mixed into the per-chunk seeds.
-_T_Q, _T_K, _T_V, _T_IQ, _T_IK, _T_OFF, _T_HOT = 1, 2, 3, 4, 5, 6, 7
+_T_Q, _T_K, _T_V, _T_IQ, _T_IK, _T_OFF, _T_HOT, _T_DOUT = 1, 2, 3, 4, 5, 6, 7, 8
 
 
 @dataclass(frozen=True)
@@ -140,6 +140,10 @@ def generate(wl, device="cpu", tensors=("q", "k", "v", "iq", "ik")):
     if "v" in tensors:
         out["v"] = torch.empty((B, Nk, wl.h_kv, wl.d), dtype=dt, device=device)
         _fill_gaussian(out["v"], wl, _T_V, 1.0 / math.sqrt(wl.d), device)
+    if "dout" in tensors:
+        # upstream gradient of the attention output (for the backward pass)
+        out["dout"] = torch.empty((B, Nq, wl.h_q, wl.d), dtype=dt, device=device)
+        _fill_gaussian(out["dout"], wl, _T_DOUT, 1.0, device)
     hot = None
     if wl.hot_frac > 0 and ("iq" in tensors or "ik" in tensors):
         hot = hot_blocks(wl, device)

@@ -99,7 +99,13 @@ typedef struct {
   int32_t idx_format;    /* msa_idx_format_t */
 } msa_problem_t;
 
-typedef enum { MSA_OP_INDEX_TOPK = 0, MSA_OP_ATTENTION = 1, MSA_OP_FORWARD = 2, MSA_OP_INVERT = 3 } msa_op_t;
+typedef enum {
+  MSA_OP_INDEX_TOPK = 0,
+  MSA_OP_ATTENTION = 1,
+  MSA_OP_FORWARD = 2,
+  MSA_OP_INVERT = 3,
+  MSA_OP_BACKWARD = 4
+} msa_op_t;
 
 /* Human-readable name of a status code (static storage). */
 const char* msa_status_string(msa_status_t status);
@@ -156,6 +162,23 @@ msa_status_t msa_sparse_attention(const msa_problem_t* prob, const void* q, cons
 msa_status_t msa_forward(const msa_problem_t* prob, const void* q, const void* k, const void* v,
                          const void* idx_q, const void* idx_k, int32_t* block_ids, void* out, float* lse,
                          void* ws, size_t ws_bytes, void* stream);
+
+/* Gradients of the Main Branch for the fixed selection block_ids (the
+ * selection is not differentiable; the pages train the Index Branch by a
+ * separate loss -- paper summary page, "Method").  Given the forward's out and
+ * lse (as msa_sparse_attention / msa_forward wrote them for these inputs and
+ * ids) and the upstream gradient dout = dL/dout (layout and dtype of q), writes
+ *   dq [B, Nq, Hq, d], dk, dv [B, Nk, Hkv, d]    (dtype of the inputs)
+ * with, per (b, i, h) over its visible selected tokens: P = softmax of
+ * scale <q, k_t>, D = <dout, out>, dS_t = P_t (<dout, v_t> - D), dq = scale
+ * sum dS_t k_t, dk_t += scale dS_t q, dv_t += P_t dout.  Tokens no query
+ * attends get zero gradients.  Sums are formed in fixed orders (no atomics), so
+ * results are bitwise reproducible.  Needs the MSA_OP_BACKWARD workspace (the
+ * whole problem in one pass).  Errors as for msa_sparse_attention. */
+msa_status_t msa_sparse_attention_backward(const msa_problem_t* prob, const void* q, const void* k, const void* v,
+                                           const void* out, const float* lse, const void* dout,
+                                           const int32_t* block_ids, void* dq, void* dk, void* dv, void* ws,
+                                           size_t ws_bytes, void* stream);
 
 /* Quantise n_rows rows of row_len elements (row_len a multiple of 32) of src
  * (device, `src_dtype` MSA_F32 or MSA_BF16, row-major) to MXFP8 following the

@@ -91,6 +91,11 @@ def test_entry_points_reject_before_any_hip_call():
     big = good(dtype="bf16", n_q=32768, n_k=32768, h_q=64, h_kv=8, d=128, d_idx=128, topk=16, sched="kv_outer")
     assert L.msa_sparse_attention(ctypes.byref(big), x, x, x, x, x, null, x, 1024, null) == api.MSA_ERR_WORKSPACE
     assert L.msa_workspace_size(ctypes.byref(p), 9, ctypes.byref(ctypes.c_size_t()), None) == api.MSA_ERR_INVALID_ARG
+    # backward: a missing gradient output, then too little workspace
+    bw = L.msa_sparse_attention_backward
+    assert bw(ctypes.byref(p), x, x, x, x, x, x, x, null, x, x, x, 1 << 30, null) == api.MSA_ERR_INVALID_ARG
+    assert bw(ctypes.byref(p), x, x, x, x, x, x, x, x, x, x, x, 1024, null) == api.MSA_ERR_WORKSPACE
+    assert bw(ctypes.byref(bad), x, x, x, x, x, x, x, x, x, x, x, 1 << 30, null) == api.MSA_ERR_UNSUPPORTED
     # MXFP8 quantiser: sizes, dtype and pointers are checked before any launch
     q = L.msa_mxfp8_quantize
     assert q(x, api.BF16, 4, 48, x, x, null) == api.MSA_ERR_INVALID_ARG   # row length not a multiple of 32
@@ -121,3 +126,6 @@ def test_workspace_sizes():
     assert inv == inv_least > 0
     inv_pre, _ = api.workspace_size(pre, api.OP_INVERT)
     assert inv_pre >= 8 * 256 * 4  # at least one count per (group, block)
+    # backward: fp32 dq partials per (query, head, slot) dominate
+    bwd, bwd_least = api.workspace_size(pre, api.OP_BACKWARD)
+    assert bwd == bwd_least >= 32768 * 64 * 16 * 128 * 4
