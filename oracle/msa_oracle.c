@@ -289,13 +289,17 @@ int mo_attend(const mo_problem* p, const void* q, const void* k, const void* v, 
 }
 
 /* Chain rule through the softmax attention of mo_attend, written out per
- * (b, i, h).  Each OpenMP thread owns whole (b, g) groups, so the dk / dv sums
- * over queries are formed by one thread in query order. */
+ * (b, i, h).  Each OpenMP thread owns whole (b, g) groups and walks the listed
+ * rows in list order, so the dk / dv sums are formed by one thread in a fixed
+ * order. */
 int mo_attend_backward(const mo_problem* p, const void* q, const void* k, const void* v, const void* dout,
-                       int dtype, const int32_t* ids, double* dq, double* dk, double* dv) {
+                       int dtype, const int32_t* ids, const int64_t* rows, int64_t n_rows, double* dq, double* dk,
+                       double* dv) {
   int rc = check_problem(p, dtype);
   if (rc) return rc;
   if (!q || !k || !v || !dout || !ids || !dq || !dk || !dv) return -1;
+  rc = check_rows(p, rows, n_rows);
+  if (rc) return rc;
   const int64_t Hq = p->h_q, Hkv = p->h_kv, G = Hq / Hkv, D = p->d, K = p->topk, Bk = p->block_size;
   const int64_t nblk = num_blocks(p);
   const double scale = softmax_scale(p);
@@ -310,14 +314,17 @@ int mo_attend_backward(const mo_problem* p, const void* q, const void* k, const 
     double* o = (double*)malloc(sizeof(double) * (size_t)D);
 #pragma omp for schedule(dynamic, 1)
     for (int64_t bg = 0; bg < p->batch * Hkv; ++bg) {
-      const int64_t b = bg / Hkv, g = bg % Hkv;
-      for (int64_t i = 0; i < p->n_q; ++i) {
+      const int64_t g = bg % Hkv;
+      for (int64_t r = 0; r < n_rows; ++r) {
+        int64_t b, i;
+        row_of(p, rows, r, &b, &i);
+        if (b != bg / Hkv) continue;
         const int64_t pos = p->q_offset + i;
-        const int32_t* sel = ids + ((b * p->n_q + i) * Hkv + g) * K;
+        const int32_t* sel = ids + (r * Hkv + g) * K;
         const int64_t n = visible_tokens(p, sel, pos, tok);
         for (int64_t h = g * G; h < (g + 1) * G; ++h) {
           const int64_t qbase = ((b * p->n_q + i) * Hq + h) * D;
-          double* dqr = dq + qbase;
+          double* dqr = dq + (r * Hq + h) * D;
           for (int64_t c = 0; c < D; ++c) dqr[c] = 0.0;
           if (n == 0) continue;
           attend_row(p, q, k, v, dtype, b, i, h, tok, n, x, o); /* x = P, o = O */

@@ -75,10 +75,13 @@ int mo_attend(const mo_problem* p, const void* q, const void* k, const void* v, 
  *   P = softmax(x), x_t = scale <q, k_t>;  O = sum_t P_t v_t;
  *   dP_t = <dout, v_t>;  dS_t = P_t (dP_t - <dout, O>);
  *   dq += scale sum_t dS_t k_t;  dk_t += scale dS_t q;  dv_t += P_t dout.
- * Covers every query (ids [B, Nq, h_kv, topk]); dq [B, Nq, h_q, d],
- * dk, dv [B, Nk, h_kv, d], all fp64 (tokens no query attends get zeros). */
+ * Over the listed rows: ids [n_rows][h_kv][topk], dq [n_rows][h_q][d];
+ * dk, dv [B, Nk, h_kv, d] hold the contributions of those rows only (all
+ * rows: the full gradients; tokens no listed query attends get zeros).  All
+ * fp64. */
 int mo_attend_backward(const mo_problem* p, const void* q, const void* k, const void* v, const void* dout,
-                       int dtype, const int32_t* ids, double* dq, double* dk, double* dv);
+                       int dtype, const int32_t* ids, const int64_t* rows, int64_t n_rows, double* dq, double* dk,
+                       double* dv);
 
 /* Block -> query lists (the bookkeeping a KV-outer schedule needs; the paper
  * summary's "Key Contributions" name KV-outer attention): for each (b, g),

@@ -74,23 +74,27 @@ class Oracle:
             raise ValueError(f"mo_attend: invalid argument ({rc})")
         return out, lse
 
-    def attend_backward(self, prob, q, k, v, dout, ids):
-        """fp64 (dq [B, Nq, h_q, d], dk [B, Nk, h_kv, d], dv [B, Nk, h_kv, d]) of the
-        attention step for upstream gradient dout and the fixed selection ids."""
+    def attend_backward(self, prob, q, k, v, dout, ids, rows=None):
+        """fp64 (dq [n_rows, h_q, d], dk [B, Nk, h_kv, d], dv [B, Nk, h_kv, d]) of the
+        attention step for upstream gradient dout and the fixed selection ids
+        ([n_rows, h_kv, topk]); dk and dv sum the listed rows' contributions."""
         q, d1 = _host(q)
         k, d2 = _host(k)
         v, d3 = _host(v)
         dout, d4 = _host(dout)
         assert d1 == d2 == d3 == d4
+        r, n = _rows(prob, rows)
         ids = np.ascontiguousarray(np.asarray(ids, dtype=np.int32))
-        assert ids.size == prob.batch * prob.n_q * prob.h_kv * prob.topk
-        dq = np.empty((prob.batch, prob.n_q, prob.h_q, prob.d), dtype=np.float64)
+        assert ids.size == n * prob.h_kv * prob.topk
+        dq = np.empty((n, prob.h_q, prob.d), dtype=np.float64)
         dk = np.empty((prob.batch, prob.n_k, prob.h_kv, prob.d), dtype=np.float64)
         dv = np.empty_like(dk)
         rc = self.L.mo_attend_backward(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), d1, _ptr(ids),
-                                       _ptr(dq), _ptr(dk), _ptr(dv))
+                                       _ptr(r), n, _ptr(dq), _ptr(dk), _ptr(dv))
         if rc:
             raise ValueError(f"mo_attend_backward: invalid argument ({rc})")
+        if rows is None:
+            dq = dq.reshape(prob.batch, prob.n_q, prob.h_q, prob.d)
         return dq, dk, dv
 
     def forward(self, prob, q, k, v, iq, ik, rows=None):
@@ -169,8 +173,8 @@ def num_threads():
     return default().num_threads()
 
 
-def attend_backward(prob, q, k, v, dout, ids):
-    return default().attend_backward(prob, q, k, v, dout, ids)
+def attend_backward(prob, q, k, v, dout, ids, rows=None):
+    return default().attend_backward(prob, q, k, v, dout, ids, rows)
 
 
 def mx_quantize(x):
@@ -189,7 +193,7 @@ def load(path):
     L.mo_select.argtypes = [P, vp, vp, ctypes.c_int64, vp]
     L.mo_attend.argtypes = [P, vp, vp, vp, ctypes.c_int, vp, vp, ctypes.c_int64, vp, vp]
     L.mo_invert.argtypes = [P, vp, vp, vp]
-    L.mo_attend_backward.argtypes = [P, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp, vp]
+    L.mo_attend_backward.argtypes = [P, vp, vp, vp, vp, ctypes.c_int, vp, vp, ctypes.c_int64, vp, vp, vp]
     for f in (L.mo_block_scores, L.mo_select, L.mo_attend, L.mo_invert, L.mo_attend_backward):
         f.restype = ctypes.c_int
     L.mo_num_threads.restype = ctypes.c_int

@@ -478,6 +478,29 @@ def test_row_subsets_match_full():
     assert np.array_equal(s[flat], s2)
 
 
+def test_backward_row_subsets():
+    """The backward over a list of rows: dq equals the full run's rows, and
+    dk, dv equal the full gradients of the loss restricted to those rows
+    (dout zeroed elsewhere, so every other row contributes exact zeros)."""
+    rng = np.random.default_rng(31)
+    B, N, Hq, Hkv, d, di, Bk, K = 2, 24, 4, 2, 8, 4, 4, 3
+    prob = O.make_problem(B, N, N, Hq, Hkv, d, di, Bk, K)
+    x = _inputs(rng, B, N, N, Hq, Hkv, d, di)
+    dout = rng.standard_normal((B, N, Hq, d))
+    ids, _, _, _ = O.forward(prob, x["q"], x["k"], x["v"], x["iq"], x["ik"])
+    dq, dk, dv = O.attend_backward(prob, x["q"], x["k"], x["v"], dout, ids)
+    rows = [[0, 3], [0, 17], [1, 0], [1, 22]]  # ascending (b, i): the full run's order
+    flat = [b * N + i for b, i in rows]
+    dq2, dk2, dv2 = O.attend_backward(prob, x["q"], x["k"], x["v"], dout, ids[flat], rows=rows)
+    assert np.array_equal(dq.reshape(B * N, Hq, d)[flat], dq2)
+    masked = np.zeros_like(dout)
+    for b, i in rows:
+        masked[b, i] = dout[b, i]
+    _, dk3, dv3 = O.attend_backward(prob, x["q"], x["k"], x["v"], masked, ids)
+    assert np.array_equal(dk2, dk3) and np.array_equal(dv2, dv3)
+    assert np.abs(dk2).max() > 0 and not np.array_equal(dk2, dk)
+
+
 def test_bf16_and_f32_inputs_widen_exactly():
     rng = np.random.default_rng(29)
     B, N, Hq, Hkv, d, di, Bk, K = 1, 16, 2, 1, 8, 8, 4, 2
