@@ -352,6 +352,89 @@ int mo_attend_backward(const mo_problem* p, const void* q, const void* k, const 
   return 0;
 }
 
+/* Index-Branch alignment loss (paper summary page, "Method"; zhichai.net
+ * write-up, section 5.1): per (b, i, g) over the visible selected tokens T,
+ * the Main Branch's group-averaged distribution pm(t) = (1/G) sum_h P_h(t)
+ * (P_h the softmax of mo_attend, a fixed target) against the Index Branch's
+ * distribution pi(t) = softmax over T of the raw token scores s_t.
+ *   kl = sum_t pm(t) (log pm(t) - log pi(t))        (terms with pm = 0 vanish)
+ *   d kl / d s_t = pi(t) - pm(t)                    (sum_t pm = 1)
+ * and through s_t = <iq, ik_t> the gradients of loss_scale * sum kl. */
+int mo_indexer_kl(const mo_problem* p, const void* q, const void* k, const void* iq, const void* ik, int dtype,
+                  const int32_t* ids, const int64_t* rows, int64_t n_rows, double loss_scale, double* kl,
+                  double* d_iq, double* d_ik) {
+  int rc = check_problem(p, dtype);
+  if (rc) return rc;
+  if (!q || !k || !iq || !ik || !ids || !kl || !d_iq || !d_ik) return -1;
+  rc = check_rows(p, rows, n_rows);
+  if (rc) return rc;
+  const int64_t Hq = p->h_q, Hkv = p->h_kv, G = Hq / Hkv, D = p->d, DI = p->d_idx, K = p->topk;
+  const int64_t Bk = p->block_size, nblk = num_blocks(p);
+  memset(d_ik, 0, sizeof(double) * (size_t)(p->batch * p->n_k * Hkv * DI));
+
+#pragma omp parallel
+  {
+    const int64_t cap = (K < nblk ? K : nblk) * Bk;
+    double* x = (double*)malloc(sizeof(double) * (size_t)cap);
+    double* pm = (double*)malloc(sizeof(double) * (size_t)cap);
+    double* si = (double*)malloc(sizeof(double) * (size_t)cap);
+    int64_t* tok = (int64_t*)malloc(sizeof(int64_t) * (size_t)cap);
+    double* o = (double*)malloc(sizeof(double) * (size_t)D);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t bg = 0; bg < p->batch * Hkv; ++bg) {
+      const int64_t g = bg % Hkv;
+      for (int64_t r = 0; r < n_rows; ++r) {
+        int64_t b, i;
+        row_of(p, rows, r, &b, &i);
+        if (b != bg / Hkv) continue;
+        const int32_t* sel = ids + (r * Hkv + g) * K;
+        const int64_t n = visible_tokens(p, sel, p->q_offset + i, tok);
+        const int64_t qi = ((b * p->n_q + i) * Hkv + g) * DI;
+        double* dq = d_iq + (r * Hkv + g) * DI;
+        for (int64_t c = 0; c < DI; ++c) dq[c] = 0.0;
+        kl[r * Hkv + g] = 0.0;
+        if (n == 0) continue;
+        /* the Main Branch target: mean over the group's heads */
+        for (int64_t a = 0; a < n; ++a) pm[a] = 0.0;
+        for (int64_t h = g * G; h < (g + 1) * G; ++h) {
+          attend_row(p, q, k, k, dtype, b, i, h, tok, n, x, o); /* x = P_h */
+          for (int64_t a = 0; a < n; ++a) pm[a] += x[a] / (double)G;
+        }
+        /* the Index Branch distribution over the same tokens */
+        double m = -INFINITY;
+        for (int64_t a = 0; a < n; ++a) {
+          const int64_t ki = ((b * p->n_k + tok[a]) * Hkv + g) * DI;
+          double sc = 0.0;
+          for (int64_t c = 0; c < DI; ++c) sc += widen(iq, dtype, qi + c) * widen(ik, dtype, ki + c);
+          si[a] = sc;
+          if (sc > m) m = sc;
+        }
+        double l = 0.0;
+        for (int64_t a = 0; a < n; ++a) l += exp(si[a] - m);
+        const double lse = m + log(l);
+        double acc = 0.0;
+        for (int64_t a = 0; a < n; ++a) {
+          const double logpi = si[a] - lse;
+          if (pm[a] > 0.0) acc += pm[a] * (log(pm[a]) - logpi);
+          const double gs = loss_scale * (exp(logpi) - pm[a]);
+          const int64_t ki = ((b * p->n_k + tok[a]) * Hkv + g) * DI;
+          for (int64_t c = 0; c < DI; ++c) {
+            dq[c] += gs * widen(ik, dtype, ki + c);
+            d_ik[ki + c] += gs * widen(iq, dtype, qi + c);
+          }
+        }
+        kl[r * Hkv + g] = acc;
+      }
+    }
+    free(x);
+    free(pm);
+    free(si);
+    free(tok);
+    free(o);
+  }
+  return 0;
+}
+
 /* ---- MXFP8: OCP Microscaling Formats v1.0 (E4M3 elements, E8M0 scales) ---- */
 
 double mo_e4m3_value(uint8_t code) {

@@ -83,6 +83,20 @@ int mo_attend_backward(const mo_problem* p, const void* q, const void* k, const 
                        int dtype, const int32_t* ids, const int64_t* rows, int64_t n_rows, double* dq, double* dk,
                        double* dv);
 
+/* Index-Branch alignment loss (KL divergence from the Main Branch's
+ * group-averaged distribution to the Index Branch's, on the selected tokens;
+ * the selection and the Main Branch are fixed targets).  Per listed row and
+ * group g, over the visible selected tokens T:
+ *   pm(t) = (1/G) sum_{h in g} P_h(t)   (P_h as in mo_attend)
+ *   pi(t) = exp(s_t) / sum_{u in T} exp(s_u),  s_t = <iq[b,i,g], ik[b,t,g]>
+ *   kl    = sum_t pm(t) log(pm(t) / pi(t))
+ * kl: [n_rows][h_kv]; d_iq: [n_rows][h_kv][d_idx]; d_ik: [B, Nk, h_kv, d_idx]
+ * (the listed rows' contributions) -- the gradients of
+ * loss_scale * sum(kl).  ids: [n_rows][h_kv][topk].  All fp64. */
+int mo_indexer_kl(const mo_problem* p, const void* q, const void* k, const void* iq, const void* ik, int dtype,
+                  const int32_t* ids, const int64_t* rows, int64_t n_rows, double loss_scale, double* kl,
+                  double* d_iq, double* d_ik);
+
 /* Block -> query lists (the bookkeeping a KV-outer schedule needs; the paper
  * summary's "Key Contributions" name KV-outer attention): for each (b, g),
  * offsets[(b*h_kv+g)*(nblk+1) + j] = number of (i, slot) pairs with

@@ -97,6 +97,27 @@ class Oracle:
             dq = dq.reshape(prob.batch, prob.n_q, prob.h_q, prob.d)
         return dq, dk, dv
 
+    def indexer_kl(self, prob, q, k, iq, ik, ids, rows=None, loss_scale=1.0):
+        """fp64 (kl [n_rows, h_kv], d_iq [n_rows, h_kv, d_idx], d_ik [B, Nk, h_kv, d_idx]):
+        the Index-Branch alignment loss per (row, group) and the gradients of
+        loss_scale * sum(kl) with respect to the index queries and keys."""
+        q, d1 = _host(q)
+        k, d2 = _host(k)
+        iq, d3 = _host(iq)
+        ik, d4 = _host(ik)
+        assert d1 == d2 == d3 == d4
+        r, n = _rows(prob, rows)
+        ids = np.ascontiguousarray(np.asarray(ids, dtype=np.int32))
+        assert ids.size == n * prob.h_kv * prob.topk
+        kl = np.empty((n, prob.h_kv), dtype=np.float64)
+        d_iq = np.empty((n, prob.h_kv, prob.d_idx), dtype=np.float64)
+        d_ik = np.empty((prob.batch, prob.n_k, prob.h_kv, prob.d_idx), dtype=np.float64)
+        rc = self.L.mo_indexer_kl(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(iq), _ptr(ik), d1, _ptr(ids), _ptr(r), n,
+                                  float(loss_scale), _ptr(kl), _ptr(d_iq), _ptr(d_ik))
+        if rc:
+            raise ValueError(f"mo_indexer_kl: invalid argument ({rc})")
+        return kl, d_iq, d_ik
+
     def forward(self, prob, q, k, v, iq, ik, rows=None):
         """Select then attend; returns (ids, out, lse, scores)."""
         s = self.block_scores(prob, iq, ik, rows)
@@ -177,6 +198,10 @@ def attend_backward(prob, q, k, v, dout, ids, rows=None):
     return default().attend_backward(prob, q, k, v, dout, ids, rows)
 
 
+def indexer_kl(prob, q, k, iq, ik, ids, rows=None, loss_scale=1.0):
+    return default().indexer_kl(prob, q, k, iq, ik, ids, rows, loss_scale)
+
+
 def mx_quantize(x):
     return default().mx_quantize(x)
 
@@ -194,7 +219,8 @@ def load(path):
     L.mo_attend.argtypes = [P, vp, vp, vp, ctypes.c_int, vp, vp, ctypes.c_int64, vp, vp]
     L.mo_invert.argtypes = [P, vp, vp, vp]
     L.mo_attend_backward.argtypes = [P, vp, vp, vp, vp, ctypes.c_int, vp, vp, ctypes.c_int64, vp, vp, vp]
-    for f in (L.mo_block_scores, L.mo_select, L.mo_attend, L.mo_invert, L.mo_attend_backward):
+    L.mo_indexer_kl.argtypes = [P, vp, vp, vp, vp, ctypes.c_int, vp, vp, ctypes.c_int64, ctypes.c_double, vp, vp, vp]
+    for f in (L.mo_block_scores, L.mo_select, L.mo_attend, L.mo_invert, L.mo_attend_backward, L.mo_indexer_kl):
         f.restype = ctypes.c_int
     L.mo_num_threads.restype = ctypes.c_int
     L.mo_e4m3_value.argtypes = [ctypes.c_uint8]

@@ -368,6 +368,91 @@ def pin_backward_finite_differences(orc):
             assert abs(fd - grad[idx]) < 1e-7, (name, idx, fd, grad[idx])
 
 
+# ---- Index-Branch alignment loss (KL from the Main Branch's group-averaged
+# distribution to the Index Branch's, on the selected tokens).
+
+def _kl_torch(prob, x, ids, loss_scale):
+    """Dense fp64 torch formulation: masked softmaxes, kl_div, autograd for the
+    index inputs (the Main Branch distribution is a constant target)."""
+    B, N, Hq, Hkv, d = prob.batch, prob.n_q, prob.h_q, prob.h_kv, prob.d
+    G = Hq // Hkv
+    allowed = torch.from_numpy(_selection_mask(prob, ids))                      # [B, Nq, Hkv, Nk]
+    q = torch.from_numpy(x["q"]).reshape(B, N, Hkv, G, d)
+    k = torch.from_numpy(x["k"])
+    logits = torch.einsum("bigch,btgh->bigct", q, k) / math.sqrt(d)             # [B, Nq, Hkv, G, Nk]
+    logits = logits.masked_fill(~allowed[:, :, :, None, :], float("-inf"))
+    pm = torch.softmax(logits, dim=-1).mean(dim=3)                              # [B, Nq, Hkv, Nk]
+    iq = torch.tensor(x["iq"], requires_grad=True)
+    ik = torch.tensor(x["ik"], requires_grad=True)
+    si = torch.einsum("bigc,btgc->bigt", iq, ik).masked_fill(~allowed, float("-inf"))
+    logpi = torch.log_softmax(si, dim=-1)
+    # kl_div(input=log q, target=p) = p (log p - log q) elementwise, 0 where p = 0
+    kl = torch.nn.functional.kl_div(logpi.masked_fill(~allowed, 0.0), pm, reduction="none").sum(dim=-1)
+    (loss_scale * kl.sum()).backward()
+    return kl.detach().numpy(), iq.grad.numpy(), ik.grad.numpy()
+
+
+def pin_kl_equals_autograd(orc):
+    """KL per (row, group) and the gradients for the index queries and keys
+    equal torch autograd of the dense masked formulation (G = 2, offset queries)."""
+    rng = np.random.default_rng(37)
+    B, Nq, Nk, Hq, Hkv, d, di, Bk, K = 2, 20, 30, 4, 2, 8, 6, 4, 3
+    prob = O.make_problem(B, Nq, Nk, Hq, Hkv, d, di, Bk, K, q_offset=Nk - Nq)
+    x = _inputs(rng, B, Nq, Nk, Hq, Hkv, d, di)
+    x["q"] *= 2.0
+    ids, _, _, _ = orc.forward(prob, x["q"], x["k"], x["v"], x["iq"], x["ik"])
+    kl, d_iq, d_ik = orc.indexer_kl(prob, x["q"], x["k"], x["iq"], x["ik"], ids, loss_scale=0.3)
+    kl_t, giq, gik = _kl_torch(prob, x, ids, 0.3)
+    np.testing.assert_allclose(kl, kl_t.reshape(B * Nq, Hkv), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(d_iq, giq.reshape(B * Nq, Hkv, di), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(d_ik, gik, rtol=0, atol=1e-12)
+    assert kl.min() >= 0 and kl.max() > 1e-2 and np.abs(d_ik).max() > 1e-3
+
+
+def pin_kl_vanishes_when_aligned(orc):
+    """With the index scores equal to the Main Branch logits (G = 1,
+    iq = scale * q, ik = k) the two distributions coincide: KL and its
+    gradients vanish.  Perturbing iq makes KL strictly positive."""
+    rng = np.random.default_rng(41)
+    B, N, H, d, Bk, K = 1, 16, 2, 4, 4, 2
+    prob = O.make_problem(B, N, N, H, H, d, d, Bk, K)
+    x = _inputs(rng, B, N, N, H, H, d, d)
+    x["iq"] = x["q"] / math.sqrt(d)
+    x["ik"] = x["k"].copy()
+    ids, _, _, _ = orc.forward(prob, x["q"], x["k"], x["v"], x["iq"], x["ik"])
+    kl, d_iq, d_ik = orc.indexer_kl(prob, x["q"], x["k"], x["iq"], x["ik"], ids)
+    assert np.abs(kl).max() < 1e-13 and np.abs(d_iq).max() < 1e-13 and np.abs(d_ik).max() < 1e-13
+    x["iq"] = x["iq"] * 1.5
+    kl2, _, _ = orc.indexer_kl(prob, x["q"], x["k"], x["iq"], x["ik"], ids)
+    rows_with_choice = [r for r in range(N) if r >= 1]  # more than one visible token
+    assert kl2.reshape(N, H)[rows_with_choice].min() > 0
+
+
+def pin_kl_finite_differences(orc):
+    """Central differences of loss_scale * sum(kl) in the index inputs match the
+    analytic gradients (G = 4: the group average matters)."""
+    rng = np.random.default_rng(43)
+    B, Nq, Nk, Hq, Hkv, d, di, Bk, K = 1, 7, 13, 4, 1, 4, 3, 4, 2
+    prob = O.make_problem(B, Nq, Nk, Hq, Hkv, d, di, Bk, K, q_offset=Nk - Nq)
+    x = _inputs(rng, B, Nq, Nk, Hq, Hkv, d, di)
+    ids, _, _, _ = orc.forward(prob, x["q"], x["k"], x["v"], x["iq"], x["ik"])
+    _, d_iq, d_ik = orc.indexer_kl(prob, x["q"], x["k"], x["iq"], x["ik"], ids, loss_scale=2.0)
+
+    def loss(iq, ik):
+        kl, _, _ = orc.indexer_kl(prob, x["q"], x["k"], iq, ik, ids)
+        return 2.0 * float(kl.sum())
+
+    eps = 1e-6
+    for name, grad in (("iq", d_iq.reshape(x["iq"].shape)), ("ik", d_ik)):
+        for idx in [tuple(rng.integers(0, n) for n in grad.shape) for _ in range(10)]:
+            xp = {k_: v_.copy() for k_, v_ in x.items()}
+            xm = {k_: v_.copy() for k_, v_ in x.items()}
+            xp[name][idx] += eps
+            xm[name][idx] -= eps
+            fd = (loss(xp["iq"], xp["ik"]) - loss(xm["iq"], xm["ik"])) / (2 * eps)
+            assert abs(fd - grad[idx]) < 1e-7, (name, idx, fd, grad[idx])
+
+
 # ---- MXFP8 index-key caches (OCP Microscaling Formats v1.0; OCP 8-bit floating
 # point E4M3).  torch's float8_e4m3fn is an independent implementation of the
 # element format; the shared-exponent rule and the saturation are the MX
@@ -455,7 +540,8 @@ PINS = [pin_golden_worked_example, pin_maxpool_closed_form, pin_scores_ignore_fu
         pin_topk_bruteforce, pin_topk_special_cases, pin_exp_free, pin_dense_equals_sdpa,
         pin_sparse_equals_masked_sdpa, pin_value_invariants, pin_causal_diagonal,
         pin_e4m3_decode_table, pin_e4m3_encode_rne, pin_mx_shared_exponent, pin_mx_roundtrip,
-        pin_backward_equals_autograd, pin_backward_finite_differences]
+        pin_backward_equals_autograd, pin_backward_finite_differences, pin_kl_equals_autograd,
+        pin_kl_vanishes_when_aligned, pin_kl_finite_differences]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -570,6 +656,13 @@ MUTANTS = {
                            "dv[kvbase + c] += ds * widen(dout, dtype, qbase + c);"),
     "bwd_dq_from_values": ("dqr[c] += scale * ds * widen(k, dtype, kvbase + c);",
                            "dqr[c] += scale * ds * widen(v, dtype, kvbase + c);"),
+    "kl_no_group_average": ("pm[a] += x[a] / (double)G;", "pm[a] += x[a];"),
+    "kl_reversed_gradient": ("const double gs = loss_scale * (exp(logpi) - pm[a]);",
+                             "const double gs = loss_scale * (pm[a] - exp(logpi));"),
+    "kl_drops_target_entropy": ("if (pm[a] > 0.0) acc += pm[a] * (log(pm[a]) - logpi);",
+                                "if (pm[a] > 0.0) acc += -pm[a] * logpi;"),
+    "kl_unnormalised_index": ("const double logpi = si[a] - lse;", "const double logpi = si[a] - m;"),
+    "kl_dik_from_keys": ("d_ik[ki + c] += gs * widen(iq, dtype, qi + c);", "d_ik[ki + c] += gs * widen(ik, dtype, ki + c);"),
     "mx_truncates": ("double q = nearbyint(ldexp(a, 3 - e));", "double q = floor(ldexp(a, 3 - e));"),
     "mx_ties_away": ("const double m = nearbyint(ldexp(a, 9));", "const double m = round(ldexp(a, 9));"),
     "mx_emax_7": ("e = (ex - 1) - 8;", "e = (ex - 1) - 7;"),
