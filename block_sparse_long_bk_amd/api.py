@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_PKG, "libmsa.so")
 MSA_OK, MSA_ERR_INVALID_ARG, MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE, MSA_ERR_HIP = 0, -1, -2, -3, -4
 F32, BF16 = 0, 1
 SCHED_AUTO, SCHED_KV_OUTER, SCHED_Q_OUTER = 0, 1, 2
-OP_INDEX_TOPK, OP_ATTENTION, OP_FORWARD, OP_INVERT, OP_BACKWARD = 0, 1, 2, 3, 4
+OP_INDEX_TOPK, OP_ATTENTION, OP_FORWARD, OP_INVERT, OP_BACKWARD, OP_INDEXER_KL = 0, 1, 2, 3, 4, 5
 IDX_PLAIN, IDX_MXFP8 = 0, 1
 _IDXF = {"plain": IDX_PLAIN, "mxfp8": IDX_MXFP8}
 _SCHED = {"auto": SCHED_AUTO, "kv_outer": SCHED_KV_OUTER, "q_outer": SCHED_Q_OUTER}
@@ -46,7 +46,7 @@ _L = None
 
 EXPORTS = ["msa_status_string", "msa_last_hip_error", "msa_validate", "msa_workspace_size", "msa_block_scores",
            "msa_topk_from_scores", "msa_index_topk", "msa_invert", "msa_sparse_attention", "msa_forward",
-           "msa_sparse_attention_backward", "msa_mxfp8_quantize", "msa_profile_enable", "msa_profile_reset",
+           "msa_sparse_attention_backward", "msa_indexer_kl", "msa_mxfp8_quantize", "msa_profile_enable", "msa_profile_reset",
            "msa_profile_count", "msa_profile_read"]
 
 
@@ -71,6 +71,7 @@ def _lib():
         L.msa_sparse_attention.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.msa_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.msa_sparse_attention_backward.argtypes = [P] + [vp] * 10 + [vp, ctypes.c_size_t, vp]
+        L.msa_indexer_kl.argtypes = [P] + [vp] * 6 + [ctypes.c_float] + [vp] * 4 + [ctypes.c_size_t, vp]
         L.msa_mxfp8_quantize.argtypes = [vp, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, vp, vp, vp]
         L.msa_profile_enable.argtypes = [ctypes.c_int]
         L.msa_profile_count.restype = ctypes.c_int
@@ -267,6 +268,34 @@ def sparse_attention_backward(p, q, k, v, out, lse, dout, ids, dq=None, dk=None,
                                                 _ptr(dout), _ptr(ids), _ptr(dq), _ptr(dk), _ptr(dv), wp, wn,
                                                 _stream()), "msa_sparse_attention_backward")
     return dq, dk, dv
+
+
+def indexer_kl(p, q, k, iq, ik, lse, ids, loss_scale=1.0, kl=None, d_iq=None, d_ik=None, ws=None):
+    """Index-Branch alignment loss: kl [B, Nq, Hkv] (fp32) and the gradients
+    (d_iq, d_ik) of loss_scale * sum(kl) for the index queries and keys, given
+    the Main Branch inputs, the forward's lse and the selection."""
+    dt = _tdtype(p)
+    if p.idx_format != IDX_PLAIN:
+        raise ValueError("indexer_kl needs plain index keys")
+    _expect(q, (p.batch, p.n_q, p.h_q, p.d), dt, "q")
+    _expect(k, (p.batch, p.n_k, p.h_kv, p.d), dt, "k")
+    _expect(iq, (p.batch, p.n_q, p.h_kv, p.d_idx), dt, "idx_q")
+    _expect(ik, (p.batch, p.n_k, p.h_kv, p.d_idx), dt, "idx_k")
+    _expect(lse, (p.batch, p.n_q, p.h_q), torch.float32, "lse")
+    _expect(ids, (p.batch, p.n_q, p.h_kv, p.topk), torch.int32, "block_ids")
+    kl = torch.empty((p.batch, p.n_q, p.h_kv), dtype=torch.float32, device=q.device) if kl is None else kl
+    d_iq = torch.empty_like(iq) if d_iq is None else d_iq
+    d_ik = torch.empty_like(ik) if d_ik is None else d_ik
+    _expect(kl, (p.batch, p.n_q, p.h_kv), torch.float32, "kl")
+    _expect(d_iq, tuple(iq.shape), dt, "d_iq")
+    _expect(d_ik, tuple(ik.shape), dt, "d_ik")
+    if ws is None:
+        ws = alloc_workspace(p, OP_INDEXER_KL, q.device)
+    wp, wn = _ws(ws)
+    _check(_lib().msa_indexer_kl(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(iq), _ptr(ik), _ptr(lse), _ptr(ids),
+                                 float(loss_scale), _ptr(kl), _ptr(d_iq), _ptr(d_ik), wp, wn, _stream()),
+           "msa_indexer_kl")
+    return kl, d_iq, d_ik
 
 
 def forward(p, q, k, v, iq, ik, ids=None, out=None, lse=None, want_lse=True, ws=None):

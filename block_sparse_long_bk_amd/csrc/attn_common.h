@@ -50,6 +50,10 @@ struct KvStage {
   frag_t<T> vr[PASSES][4];
 
   __device__ __forceinline__ void load(const T* kbase, const T* vbase, int64_t tok_stride, int j, int n_k, int tid) {
+    load_k(kbase, tok_stride, j, n_k, tid);
+    load_v(vbase, tok_stride, j, n_k, tid);
+  }
+  __device__ __forceinline__ void load_k(const T* kbase, int64_t tok_stride, int j, int n_k, int tid) {
 #pragma unroll
     for (int u = 0; u < KLD; ++u) {
       const int c = tid + u * 256;
@@ -59,6 +63,8 @@ struct KvStage {
       if (c < KCH && t < n_k)
         kr[u] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(kbase + t * tok_stride) + col * 16);
     }
+  }
+  __device__ __forceinline__ void load_v(const T* vbase, int64_t tok_stride, int j, int n_k, int tid) {
     const int dch = tid % DCH, kg = tid / DCH;
 #pragma unroll
     for (int ps = 0; ps < PASSES; ++ps)
@@ -77,7 +83,10 @@ struct KvStage {
       const int c = tid + u * 256;
       if (c < KCH) *reinterpret_cast<u32x4*>(lds + (c / CPR) * L::KPITCH + (c % CPR) * 16) = kr[u];
     }
-    char* vt = lds + L::KBYTES;
+    store_vt(lds + L::KBYTES, tid);
+  }
+  // The transposed rows alone, at vt (D rows of VPITCH bytes).
+  __device__ __forceinline__ void store_vt(char* vt, int tid) const {
     const int dch = tid % DCH, kg = tid / DCH;
 #pragma unroll
     for (int ps = 0; ps < PASSES; ++ps) {
@@ -119,9 +128,8 @@ __device__ __forceinline__ void stage_kv(char* lds, const T* kbase, const T* vba
 
 // A fragment of V^T for k-step (mt, a): row d, keys 32mt+16a+4h+[0..3] and +8.
 template <typename T, int D, int BK>
-__device__ __forceinline__ frag_t<T> vt_frag(const char* lds, int d, int mt, int a, int half) {
+__device__ __forceinline__ frag_t<T> vt_frag_at(const char* vt, int d, int mt, int a, int half) {
   using L = KvLds<T, D, BK>;
-  const char* vt = lds + L::KBYTES;
   const int c0 = 8 * mt + 4 * a + half;  // chunk of keys 32mt+16a+4h .. +3
   const typename Pack4<T>::type lo = *reinterpret_cast<const typename Pack4<T>::type*>(vt + L::vt_off(d, c0));
   const typename Pack4<T>::type hi = *reinterpret_cast<const typename Pack4<T>::type*>(vt + L::vt_off(d, c0 + 2));
@@ -132,6 +140,10 @@ __device__ __forceinline__ frag_t<T> vt_frag(const char* lds, int d, int mt, int
     f[4 + e] = hi[e];
   }
   return f;
+}
+template <typename T, int D, int BK>
+__device__ __forceinline__ frag_t<T> vt_frag(const char* lds, int d, int mt, int a, int half) {
+  return vt_frag_at<T, D, BK>(lds + KvLds<T, D, BK>::KBYTES, d, mt, a, half);
 }
 
 template <typename T> __device__ __forceinline__ T from_f32(float x);

@@ -1,0 +1,579 @@
+// indexer_kl.hip -- the Index-Branch alignment loss and its gradients (gfx950).
+//
+// The pages train the Index Branch with a KL divergence that pulls its
+// distribution towards the Main Branch's group-averaged one on the selected
+// tokens; the Main Branch and the selection are fixed targets (gradient
+// detach), so only the index queries and keys receive gradients (paper
+// summary page, "Method"; zhichai.net write-up, section 5.1).  Per (b, i, g)
+// over the visible selected tokens T:
+//     pm(t) = (1/G) sum_{h in g} P_h(t)            P_h from the forward's LSE
+//     pi(t) = exp(s_t - lse_s),  s_t = <iq, ik_t>,  lse_s = log sum_T exp(s)
+//     kl    = sum_t pm(t) (log pm(t) - s_t + lse_s)
+//     d kl / d s_t = pi(t) - pm(t)
+// Work is organised on the KV-outer work items of the forward (block j and the
+// (query, slot) entries that chose it), each entry once for all its heads:
+//   k_kl_lse      entry = lane: the block's index scores -> a partial lse_s
+//                 per (query, group, slot)
+//   k_kl_lse_sum  lse_s per (query, group) over its slots
+//   k_kl_main     a lane owns a key (wave w: keys 32w..): index scores and the
+//                 G heads' probabilities for a 32-entry tile, the per-element
+//                 KL term and gradient g = loss_scale (pi - pm); d ik += g^T iq
+//                 in registers over the item's tiles; g goes through LDS to
+//                 form d iq^T = ik^T g^T per entry (fp32 partial per slot)
+//   k_kl_finish   kl and d iq per (query, group): slot partials summed in slot
+//                 order;  k_kl_dik_reduce: d ik summed over a block's items in
+//                 item order.  No atomics: results are bitwise reproducible.
+#include "attn_common.h"
+
+namespace msa {
+namespace {
+
+struct KlArgs {
+  const void* q;
+  const void* k;
+  const void* iq;
+  const void* ik;
+  const float* lse;      // [B, Nq, Hq] Main Branch log-sum-exp (natural log)
+  const int32_t* ids;    // [B, Nq, Hkv, topk]
+  const int32_t* entries;
+  const int32_t* item_count;
+  const int4* items;
+  float* plse;           // [B, Nq, Hkv, topk] partial index lse per slot
+  float* lse_s;          // [B, Nq, Hkv]
+  float* kl_part;        // [B, Nq, Hkv, topk]
+  float* diq_part;       // [B, Nq, Hkv, topk, DI]
+  float* dik_part;       // [B*Hkv][items_cap][BK][DI]
+  int Nq, Nk, Hq, Hkv, G, topk, items_cap;
+  int64_t q_offset;
+  uint64_t topk_magic;
+  float c_log2;      // Main Branch softmax scale * log2(e)
+  float loss_scale;
+};
+
+__device__ __forceinline__ void split_entry(int e, int topk, uint64_t magic, int& qq, int& slot) {
+  qq = (int)(((uint64_t)(uint32_t)e * magic) >> 40);
+  slot = e - qq * topk;
+}
+
+// ---- partial index lse per (query, group, slot): entry = lane ---------------
+template <typename T, int DI, int BK>
+__global__ void __launch_bounds__(256) k_kl_lse(KlArgs a) {
+  using L = KvLds<T, DI, BK>;
+  constexpr int MT = BK / 32;
+  __shared__ __attribute__((aligned(16))) char lds[BK * L::KPITCH];
+  __shared__ int32_t ent_lds[kMaxItemEntries];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
+  const int bg = blockIdx.y, b = bg / a.Hkv, g = bg % a.Hkv;
+  const int n = a.item_count[bg];
+  const int per = (n + 7) / 8;
+  const int x = blockIdx.x;
+  const int item = (x % 8) * per + x / 8;
+  if (x / 8 >= per || item >= n) return;
+  const int4 it = a.items[(int64_t)bg * a.items_cap + item];
+  const int j = it.x, e0 = it.y, nent = it.z - it.y;
+  const int32_t* ent = a.entries + (int64_t)bg * a.Nq * a.topk + e0;
+  for (int u = tid; u < nent; u += 256) ent_lds[u] = ent[u];
+  const int64_t tok_stride = (int64_t)a.Hkv * DI;
+  const T* ikb = static_cast<const T*>(a.ik) + (int64_t)b * a.Nk * tok_stride + g * DI;
+  {
+    constexpr int CPR = DI * (int)sizeof(T) / 16;
+    for (int c = tid; c < BK * CPR; c += 256) {
+      const int row = c / CPR, col = c % CPR;
+      const int64_t t = (int64_t)j * BK + row;
+      u32x4 v = u32x4{};
+      if (t < a.Nk) v = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(ikb + t * tok_stride) + col * 16);
+      *reinterpret_cast<u32x4*>(lds + row * L::KPITCH + col * 16) = v;
+    }
+  }
+  __syncthreads();
+  const int64_t key0 = (int64_t)j * BK;
+  for (int tile = wave; tile * 32 < nent; tile += 4) {
+    const int r = tile * 32 + (lane & 31);
+    const bool valid = r < nent;
+    int qq, slot;
+    split_entry(valid ? ent_lds[r] : ent_lds[0], a.topk, a.topk_magic, qq, slot);
+    const T* iqr = static_cast<const T*>(a.iq) + (((int64_t)b * a.Nq + qq) * a.Hkv + g) * DI + 8 * half;
+    frag_t<T> qf[DI / 16];
+#pragma unroll
+    for (int ks = 0; ks < DI / 16; ++ks) qf[ks] = load8(iqr + 16 * ks);
+    const int64_t pos = a.q_offset + qq;
+    const int vis = (int)max((int64_t)0, min((int64_t)BK, min(pos + 1, (int64_t)a.Nk) - key0));
+    float m = -__builtin_huge_valf(), l = 0.f;
+    f32x16 s[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const T* kr = reinterpret_cast<const T*>(lds + (mt * 32 + (lane & 31)) * L::KPITCH) + 8 * half;
+      s[mt] = mma0(load8(kr), qf[0]);
+#pragma unroll
+      for (int ks = 1; ks < DI / 16; ++ks) mma(load8(kr + 16 * ks), qf[ks], s[mt]);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int t = 32 * mt + 8 * (e / 4) + 4 * half + (e % 4);
+        if (t < vis) m = fmaxf(m, s[mt][e]);
+      }
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int t = 32 * mt + 8 * (e / 4) + 4 * half + (e % 4);
+        if (t < vis) l += exp2_fast((s[mt][e] - m) * kLog2e);
+      }
+    // merge the two halves' keys; token 0 of the block is always visible, so
+    // half 0 holds a finite maximum
+    const float mo = xor_shfl(m, 32), lo = xor_shfl(l, 32);
+    const float mm = fmaxf(m, mo);
+    const float lt = l * exp2_fast((m - mm) * kLog2e) + lo * exp2_fast((mo - mm) * kLog2e);
+    if (half == 0 && valid) a.plse[(((int64_t)b * a.Nq + qq) * a.Hkv + g) * a.topk + slot] = mm + __logf(lt);
+  }
+}
+
+// ---- lse_s per (query, group) over its selected slots -----------------------
+__global__ void __launch_bounds__(256) k_kl_lse_sum(const float* __restrict__ plse, const int32_t* __restrict__ ids,
+                                                    float* __restrict__ lse_s, int topk, int64_t nrows) {
+  const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (row >= nrows) return;
+  const int32_t* sel = ids + row * topk;
+  const float* p = plse + row * topk;
+  float m = -__builtin_huge_valf();
+  for (int s = 0; s < topk; ++s)
+    if (sel[s] >= 0) m = fmaxf(m, p[s]);
+  float l = 0.f;
+  for (int s = 0; s < topk; ++s)
+    if (sel[s] >= 0) l += exp2_fast((p[s] - m) * kLog2e);
+  lse_s[row] = m + __logf(l);
+}
+
+// ---- the main pass: a lane owns a key ---------------------------------------
+template <typename T, int D, int DI, int BK>
+struct KlLds {
+  using LI = KvLds<T, DI, BK>;
+  static constexpr int QPITCH = D * (int)sizeof(T) + 16;    // a Main Branch query row
+  static constexpr int IPITCH = DI * (int)sizeof(T) + 16;   // an index query row
+  static constexpr int TPITCH = 32 * (int)sizeof(T) + (sizeof(T) == 2 ? 8 : 16);  // 32 entries, transposed
+  static constexpr int GPITCH = BK * (int)sizeof(T) + 16;   // g row [entry][key]
+  static constexpr int IKT_OFF = 0;                          // ik^T [DI][BK]
+  static constexpr int IQ_OFF = IKT_OFF + DI * LI::VPITCH;   // iq tile [32][DI]
+  static constexpr int IQT_OFF = IQ_OFF + 32 * IPITCH;       // iq^T tile [DI][32]
+  static constexpr int G_OFF = IQT_OFF + DI * TPITCH;        // g [32][BK]
+  static constexpr int Q_OFF = G_OFF + 32 * GPITCH;          // HC heads x 32 query rows
+  static constexpr int FIXED = Q_OFF + 4 * kMaxItemEntries + 32 * 4 * 4 + 32 * 4 * 4 + 512;
+  static constexpr int BUDGET = 160 * 1024;
+  static constexpr int HC_FIT = (BUDGET - FIXED) / (32 * QPITCH);
+  static constexpr int HC = HC_FIT >= 8 ? 8 : HC_FIT >= 4 ? 4 : HC_FIT >= 2 ? 2 : 1;  // heads per staged chunk
+  static constexpr int BYTES = Q_OFF + HC * 32 * QPITCH;
+  static_assert(HC_FIT >= 1, "LDS budget");
+};
+
+// A fragment of a transposed 32-entry tile for k-step a: row c, entries
+// 16a + 4h + [0..3] and 16a + 8 + 4h + [0..3] (the accumulator order).
+template <typename T, int TPITCH>
+__device__ __forceinline__ frag_t<T> entries_t_frag(const char* base, int c, int a, int half) {
+  const T* row = reinterpret_cast<const T*>(base + c * TPITCH);
+  const int r0 = 16 * a + 4 * half;
+  const typename Pack4<T>::type lo = *reinterpret_cast<const typename Pack4<T>::type*>(row + r0);
+  const typename Pack4<T>::type hi = *reinterpret_cast<const typename Pack4<T>::type*>(row + r0 + 8);
+  frag_t<T> f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f[e] = lo[e];
+    f[4 + e] = hi[e];
+  }
+  return f;
+}
+
+template <typename T, int D, int DI, int BK>
+__global__ void __launch_bounds__(256, 1) k_kl_main(KlArgs a) {
+  using X = KlLds<T, D, DI, BK>;
+  constexpr int HC = X::HC;
+  __shared__ __attribute__((aligned(16))) char lds[X::BYTES];
+  __shared__ int32_t ent_lds[kMaxItemEntries];
+  __shared__ float row_lse_s[32], klw[4][32];
+  __shared__ int row_pos[32], row_q[32], row_slot[32];  // row_pos -1 past the item's end
+  __shared__ float row_lsm[HC][32];                      // Main Branch lse * log2(e) per (head, entry)
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
+  const int bg = blockIdx.y, b = bg / a.Hkv, g = bg % a.Hkv;
+  const int n = a.item_count[bg];
+  const int per = (n + 7) / 8;
+  const int x = blockIdx.x;
+  const int item = (x % 8) * per + x / 8;
+  if (x / 8 >= per || item >= n) return;
+  const int4 it = a.items[(int64_t)bg * a.items_cap + item];
+  const int j = it.x, e0 = it.y, nent = it.z - it.y;
+  const int32_t* ent = a.entries + (int64_t)bg * a.Nq * a.topk + e0;
+  for (int u = tid; u < nent; u += 256) ent_lds[u] = ent[u];
+
+  const int64_t ik_stride = (int64_t)a.Hkv * DI, k_stride = (int64_t)a.Hkv * D;
+  const T* ikb = static_cast<const T*>(a.ik) + (int64_t)b * a.Nk * ik_stride + g * DI;
+  const T* kb = static_cast<const T*>(a.k) + (int64_t)b * a.Nk * k_stride + g * D;
+  const T* iqb = static_cast<const T*>(a.iq);
+  const T* qb = static_cast<const T*>(a.q);
+  {
+    KvStage<T, DI, BK> st;
+    st.load_v(ikb, ik_stride, j, a.Nk, tid);
+    st.store_vt(lds + X::IKT_OFF, tid);
+  }
+  const int64_t key0 = (int64_t)j * BK;
+  const bool has_keys = wave * 32 < BK;
+  const int kk = wave * 32 + (lane & 31);                 // this lane's key in the block
+  const int64_t my_key = key0 + kk;
+  const int64_t kt = min(my_key, (int64_t)a.Nk - 1);      // keys past n_k are masked below
+  // this lane's key rows (B operands of the score products)
+  frag_t<T> kf[D / 16], ikf[DI / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) kf[ks] = load8(kb + kt * k_stride + 8 * half + 16 * ks);
+#pragma unroll
+  for (int ks = 0; ks < DI / 16; ++ks) ikf[ks] = load8(ikb + kt * ik_stride + 8 * half + 16 * ks);
+
+  f32x16 dik[DI / 32];
+#pragma unroll
+  for (int dt = 0; dt < DI / 32; ++dt) dik[dt] = f32x16{};
+  constexpr int ICPR = DI * (int)sizeof(T) / 16;
+  constexpr int QCPR = D * (int)sizeof(T) / 16;
+  const float inv_g = 1.f / (float)a.G;
+
+  for (int tile = 0; tile * 32 < nent; ++tile) {
+    __syncthreads();  // the previous tile's LDS is no longer read
+    for (int c = tid; c < 32 * ICPR; c += 256) {
+      const int rr = c / ICPR, col = c % ICPR;
+      const int r = tile * 32 + rr;
+      const bool valid = r < nent;
+      int qq, slot;
+      split_entry(valid ? ent_lds[r] : ent_lds[0], a.topk, a.topk_magic, qq, slot);
+      u32x4 v = *reinterpret_cast<const u32x4*>(
+          reinterpret_cast<const char*>(iqb + (((int64_t)b * a.Nq + qq) * a.Hkv + g) * DI) + col * 16);
+      if (!valid) v = u32x4{};
+      *reinterpret_cast<u32x4*>(lds + X::IQ_OFF + rr * X::IPITCH + col * 16) = v;
+      T el[16 / sizeof(T)];
+      __builtin_memcpy(el, &v, 16);
+#pragma unroll
+      for (int e = 0; e < (int)(16 / sizeof(T)); ++e)
+        *reinterpret_cast<T*>(lds + X::IQT_OFF + (col * (16 / (int)sizeof(T)) + e) * X::TPITCH +
+                              rr * (int)sizeof(T)) = el[e];
+      if (col == 0) {
+        const int64_t row = ((int64_t)b * a.Nq + qq) * a.Hkv + g;
+        row_lse_s[rr] = valid ? a.lse_s[row] : 0.f;
+        row_pos[rr] = valid ? (int)min(a.q_offset + qq, (int64_t)a.Nk - 1) : -1;
+        row_q[rr] = qq;
+        row_slot[rr] = slot;
+      }
+    }
+    __syncthreads();
+    // index scores s[entry][key] (accumulator rows = entries)
+    f32x16 si = f32x16{}, pm = f32x16{};
+    if (has_keys) {
+      const T* ir = reinterpret_cast<const T*>(lds + X::IQ_OFF + (lane & 31) * X::IPITCH) + 8 * half;
+#pragma unroll
+      for (int ks = 0; ks < DI / 16; ++ks) mma(load8(ir + 16 * ks), ikf[ks], si);
+    }
+    // the group's heads, HC at a time: pm += P_h
+    for (int h0 = 0; h0 < a.G; h0 += HC) {
+      const int hn = min(HC, a.G - h0);
+      __syncthreads();  // the previous chunk's query rows are no longer read
+      for (int c = tid; c < hn * 32 * QCPR; c += 256) {
+        const int hr = c / QCPR, col = c % QCPR;  // hr = hl * 32 + rr
+        const int hl = hr >> 5, rr = hr & 31;
+        const int r = tile * 32 + rr;
+        const bool valid = r < nent;
+        const int qq = row_q[rr];
+        const int64_t qrow = ((int64_t)b * a.Nq + qq) * a.Hq + g * a.G + h0 + hl;
+        u32x4 v = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(qb + qrow * D) + col * 16);
+        if (!valid) v = u32x4{};
+        *reinterpret_cast<u32x4*>(lds + X::Q_OFF + hr * X::QPITCH + col * 16) = v;
+        if (col == 0) row_lsm[hl][rr] = valid ? a.lse[qrow] * kLog2e : 0.f;
+      }
+      __syncthreads();
+      if (has_keys) {
+        for (int hl = 0; hl < hn; ++hl) {
+          const T* qr = reinterpret_cast<const T*>(lds + X::Q_OFF + (hl * 32 + (lane & 31)) * X::QPITCH) + 8 * half;
+          f32x16 s = mma0(load8(qr), kf[0]);
+#pragma unroll
+          for (int ks = 1; ks < D / 16; ++ks) mma(load8(qr + 16 * ks), kf[ks], s);
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int rr = 8 * (e / 4) + 4 * half + (e % 4);
+            const bool vis = row_pos[rr] >= 0 && my_key <= row_pos[rr];
+            pm[e] += vis ? exp2_fast(fmaf(s[e], a.c_log2, -row_lsm[hl][rr])) : 0.f;
+          }
+        }
+      }
+    }
+    if (has_keys) {
+      // per element: KL term and gradient; g to LDS as [entry][key]
+      f32x16 gs;
+      float term[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int rr = 8 * (e / 4) + 4 * half + (e % 4);
+        const bool vis = row_pos[rr] >= 0 && my_key <= row_pos[rr];
+        const float p = pm[e] * inv_g;
+        const float logpi = si[e] - row_lse_s[rr];
+        const float pi = exp2_fast(logpi * kLog2e);
+        term[e] = (vis && p > 0.f) ? p * (__logf(p) - logpi) : 0.f;
+        gs[e] = vis ? a.loss_scale * (pi - p) : 0.f;
+        *reinterpret_cast<T*>(lds + X::G_OFF + rr * X::GPITCH + kk * (int)sizeof(T)) = from_f32<T>(gs[e]);
+      }
+      // KL partial per entry over this wave's 32 keys
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+#pragma unroll
+        for (int m = 1; m < 32; m <<= 1) term[e] += xor_shfl(term[e], m);
+      }
+      if ((lane & 31) == 0) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) klw[wave][8 * (e / 4) + 4 * half + (e % 4)] = term[e];
+      }
+      // d ik[key][c] += sum over entries g^T[key][e] iq[e][c]
+#pragma unroll
+      for (int aa = 0; aa < 2; ++aa) {
+        frag_t<T> ga;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ga[e] = from_f32<T>(gs[8 * aa + e]);
+#pragma unroll
+        for (int dt = 0; dt < DI / 32; ++dt)
+          mma(ga, entries_t_frag<T, X::TPITCH>(lds + X::IQT_OFF, 32 * dt + (lane & 31), aa, half), dik[dt]);
+      }
+    }
+    __syncthreads();  // g and the KL partials of every wave are in LDS
+    // d iq^T[c][entry] = sum over the block's keys ik^T[c][key] g^T[key][entry];
+    // wave w takes c in [32w, 32w + 32)
+    if (wave < DI / 32) {
+      f32x16 o = f32x16{};
+      const int c = 32 * wave + (lane & 31);
+      const T* grow = reinterpret_cast<const T*>(lds + X::G_OFF + (lane & 31) * X::GPITCH);
+#pragma unroll
+      for (int mt = 0; mt < BK / 32; ++mt)
+#pragma unroll
+        for (int aa = 0; aa < 2; ++aa) {
+          const frag_t<T> ka = vt_frag_at<T, DI, BK>(lds + X::IKT_OFF, c, mt, aa, half);
+          const int k0 = 32 * mt + 16 * aa + 4 * half;
+          const typename Pack4<T>::type lo = *reinterpret_cast<const typename Pack4<T>::type*>(grow + k0);
+          const typename Pack4<T>::type hi = *reinterpret_cast<const typename Pack4<T>::type*>(grow + k0 + 8);
+          frag_t<T> gb;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            gb[e] = lo[e];
+            gb[4 + e] = hi[e];
+          }
+          mma(ka, gb, o);
+        }
+      const int rr = lane & 31;
+      if (row_pos[rr] >= 0) {
+        float* dst = a.diq_part + ((((int64_t)b * a.Nq + row_q[rr]) * a.Hkv + g) * a.topk + row_slot[rr]) * DI;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          *reinterpret_cast<f32x4*>(dst + 32 * wave + 8 * i + 4 * half) =
+              f32x4{o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]};
+      }
+    }
+    if (tid < 32 && row_pos[tid] >= 0) {
+      float acc = 0.f;
+      for (int w = 0; w < 4 && w * 32 < BK; ++w) acc += klw[w][tid];
+      a.kl_part[(((int64_t)b * a.Nq + row_q[tid]) * a.Hkv + g) * a.topk + row_slot[tid]] = acc;
+    }
+  }
+  if (!has_keys) return;
+  // this item's d ik: lane holds key 32w + 8(e/4) + 4h + e%4, c = 32 dt + lane%32
+  float* dst = a.dik_part + ((int64_t)bg * a.items_cap + item) * BK * DI;
+#pragma unroll
+  for (int dt = 0; dt < DI / 32; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int key = wave * 32 + 8 * (e / 4) + 4 * half + (e % 4);
+      dst[key * DI + 32 * dt + (lane & 31)] = dik[dt][e];
+    }
+}
+
+// ---- kl and d iq per (query, group): slot partials in slot order ------------
+template <typename T, int DI>
+__global__ void __launch_bounds__(256) k_kl_finish(const float* __restrict__ kl_part,
+                                                   const float* __restrict__ diq_part,
+                                                   const int32_t* __restrict__ ids, float* __restrict__ kl,
+                                                   T* __restrict__ d_iq, int topk, int64_t nrows) {
+  constexpr int LPR = DI / 8;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * (64 / LPR) + lane / LPR;  // (b, i, g)
+  if (row >= nrows) return;
+  const int32_t* sel = ids + row * topk;
+  const float* p = diq_part + row * topk * DI + (lane % LPR) * 8;
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  float kacc = 0.f;
+  for (int s = 0; s < topk; ++s) {
+    if (sel[s] < 0) continue;
+    const f32x4 lo = *reinterpret_cast<const f32x4*>(p + (int64_t)s * DI);
+    const f32x4 hi = *reinterpret_cast<const f32x4*>(p + (int64_t)s * DI + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[e] += lo[e];
+      acc[4 + e] += hi[e];
+    }
+    kacc += kl_part[row * topk + s];
+  }
+  if (lane % LPR == 0) kl[row] = kacc;
+  frag_t<T> o;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = from_f32<T>(acc[e]);
+  T* dst = d_iq + row * DI + (lane % LPR) * 8;
+  if constexpr (sizeof(T) == 2) {
+    *reinterpret_cast<frag_t<T>*>(dst) = o;
+  } else {
+    *reinterpret_cast<f32x4*>(dst) = f32x4{o[0], o[1], o[2], o[3]};
+    *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[4], o[5], o[6], o[7]};
+  }
+}
+
+// ---- d ik: item partials of each block in item order ------------------------
+template <typename T, int DI, int BK>
+__global__ void __launch_bounds__(256) k_kl_dik_reduce(const float* __restrict__ part, const int4* __restrict__ items,
+                                                       const int32_t* __restrict__ item_count, T* __restrict__ d_ik,
+                                                       int Nk, int Hkv, int nblk, int items_cap) {
+  constexpr int CH = DI / 8;
+  const int bg = blockIdx.y, b = bg / Hkv, g = bg % Hkv;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // over nblk * BK * CH
+  if (idx >= (int64_t)nblk * BK * CH) return;
+  const int j = (int)(idx / (BK * CH));
+  const int tk = (int)(idx / CH % BK), c = (int)(idx % CH);
+  const int64_t t = (int64_t)j * BK + tk;
+  if (t >= Nk) return;
+  const int4* its = items + (int64_t)bg * items_cap;
+  const int n = item_count[bg];
+  int lo = 0, hi = n;  // first item of block j (items are in block order)
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (its[mid].x < j) lo = mid + 1;
+    else hi = mid;
+  }
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int u = lo; u < n && its[u].x == j; ++u) {
+    const float* p = part + ((int64_t)bg * items_cap + u) * BK * DI + tk * DI + c * 8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += p[e];
+  }
+  frag_t<T> o;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = from_f32<T>(acc[e]);
+  T* dst = d_ik + (((int64_t)b * Nk + t) * Hkv + g) * DI + c * 8;
+  if constexpr (sizeof(T) == 2) {
+    *reinterpret_cast<frag_t<T>*>(dst) = o;
+  } else {
+    *reinterpret_cast<f32x4*>(dst) = f32x4{o[0], o[1], o[2], o[3]};
+    *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[4], o[5], o[6], o[7]};
+  }
+}
+
+struct KlKernels {
+  int lse, lse_sum, main, finish, reduce;
+};
+
+template <typename T, int D, int DI, int BK>
+void kl_launch_bk(const Shape& s, const KlArgs& a, const InvertPlan& p, float* kl, void* d_iq, void* d_ik,
+                  hipStream_t st, const KlKernels& kid) {
+  const dim3 grid(p.items_cap, s.B * s.Hkv);
+  const int64_t nrows = (int64_t)s.B * s.Nq * s.Hkv;
+  prof_begin(st, kid.lse);
+  hipLaunchKernelGGL((k_kl_lse<T, DI, BK>), grid, dim3(256), 0, st, a);
+  prof_end(st, kid.lse);
+  prof_begin(st, kid.lse_sum);
+  hipLaunchKernelGGL(k_kl_lse_sum, dim3((unsigned)((nrows + 255) / 256)), dim3(256), 0, st, a.plse, a.ids, a.lse_s,
+                     s.topk, nrows);
+  prof_end(st, kid.lse_sum);
+  prof_begin(st, kid.main);
+  hipLaunchKernelGGL((k_kl_main<T, D, DI, BK>), grid, dim3(256), 0, st, a);
+  prof_end(st, kid.main);
+  const int rpb = 4 * (64 / (DI / 8));
+  prof_begin(st, kid.finish);
+  hipLaunchKernelGGL((k_kl_finish<T, DI>), dim3((unsigned)((nrows + rpb - 1) / rpb)), dim3(256), 0, st, a.kl_part,
+                     a.diq_part, a.ids, kl, static_cast<T*>(d_iq), s.topk, nrows);
+  prof_end(st, kid.finish);
+  const int64_t nthr = (int64_t)s.nblk * BK * (DI / 8);
+  prof_begin(st, kid.reduce);
+  hipLaunchKernelGGL((k_kl_dik_reduce<T, DI, BK>), dim3((unsigned)((nthr + 255) / 256), s.B * s.Hkv), dim3(256), 0,
+                     st, a.dik_part, a.items, a.item_count, static_cast<T*>(d_ik), s.Nk, s.Hkv, s.nblk, p.items_cap);
+  prof_end(st, kid.reduce);
+}
+
+template <typename T, int D, int DI>
+void kl_launch_di(const Shape& s, const KlArgs& a, const InvertPlan& p, float* kl, void* d_iq, void* d_ik,
+                  hipStream_t st, const KlKernels& kid) {
+  if (s.Bk == 32) kl_launch_bk<T, D, DI, 32>(s, a, p, kl, d_iq, d_ik, st, kid);
+  else if (s.Bk == 64) kl_launch_bk<T, D, DI, 64>(s, a, p, kl, d_iq, d_ik, st, kid);
+  else kl_launch_bk<T, D, DI, 128>(s, a, p, kl, d_iq, d_ik, st, kid);
+}
+
+template <typename T, int D>
+void kl_launch_d(const Shape& s, const KlArgs& a, const InvertPlan& p, float* kl, void* d_iq, void* d_ik,
+                 hipStream_t st, const KlKernels& kid) {
+  if (s.DI == 32) kl_launch_di<T, D, 32>(s, a, p, kl, d_iq, d_ik, st, kid);
+  else if (s.DI == 64) kl_launch_di<T, D, 64>(s, a, p, kl, d_iq, d_ik, st, kid);
+  else kl_launch_di<T, D, 128>(s, a, p, kl, d_iq, d_ik, st, kid);
+}
+
+}  // namespace
+
+size_t kl_bytes(const Shape& s, const InvertPlan& p, KlWorkspace* w) {
+  const size_t rows = (size_t)s.B * s.Nq * s.Hkv;
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  size_t off = 0;
+  KlWorkspace L;
+  L.plse = off;
+  off += up(rows * s.topk * 4);
+  L.lse_s = off;
+  off += up(rows * 4);
+  L.kl_part = off;
+  off += up(rows * s.topk * 4);
+  L.diq_part = off;
+  off += up(rows * s.topk * s.DI * 4);
+  L.dik_part = off;
+  off += up((size_t)s.B * s.Hkv * p.items_cap * s.Bk * s.DI * 4);
+  if (w) *w = L;
+  return off;
+}
+
+hipError_t launch_indexer_kl(const Shape& s, const InvertPlan& p, const void* q, const void* k, const void* iq,
+                             const void* ik, const float* lse, const int32_t* ids, const InvertOut& inv, char* ws,
+                             float loss_scale, float* kl, void* d_iq, void* d_ik, hipStream_t st) {
+  static const KlKernels kid{prof_register("kl_lse"), prof_register("kl_lse_sum"), prof_register("kl_main"),
+                             prof_register("kl_finish"), prof_register("kl_dik_reduce")};
+  KlWorkspace L;
+  kl_bytes(s, p, &L);
+  KlArgs a;
+  a.q = q;
+  a.k = k;
+  a.iq = iq;
+  a.ik = ik;
+  a.lse = lse;
+  a.ids = ids;
+  a.entries = inv.entries;
+  a.item_count = inv.item_count;
+  a.items = inv.items;
+  a.plse = reinterpret_cast<float*>(ws + L.plse);
+  a.lse_s = reinterpret_cast<float*>(ws + L.lse_s);
+  a.kl_part = reinterpret_cast<float*>(ws + L.kl_part);
+  a.diq_part = reinterpret_cast<float*>(ws + L.diq_part);
+  a.dik_part = reinterpret_cast<float*>(ws + L.dik_part);
+  a.Nq = s.Nq;
+  a.Nk = s.Nk;
+  a.Hq = s.Hq;
+  a.Hkv = s.Hkv;
+  a.G = s.Hq / s.Hkv;
+  a.topk = s.topk;
+  a.items_cap = p.items_cap;
+  a.q_offset = s.q_offset;
+  a.topk_magic = ((uint64_t)1 << 40) / (uint64_t)s.topk + 1;
+  a.c_log2 = s.scale * kLog2e;
+  a.loss_scale = loss_scale;
+  if (s.dtype == kBF16) {
+    if (s.D == 64) kl_launch_d<bf16_t, 64>(s, a, p, kl, d_iq, d_ik, st, kid);
+    else kl_launch_d<bf16_t, 128>(s, a, p, kl, d_iq, d_ik, st, kid);
+  } else {
+    if (s.D == 64) kl_launch_d<float, 64>(s, a, p, kl, d_iq, d_ik, st, kid);
+    else kl_launch_d<float, 128>(s, a, p, kl, d_iq, d_ik, st, kid);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace msa

@@ -165,6 +165,33 @@ BwdLayout bwd_layout(const msa::Shape& s) {
   return L;
 }
 
+// Indexer KL workspace: the inversion of the whole problem, then the loss's
+// partials.
+struct KlLayout {
+  size_t offsets, entries, item_count, items, inv_scratch, kl, total;
+};
+
+KlLayout kl_layout(const msa::Shape& s) {
+  const msa::InvertPlan p = msa::invert_plan(s, s.Nq);
+  const size_t BG = (size_t)s.B * s.Hkv;
+  KlLayout L;
+  size_t off = 0;
+  L.offsets = off;
+  off += align_up(BG * (s.nblk + 1) * 4);
+  L.entries = off;
+  off += align_up(BG * (size_t)s.Nq * s.topk * 4);
+  L.item_count = off;
+  off += align_up(BG * 4);
+  L.items = off;
+  off += align_up(BG * (size_t)p.items_cap * 16);
+  L.inv_scratch = off;
+  off += align_up(msa::invert_ws_bytes(s, p));
+  L.kl = off;
+  off += align_up(msa::kl_bytes(s, p, nullptr));
+  L.total = off;
+  return L;
+}
+
 size_t qo_bytes(const msa::Shape& s, int nc, int nsplit) {
   if (nsplit <= 1) return 0;
   return align_up((size_t)s.B * nc * s.Hq * nsplit * s.D * elem_bytes(s)) + align_up((size_t)s.B * nc * s.Hq * nsplit * 4);
@@ -354,7 +381,7 @@ msa_status_t msa_validate(const msa_problem_t* prob) { return validate(prob); }
 msa_status_t msa_workspace_size(const msa_problem_t* prob, int op, size_t* bytes, size_t* min_bytes) {
   msa_status_t rc = validate(prob);
   if (rc != MSA_OK) return rc;
-  if (!bytes || op < MSA_OP_INDEX_TOPK || op > MSA_OP_BACKWARD) return MSA_ERR_INVALID_ARG;
+  if (!bytes || op < MSA_OP_INDEX_TOPK || op > MSA_OP_INDEXER_KL) return MSA_ERR_INVALID_ARG;
   const msa::Shape s = shape_of(prob);
   size_t full = 0, least = 0;
   if (op == MSA_OP_INVERT) {
@@ -362,6 +389,9 @@ msa_status_t msa_workspace_size(const msa_problem_t* prob, int op, size_t* bytes
   }
   if (op == MSA_OP_BACKWARD) {
     full = least = bwd_layout(s).total;
+  }
+  if (op == MSA_OP_INDEXER_KL) {
+    full = least = kl_layout(s).total;
   }
   if (op == MSA_OP_INDEX_TOPK || op == MSA_OP_FORWARD) {
     full = std::max(full, index_bytes(s));
@@ -419,6 +449,34 @@ msa_status_t msa_sparse_attention_backward(const msa_problem_t* prob, const void
     e = msa::launch_bwd_attention(s, plan, q, k, v, dout, lse, drow, block_ids, inv,
                                   reinterpret_cast<float*>(w + L.dq_part), reinterpret_cast<float*>(w + L.dkv_part),
                                   w + L.trash, dq, dk, dv, st);
+  return e == hipSuccess ? MSA_OK : hip_fail(e);
+}
+
+msa_status_t msa_indexer_kl(const msa_problem_t* prob, const void* q, const void* k, const void* idx_q,
+                            const void* idx_k, const float* lse, const int32_t* block_ids, float loss_scale,
+                            float* kl, void* d_iq, void* d_ik, void* ws, size_t ws_bytes, void* stream) {
+  msa_status_t rc = validate(prob);
+  if (rc != MSA_OK) return rc;
+  if (prob->idx_format != MSA_IDX_PLAIN) return MSA_ERR_UNSUPPORTED;
+  if (!std::isfinite(loss_scale)) return MSA_ERR_INVALID_ARG;
+  const void* ptrs[] = {q, k, idx_q, idx_k, lse, block_ids, kl, d_iq, d_ik, ws};
+  for (const void* x : ptrs)
+    if (!x || !aligned16(x)) return MSA_ERR_INVALID_ARG;
+  const msa::Shape s = shape_of(prob);
+  const KlLayout L = kl_layout(s);
+  if (ws_bytes < L.total) return MSA_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  const msa::InvertPlan plan = msa::invert_plan(s, s.Nq);
+  msa::InvertOut inv;
+  inv.offsets = reinterpret_cast<int32_t*>(w + L.offsets);
+  inv.entries = reinterpret_cast<int32_t*>(w + L.entries);
+  inv.item_count = reinterpret_cast<int32_t*>(w + L.item_count);
+  inv.items = reinterpret_cast<int4*>(w + L.items);
+  hipError_t e = msa::launch_invert(s, plan, block_ids, 0, s.Nq, inv, w + L.inv_scratch, st);
+  if (e == hipSuccess)
+    e = msa::launch_indexer_kl(s, plan, q, k, idx_q, idx_k, lse, block_ids, inv, w + L.kl, loss_scale, kl, d_iq,
+                               d_ik, st);
   return e == hipSuccess ? MSA_OK : hip_fail(e);
 }
 

@@ -105,4 +105,16 @@ hipError_t launch_bwd_attention(const Shape& s, const InvertPlan& p, const void*
                                 const InvertOut& inv, float* dq_part, float* dkv_part, void* trash, void* dq, void* dk,
                                 void* dv, hipStream_t st);
 
+// Index-Branch alignment loss -----------------------------------------------
+struct KlWorkspace {
+  size_t plse, lse_s, kl_part, diq_part, dik_part;
+};
+// Bytes of the loss's scratch after the inversion (layout in *w when given).
+size_t kl_bytes(const Shape& s, const InvertPlan& p, KlWorkspace* w);
+// kl per (b, i, g) and the gradients of loss_scale * sum(kl) for idx_q / idx_k,
+// for the work items of `inv` (whole problem); ws holds kl_bytes() bytes.
+hipError_t launch_indexer_kl(const Shape& s, const InvertPlan& p, const void* q, const void* k, const void* iq,
+                             const void* ik, const float* lse, const int32_t* ids, const InvertOut& inv, char* ws,
+                             float loss_scale, float* kl, void* d_iq, void* d_ik, hipStream_t st);
+
 }  // namespace msa

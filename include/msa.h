@@ -104,7 +104,8 @@ typedef enum {
   MSA_OP_ATTENTION = 1,
   MSA_OP_FORWARD = 2,
   MSA_OP_INVERT = 3,
-  MSA_OP_BACKWARD = 4
+  MSA_OP_BACKWARD = 4,
+  MSA_OP_INDEXER_KL = 5
 } msa_op_t;
 
 /* Human-readable name of a status code (static storage). */
@@ -179,6 +180,25 @@ msa_status_t msa_sparse_attention_backward(const msa_problem_t* prob, const void
                                            const void* out, const float* lse, const void* dout,
                                            const int32_t* block_ids, void* dq, void* dk, void* dv, void* ws,
                                            size_t ws_bytes, void* stream);
+
+/* The Index-Branch alignment loss (paper summary page, "Method"; zhichai.net
+ * write-up, section 5.1): the KL divergence from the Main Branch's
+ * group-averaged attention distribution to the Index Branch's distribution,
+ * both over the visible selected tokens T of (b, i, g).  With P_h the Main
+ * Branch softmax of head h (recomputed from q, k and the forward's lse) and
+ * s_t = <idx_q, idx_k_t> the raw token scores:
+ *   pm(t) = mean over the group's heads of P_h(t),  pi = softmax over T of s,
+ *   kl[b, i, g] = sum_t pm(t) log(pm(t) / pi(t))          (fp32 [B, Nq, Hkv])
+ * and the gradients of loss_scale * sum(kl) with respect to the index inputs,
+ *   d_iq [B, Nq, Hkv, d_idx], d_ik [B, Nk, Hkv, d_idx]    (dtype of the inputs)
+ * (d kl / d s_t = pi(t) - pm(t)).  The Main Branch and the selection are fixed
+ * targets: nothing flows to q or k (the pages' gradient detach).  Keys no query
+ * selects get zero d_ik.  Sums in fixed orders (no atomics).  Needs plain
+ * (not MXFP8) index keys and the MSA_OP_INDEXER_KL workspace (whole problem).
+ * Errors as for msa_sparse_attention. */
+msa_status_t msa_indexer_kl(const msa_problem_t* prob, const void* q, const void* k, const void* idx_q,
+                            const void* idx_k, const float* lse, const int32_t* block_ids, float loss_scale,
+                            float* kl, void* d_iq, void* d_ik, void* ws, size_t ws_bytes, void* stream);
 
 /* Quantise n_rows rows of row_len elements (row_len a multiple of 32) of src
  * (device, `src_dtype` MSA_F32 or MSA_BF16, row-major) to MXFP8 following the

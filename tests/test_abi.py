@@ -96,6 +96,13 @@ def test_entry_points_reject_before_any_hip_call():
     assert bw(ctypes.byref(p), x, x, x, x, x, x, x, null, x, x, x, 1 << 30, null) == api.MSA_ERR_INVALID_ARG
     assert bw(ctypes.byref(p), x, x, x, x, x, x, x, x, x, x, x, 1024, null) == api.MSA_ERR_WORKSPACE
     assert bw(ctypes.byref(bad), x, x, x, x, x, x, x, x, x, x, x, 1 << 30, null) == api.MSA_ERR_UNSUPPORTED
+    # indexer loss: plain index keys only, finite loss scale, workspace
+    kl = L.msa_indexer_kl
+    assert kl(ctypes.byref(p), x, x, x, x, x, x, 1.0, x, x, x, x, 1024, null) == api.MSA_ERR_WORKSPACE
+    assert kl(ctypes.byref(p), x, x, x, x, x, x, float("inf"), x, x, x, x, 1 << 30, null) == api.MSA_ERR_INVALID_ARG
+    assert kl(ctypes.byref(p), x, x, x, x, x, x, 1.0, x, null, x, x, 1 << 30, null) == api.MSA_ERR_INVALID_ARG
+    mx = good(idx_format="mxfp8")
+    assert kl(ctypes.byref(mx), x, x, x, x, x, x, 1.0, x, x, x, x, 1 << 30, null) == api.MSA_ERR_UNSUPPORTED
     # MXFP8 quantiser: sizes, dtype and pointers are checked before any launch
     q = L.msa_mxfp8_quantize
     assert q(x, api.BF16, 4, 48, x, x, null) == api.MSA_ERR_INVALID_ARG   # row length not a multiple of 32
@@ -129,3 +136,6 @@ def test_workspace_sizes():
     # backward: fp32 dq partials per (query, head, slot) dominate
     bwd, bwd_least = api.workspace_size(pre, api.OP_BACKWARD)
     assert bwd == bwd_least >= 32768 * 64 * 16 * 128 * 4
+    # indexer loss: fp32 d_iq partials per (query, group, slot)
+    klw, klw_least = api.workspace_size(pre, api.OP_INDEXER_KL)
+    assert klw == klw_least >= 32768 * 8 * 16 * 128 * 4

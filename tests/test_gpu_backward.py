@@ -130,3 +130,48 @@ def test_backward_is_deterministic(name):
     for u, w, nm in zip(a, b, ("dq", "dk", "dv")):
         assert torch.equal(u.view(torch.uint8) if u.dtype == torch.bfloat16 else u,
                            w.view(torch.uint8) if w.dtype == torch.bfloat16 else w), nm
+
+
+def test_backward_full_size_prefill_32k():
+    """The bench's prefill shape (32k tokens, Hq 64, Hkv 8, d 128, k 16, bf16),
+    whole problem in one call.  Checked against the oracle on a sample of query
+    rows (dq) and on the last key block of every group (dk, dv: only the last
+    Bk queries can select it, and all of them are in the sample), with the
+    oracle's selection substituted for those rows.  Over all rows, two
+    properties of the chain rule through a softmax: sum_t dv_t equals the sum
+    of dout over the group's query rows (the P of a row sum to 1), and
+    sum_t dk_t vanishes (the dS of a row sum to 0)."""
+    wl = inputs.WORKLOADS["prefill_32k"]
+    print(f"[{wl.name}] generating", flush=True)
+    x = inputs.generate(wl, device="cuda", tensors=("q", "k", "v", "iq", "ik", "dout"))
+    p = api.problem_of(wl)
+    ids = api.index_topk(p, x["iq"], x["ik"])
+    Bk, N = wl.block_size, wl.n_q
+    last0 = (wl.nblk - 1) * Bk
+    qi = np.unique(np.concatenate([np.linspace(0, last0 - 1, 24).astype(np.int64), np.arange(last0, N)]))
+    rows = np.stack([np.zeros_like(qi), qi], axis=1)
+    prob = O.problem_of(wl)
+    hx = {k: host(v) for k, v in x.items()}
+    s = O.block_scores(prob, hx["iq"], hx["ik"], rows)
+    ids_o = O.select(prob, s, rows)
+    ids[0, qi] = torch.from_numpy(ids_o).cuda()
+    print(f"[{wl.name}] oracle selection of {len(qi)} rows done", flush=True)
+    out, lse = api.sparse_attention(p, x["q"], x["k"], x["v"], ids)
+    dq, dk, dv = api.sparse_attention_backward(p, x["q"], x["k"], x["v"], out, lse, x["dout"], ids)
+    torch.cuda.synchronize()
+    print(f"[{wl.name}] GPU backward done", flush=True)
+    rq, rk, rv = O.attend_backward(prob, hx["q"], hx["k"], hx["v"], hx["dout"], ids_o, rows=rows)
+    print(f"[{wl.name}] oracle backward done", flush=True)
+    e_q = check(wl.dtype, dq[0, qi], rq, "dq (sampled rows)")
+    e_k = check(wl.dtype, dk[0, last0:], rk[0, last0:], "dk (last block)")
+    e_v = check(wl.dtype, dv[0, last0:], rv[0, last0:], "dv (last block)")
+    print(f"[{wl.name}] dq {e_q}, dk {e_k}, dv {e_v}", flush=True)
+    # properties over every row
+    G = wl.h_q // wl.h_kv
+    dv_sum = dv.double().sum(dim=1)                                             # [B, Hkv, D]
+    do_sum = x["dout"].double().sum(dim=1).reshape(wl.batch, wl.h_kv, G, wl.d).sum(dim=2)
+    rel_v = float((dv_sum - do_sum).norm() / do_sum.norm())
+    dk_sum = dk.double().sum(dim=1)
+    rel_k = float(dk_sum.norm() / dk.double().abs().sum(dim=1).norm())
+    print(f"[{wl.name}] sum dv vs sum dout rel {rel_v:.2e}; |sum dk| / sum |dk| {rel_k:.2e}", flush=True)
+    assert rel_v <= 1e-2 and rel_k <= 1e-2
