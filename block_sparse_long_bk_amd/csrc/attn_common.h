@@ -150,6 +150,25 @@ template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) { return static_cast<bf16_t>(x); }
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 
+// A fragment of a transposed 32-row tile (rows of TPITCH bytes, one per
+// column) for k-step a: column c, tile rows 16a + 4h + [0..3] and
+// 16a + 8 + 4h + [0..3] -- the order of an accumulator's rows, so that a
+// product whose other operand comes straight from an accumulator lines up.
+template <typename T, int TPITCH>
+__device__ __forceinline__ frag_t<T> tile_t_frag(const char* base, int c, int a, int half) {
+  const T* row = reinterpret_cast<const T*>(base + c * TPITCH);
+  const int r0 = 16 * a + 4 * half;
+  const typename Pack4<T>::type lo = *reinterpret_cast<const typename Pack4<T>::type*>(row + r0);
+  const typename Pack4<T>::type hi = *reinterpret_cast<const typename Pack4<T>::type*>(row + r0 + 8);
+  frag_t<T> f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f[e] = lo[e];
+    f[4 + e] = hi[e];
+  }
+  return f;
+}
+
 // Query rows of one 32-row tile of a KV-outer work item.
 struct TileRows {
   bool valid;

@@ -14,18 +14,14 @@
 // P is recomputed from the forward's log-sum-exp, so nothing of the forward
 // but O and LSE is kept.
 //
-// Both heavy kernels walk the KV-outer work items of the forward (block j and
-// the (query, head) rows that chose it; msa_invert's lists):
-//  * k_bwd_dq keeps the forward's orientation -- each query row in a lane pair,
-//    S^T = K Q^T, dP^T = V dO^T, dQ^T = K^T dS^T (dS taken straight from the
-//    accumulators) -- and writes one fp32 dq partial per (row, slot), summed
-//    in slot order afterwards: no atomics.
-//  * k_bwd_dkdv turns the products around so that a lane owns a key: wave w
-//    takes keys [32w, 32w+32) of the block, S = Q K^T and dP = dO V^T per
-//    32-row tile, and accumulates dV += P^T dO and dK += dS^T Q in registers
-//    over the item's tiles (the tile's Q and dO are staged in LDS, row-major
-//    and transposed).  Each item writes fp32 dk/dv partials of its block;
-//    k_bwd_dkdv_reduce sums the items of every block in item order.
+// The heavy kernel walks the KV-outer work items of the forward (block j and
+// the (query, head) rows that chose it; msa_invert's lists) with a lane owning
+// a key of the block: S = Q K^T and dP = dO V^T per 32-row tile, dV += P^T dO
+// and dK += dS^T Q accumulated in registers over the item's tiles, and
+// dQ = dS K formed per tile from dS passed through LDS (k_bwd_fused).  dq goes
+// out as one partial per (row, slot), summed in slot order (k_bwd_dq_sum); dk
+// and dv as fp32 partials per item, summed per block in item order
+// (k_bwd_dkdv_reduce).  No atomics.
 #include "attn_common.h"
 
 namespace msa {
@@ -41,7 +37,7 @@ struct BwdArgs {
   const int32_t* entries;
   const int32_t* item_count;
   const int4* items;
-  float* dq_part;        // [B, Nq, Hq, topk, D] fp32
+  void* dq_part;         // [B, Nq, Hq, topk, D] in the input type
   float* dkv_part;       // [B*Hkv][items_cap][2][BK][D] fp32 (dk, then dv)
   void* trash;           // scratch line for the stores of rows past an item's end
   int Nq, Nk, Hq, Hkv, G, topk, items_cap, gshift;
@@ -69,43 +65,135 @@ __global__ void __launch_bounds__(256) k_bwd_rowdot(const T* __restrict__ out, c
   if (lane % LPR == 0) drow[row] = acc;
 }
 
-// Rows of one key block (BK rows of D elements at a token stride) staged into
-// LDS with the row pitch of KvLds.  Rows past n_k are zero-filled.
+// ---- the fused pass over one work item -------------------------------------
+// A lane owns a key (wave w: keys [32w, 32w+32) of the block, held in
+// registers as MFMA B operands); the item's (query, head) rows go by in tiles
+// of 32.  Per tile: S = Q K^T and dP = dO V^T (rows in the accumulator), P and
+// dS = P (dP - D) in place, dV += P^T dO and dK += dS^T Q with the
+// accumulators as A operands and the tile's transposed rows as B operands.
+// dS is written to LDS as [row][key]; after a barrier wave w forms
+// dQ^T[32w..32w+32) = K^T dS^T over the whole block (K^T staged once per item)
+// and stores it as the (row, slot) partial.  The next tile's rows are fetched
+// into registers before the current tile's products and written to LDS while
+// the dQ products run.
 template <typename T, int D, int BK>
-__device__ __forceinline__ void stage_rows(char* dst, const T* base, int64_t tok_stride, int j, int n_k, int tid) {
+struct FusedLds {
   using L = KvLds<T, D, BK>;
-  constexpr int CPR = D * (int)sizeof(T) / 16;
-  constexpr int CH = BK * CPR;
+  static constexpr int RPITCH = D * (int)sizeof(T) + 16;                          // a tile row
+  static constexpr int TPITCH = 32 * (int)sizeof(T) + (sizeof(T) == 2 ? 8 : 16);  // a transposed tile row
+  static constexpr int SPITCH = BK * (int)sizeof(T) + 16;                         // a dS row [row][key]
+  static constexpr int KT_OFF = 0;                                                 // K^T [D][BK]
+  static constexpr int Q_OFF = KT_OFF + D * L::VPITCH;
+  static constexpr int DO_OFF = Q_OFF + 32 * RPITCH;
+  static constexpr int QT_OFF = DO_OFF + 32 * RPITCH;
+  static constexpr int DOT_OFF = QT_OFF + D * TPITCH;
+  static constexpr int DS_OFF = DOT_OFF + D * TPITCH;
+  static constexpr int BYTES = DS_OFF + 32 * SPITCH;
+};
+
+// The Q and dO rows of one tile: each task moves a 16-byte column chunk of
+// four consecutive rows of one tensor, so that the transposed copy is written
+// four rows at a time.
+template <typename T, int D>
+struct TileStage {
+  static constexpr int CPR = D * (int)sizeof(T) / 16;  // chunks per row
+  static constexpr int EPC = 16 / (int)sizeof(T);      // elements per chunk
+  static constexpr int TASKS = 2 * 8 * CPR;
+  static constexpr int NT = (TASKS + 255) / 256;
+  // Loaded values are left untouched until store(): any use right after the
+  // loads would make the compiler wait for them there, and the fetch would no
+  // longer overlap the current tile's products.
+  u32x4 v[NT][4];
+  float lse[4], dr[4];
+  int pos[4];
+  int64_t prow[4];
+  uint32_t valid_mask;
+
+  __device__ __forceinline__ void load(const BwdArgs& a, const int32_t* ent_lds, int tile, int nrows, int b, int g,
+                                       int tid) {
+    valid_mask = 0;
 #pragma unroll
-  for (int u = 0; u < (CH + 255) / 256; ++u) {
-    const int c = tid + u * 256;
-    if (c < CH) {
-      const int row = c / CPR, col = c % CPR;
-      const int64_t t = (int64_t)j * BK + row;
-      u32x4 x = u32x4{};
-      if (t < n_k) x = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(base + t * tok_stride) + col * 16);
-      *reinterpret_cast<u32x4*>(dst + row * L::KPITCH + col * 16) = x;
+    for (int u = 0; u < NT; ++u) {
+      const int task = tid + 256 * u;
+      if (task >= TASKS) continue;
+      const int tensor = task / (8 * CPR), rg = task / CPR % 8, col = task % CPR;
+      const T* base = static_cast<const T*>(tensor ? a.dout : a.q);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int rr = tile * 32 + 4 * rg + r;
+        const bool valid = rr < nrows;
+        const TileRows t = rows_of(valid ? ent_lds[rr >> a.gshift] : ent_lds[0], valid, rr, a.gshift, a.topk,
+                                   a.topk_magic, g);
+        const int64_t rowi = ((int64_t)b * a.Nq + t.qq) * a.Hq + t.h;
+        // rows past the item's end read a valid row (entry 0) and store zeros
+        v[u][r] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(base + rowi * D) + col * 16);
+        valid_mask |= (uint32_t)valid << (4 * u + r);
+        if (u == 0 && tensor == 0 && col == 0) {
+          lse[r] = a.lse[rowi];
+          dr[r] = a.drow[rowi];
+          pos[r] = valid ? (int)min(a.q_offset + t.qq, (int64_t)a.Nk - 1) : -1;
+          prow[r] = rowi * a.topk + t.slot;
+        }
+      }
     }
   }
-}
 
-// ---- dq partials: forward orientation ---------------------------------------
-// LDS: K rows | K^T (the KvLds "V^T" region, filled with K) | V rows | obuf.
+  template <int BK>
+  __device__ __forceinline__ void store(char* lds, float* row_lse2, float* row_d, int* row_pos, int64_t* row_prow,
+                                        int tid) const {
+    using X = FusedLds<T, D, BK>;
+#pragma unroll
+    for (int u = 0; u < NT; ++u) {
+      const int task = tid + 256 * u;
+      if (task >= TASKS) continue;
+      const int tensor = task / (8 * CPR), rg = task / CPR % 8, col = task % CPR;
+      char* rows = lds + (tensor ? X::DO_OFF : X::Q_OFF);
+      char* tr = lds + (tensor ? X::DOT_OFF : X::QT_OFF);
+      u32x4 vv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        vv[r] = (valid_mask >> (4 * u + r)) & 1 ? v[u][r] : u32x4{};
+        *reinterpret_cast<u32x4*>(rows + (4 * rg + r) * X::RPITCH + col * 16) = vv[r];
+      }
+      if constexpr (sizeof(T) == 2) {
+        // elements 2w and 2w+1 of the chunk for the four rows: 2x2 transposes
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t x0 = vv[0][w], x1 = vv[1][w], x2 = vv[2][w], x3 = vv[3][w];
+          const uint2 lo = make_uint2(__builtin_amdgcn_perm(x1, x0, 0x05040100u), __builtin_amdgcn_perm(x3, x2, 0x05040100u));
+          const uint2 hi = make_uint2(__builtin_amdgcn_perm(x1, x0, 0x07060302u), __builtin_amdgcn_perm(x3, x2, 0x07060302u));
+          *reinterpret_cast<uint2*>(tr + (col * EPC + 2 * w) * X::TPITCH + 4 * rg * 2) = lo;
+          *reinterpret_cast<uint2*>(tr + (col * EPC + 2 * w + 1) * X::TPITCH + 4 * rg * 2) = hi;
+        }
+      } else {
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          *reinterpret_cast<u32x4*>(tr + (col * EPC + w) * X::TPITCH + 4 * rg * 4) =
+              u32x4{vv[0][w], vv[1][w], vv[2][w], vv[3][w]};
+      }
+      if (u == 0 && tensor == 0 && col == 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool ok = (valid_mask >> r) & 1;
+          row_lse2[4 * rg + r] = ok ? lse[r] * kLog2e : 0.f;
+          row_d[4 * rg + r] = ok ? dr[r] : 0.f;
+          row_pos[4 * rg + r] = pos[r];
+          row_prow[4 * rg + r] = prow[r];
+        }
+      }
+    }
+  }
+};
+
 template <typename T, int D, int BK>
-__global__ void __launch_bounds__(256, 1) k_bwd_dq(BwdArgs a) {
-  using L = KvLds<T, D, BK>;
-  constexpr int MT = BK / 32;
-  constexpr int ROWB = D * 4;           // one fp32 dq partial row
-  constexpr int OPITCH = ROWB + 16;
-  constexpr int LPR = ROWB / 16;        // lanes per row on the way out
-  constexpr int RPS = 64 / LPR;         // rows per store instruction
-  // fp32 with d = 128 and 128-token blocks: V rows would not fit beside K and
-  // K^T, so its fragments are read from global memory instead.
-  constexpr bool V_LDS = !(sizeof(T) == 4 && D == 128 && BK == 128);
-  __shared__ __attribute__((aligned(16))) char lds[L::BYTES + (V_LDS ? BK * L::KPITCH : 16)];
+__global__ void __launch_bounds__(256, 1) k_bwd_fused(BwdArgs a) {
+  using X = FusedLds<T, D, BK>;
+  __shared__ __attribute__((aligned(16))) char lds[X::BYTES];
   __shared__ int32_t ent_lds[kMaxItemEntries];
-  __shared__ __attribute__((aligned(16))) char obuf[4][8 * OPITCH];
-  char* vrows = lds + L::BYTES;
+  __shared__ __attribute__((aligned(16))) float row_lse2[32];
+  __shared__ __attribute__((aligned(16))) float row_d[32];
+  __shared__ __attribute__((aligned(16))) int row_pos[32];  // -1 for rows past the item's end
+  __shared__ int64_t row_prow[32];                           // dq partial row: (b, i, h) * topk + slot
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
   const int bg = blockIdx.y, b = bg / a.Hkv, g = bg % a.Hkv;
   const int n = a.item_count[bg];
@@ -123,286 +211,123 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dq(BwdArgs a) {
   const int64_t tok_stride = (int64_t)a.Hkv * D;
   const T* kb = static_cast<const T*>(a.k) + (int64_t)b * a.Nk * tok_stride + g * D;
   const T* vb = static_cast<const T*>(a.v) + (int64_t)b * a.Nk * tok_stride + g * D;
-  stage_kv<T, D, BK>(lds, kb, kb, tok_stride, j, a.Nk, tid);  // K rows and K^T
-  if constexpr (V_LDS) stage_rows<T, D, BK>(vrows, vb, tok_stride, j, a.Nk, tid);
-  __syncthreads();
+  {
+    KvStage<T, D, BK> st;
+    st.load_v(kb, tok_stride, j, a.Nk, tid);
+    st.store_vt(lds + X::KT_OFF, tid);
+  }
   const int64_t key0 = (int64_t)j * BK;
-  const T* qbase = static_cast<const T*>(a.q);
-  const T* dobase = static_cast<const T*>(a.dout);
-  char* ob = obuf[wave];
-
-  for (int tile = wave; tile * 32 < nrows; tile += 4) {
-    const int r = tile * 32 + (lane & 31);
-    const bool valid = r < nrows;
-    const TileRows cur = rows_of(valid ? ent_lds[r >> a.gshift] : 0, valid, r, a.gshift, a.topk, a.topk_magic, g);
-    frag_t<T> qf[D / 16], dof[D / 16];
-    load_q_rows<T, D>(qf, qbase, cur, b, a.Nq, a.Hq, 0, half);
-    load_q_rows<T, D>(dof, dobase, cur, b, a.Nq, a.Hq, 0, half);
-    const int64_t rowi = ((int64_t)b * a.Nq + cur.qq) * a.Hq + cur.h;
-    const float lse2 = a.lse[rowi] * kLog2e;
-    const float dr = a.drow[rowi];
-    const int64_t pos = a.q_offset + cur.qq;
-    const int vis = (int)max((int64_t)0, min((int64_t)BK, min(pos + 1, (int64_t)a.Nk) - key0));
-    // S^T = K Q^T and dP^T = V dO^T (each lane pair holds row c's keys)
-    f32x16 s[MT], dp[MT];
+  const bool has_keys = wave * 32 < BK;  // waves past the block's keys stage and form dQ only
+  const int kk = wave * 32 + (lane & 31);
+  const int64_t my_key = key0 + kk;
+  const int64_t kt = min(my_key, (int64_t)a.Nk - 1);  // keys past n_k are masked below
+  frag_t<T> kf[D / 16], vf[D / 16];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int kk = mt * 32 + (lane & 31);  // key of this lane's A rows
-      const T* krow = reinterpret_cast<const T*>(lds + kk * L::KPITCH) + 8 * half;
-      // V rows past n_k read token n_k - 1: their keys are masked below
-      const T* vrow = V_LDS ? reinterpret_cast<const T*>(vrows + kk * L::KPITCH) + 8 * half
-                            : vb + min(key0 + kk, (int64_t)a.Nk - 1) * tok_stride + 8 * half;
-      s[mt] = mma0(load8(krow), qf[0]);
-      dp[mt] = mma0(load8(vrow), dof[0]);
-#pragma unroll
-      for (int ks = 1; ks < D / 16; ++ks) {
-        mma(load8(krow + 16 * ks), qf[ks], s[mt]);
-        mma(load8(vrow + 16 * ks), dof[ks], dp[mt]);
-      }
-    }
-    // dS = P (dP - D), P = exp2(x log2e - lse log2e); masked keys give P = 0
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int t = 32 * mt + 8 * (e / 4) + 4 * half + (e % 4);
-        const float p = t < vis ? exp2_fast(fmaf(s[mt][e], a.c_log2, -lse2)) : 0.f;
-        s[mt][e] = p * (dp[mt][e] - dr);
-      }
-    // dQ^T = K^T dS^T, dS taken from the accumulators (k permuted as in the forward)
-    f32x16 o[D / 32];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int aa = 0; aa < 2; ++aa) {
-        frag_t<T> pb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pb[e] = from_f32<T>(s[mt][8 * aa + e]);
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          const frag_t<T> ka = vt_frag<T, D, BK>(lds, 32 * dt + (lane & 31), mt, aa, half);
-          if (mt == 0 && aa == 0) o[dt] = mma0(ka, pb);
-          else mma(ka, pb, o[dt]);
-        }
-      }
-    // fp32 partial rows out through LDS, 8 rows per pass (whole rows per store)
-    const int64_t prow = rowi * a.topk + cur.slot;
-#pragma unroll
-    for (int ps = 0; ps < 4; ++ps) {
-      if (((lane & 31) >> 3) == ps) {
-        char* orow = ob + ((lane & 7) * OPITCH);
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const f32x4 w = f32x4{o[dt][4 * i] * a.scale, o[dt][4 * i + 1] * a.scale, o[dt][4 * i + 2] * a.scale,
-                                  o[dt][4 * i + 3] * a.scale};
-            *reinterpret_cast<f32x4*>(orow + (32 * dt + 8 * i + 4 * half) * 4) = w;
-          }
-      }
-      wave_lds_sync();
-#pragma unroll
-      for (int kk = 0; kk < 8 / RPS; ++kk) {
-        const int rl = lane / LPR + kk * RPS;
-        const int src = ps * 8 + rl;
-        const int64_t dst_row = __shfl(prow, src, 64);
-        const int ok = __shfl((int)cur.valid, src, 64);
-        const u32x4 v = *reinterpret_cast<const u32x4*>(ob + rl * OPITCH + (lane % LPR) * 16);
-        char* dst = ok ? reinterpret_cast<char*>(a.dq_part) + dst_row * ROWB : static_cast<char*>(a.trash);
-        *reinterpret_cast<u32x4*>(dst + (lane % LPR) * 16) = v;
-      }
-      wave_lds_sync();
-    }
+  for (int ks = 0; ks < D / 16; ++ks) {
+    kf[ks] = load8(kb + kt * tok_stride + 8 * half + 16 * ks);
+    vf[ks] = load8(vb + kt * tok_stride + 8 * half + 16 * ks);
   }
-}
-
-// ---- dq = sum of the slot partials, in slot order ---------------------------
-template <typename T, int D>
-__global__ void __launch_bounds__(256) k_bwd_dq_sum(const float* __restrict__ part, const int32_t* __restrict__ ids,
-                                                    T* __restrict__ dq, int Nq, int Hq, int Hkv, int G, int topk,
-                                                    int64_t nrows) {
-  constexpr int LPR = D / 8;
-  const int lane = threadIdx.x & 63;
-  const int64_t row = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * (64 / LPR) + lane / LPR;  // (b, i, h)
-  if (row >= nrows) return;
-  const int h = (int)(row % Hq);
-  const int64_t bi = row / Hq;
-  const int32_t* sel = ids + (bi * Hkv + h / G) * topk;
-  const float* p = part + row * topk * D + (lane % LPR) * 8;
-  float acc[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-  for (int s = 0; s < topk; ++s) {
-    if (sel[s] < 0) continue;
-    const f32x4 lo = *reinterpret_cast<const f32x4*>(p + (int64_t)s * D);
-    const f32x4 hi = *reinterpret_cast<const f32x4*>(p + (int64_t)s * D + 4);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc[e] += lo[e];
-      acc[4 + e] += hi[e];
-    }
-  }
-  frag_t<T> o;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) o[e] = from_f32<T>(acc[e]);
-  T* dst = dq + row * D + (lane % LPR) * 8;
-  if constexpr (sizeof(T) == 2) {
-    *reinterpret_cast<frag_t<T>*>(dst) = o;
-  } else {
-    *reinterpret_cast<f32x4*>(dst) = f32x4{o[0], o[1], o[2], o[3]};
-    *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[4], o[5], o[6], o[7]};
-  }
-}
-
-// ---- dk / dv partials: a lane owns a key ------------------------------------
-// LDS: K rows | V rows | the tile's Q and dO rows (row-major) | their
-// transposes | per-row log-sum-exp, D and position.
-template <typename T, int D, int BK>
-struct DkdvLds {
-  using L = KvLds<T, D, BK>;
-  // fp32 with d = 128 and 128-token blocks: K and V fragments come from global
-  // memory (the block would not fit beside the tile buffers).
-  static constexpr bool KV_LDS = !(sizeof(T) == 4 && D == 128 && BK == 128);
-  static constexpr int RPITCH = D * (int)sizeof(T) + 16;            // a tile row
-  static constexpr int TPITCH = 32 * (int)sizeof(T) + (sizeof(T) == 2 ? 8 : 16);  // a transposed row (32 rows)
-  static constexpr int K_OFF = 0;
-  static constexpr int V_OFF = KV_LDS ? BK * L::KPITCH : 0;
-  static constexpr int Q_OFF = KV_LDS ? V_OFF + BK * L::KPITCH : 0;
-  static constexpr int DO_OFF = Q_OFF + 32 * RPITCH;
-  static constexpr int QT_OFF = DO_OFF + 32 * RPITCH;
-  static constexpr int DOT_OFF = QT_OFF + D * TPITCH;
-  static constexpr int BYTES = DOT_OFF + D * TPITCH;
-};
-
-// A fragment of a transposed tile for k-step a: row d, tile rows
-// 16a + 4h + [0..3] and 16a + 8 + 4h + [0..3] (the accumulator order).
-template <typename T, int D, int BK>
-__device__ __forceinline__ frag_t<T> tile_t_frag(const char* base, int d, int a, int half) {
-  using X = DkdvLds<T, D, BK>;
-  const T* row = reinterpret_cast<const T*>(base + d * X::TPITCH);
-  const int r0 = 16 * a + 4 * half;
-  const typename Pack4<T>::type lo = *reinterpret_cast<const typename Pack4<T>::type*>(row + r0);
-  const typename Pack4<T>::type hi = *reinterpret_cast<const typename Pack4<T>::type*>(row + r0 + 8);
-  frag_t<T> f;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    f[e] = lo[e];
-    f[4 + e] = hi[e];
-  }
-  return f;
-}
-
-template <typename T, int D, int BK>
-__global__ void __launch_bounds__(256, 1) k_bwd_dkdv(BwdArgs a) {
-  using L = KvLds<T, D, BK>;
-  using X = DkdvLds<T, D, BK>;
-  __shared__ __attribute__((aligned(16))) char lds[X::BYTES];
-  __shared__ int32_t ent_lds[kMaxItemEntries];
-  __shared__ float row_lse2[32], row_d[32];
-  __shared__ int row_pos[32];  // -1 for rows past the item's end
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
-  const int bg = blockIdx.y, b = bg / a.Hkv, g = bg % a.Hkv;
-  const int n = a.item_count[bg];
-  const int per = (n + 7) / 8;
-  const int x = blockIdx.x;
-  const int item = (x % 8) * per + x / 8;
-  if (x / 8 >= per || item >= n) return;
-  const int4 it = a.items[(int64_t)bg * a.items_cap + item];
-  const int j = it.x, e0 = it.y, e1 = it.z;
-  const int nrows = (e1 - e0) * a.G;
-  const int nent = e1 - e0;
-  const int32_t* ent = a.entries + (int64_t)bg * a.Nq * a.topk + e0;
-  for (int u = tid; u < nent; u += 256) ent_lds[u] = ent[u];
-
-  const int64_t tok_stride = (int64_t)a.Hkv * D;
-  const T* kb = static_cast<const T*>(a.k) + (int64_t)b * a.Nk * tok_stride + g * D;
-  const T* vb = static_cast<const T*>(a.v) + (int64_t)b * a.Nk * tok_stride + g * D;
-  if constexpr (X::KV_LDS) {
-    stage_rows<T, D, BK>(lds + X::K_OFF, kb, tok_stride, j, a.Nk, tid);
-    stage_rows<T, D, BK>(lds + X::V_OFF, vb, tok_stride, j, a.Nk, tid);
-  }
-  const T* qbase = static_cast<const T*>(a.q);
-  const T* dobase = static_cast<const T*>(a.dout);
-  const int64_t key0 = (int64_t)j * BK;
-  const bool has_keys = wave * 32 < BK;  // waves past the block's keys only help staging
-  const int64_t my_key = key0 + wave * 32 + (lane & 31);
-
   f32x16 dkacc[D / 32], dvacc[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) {
     dkacc[dt] = f32x16{};
     dvacc[dt] = f32x16{};
   }
-  constexpr int CPR = D * (int)sizeof(T) / 16;  // 16-byte chunks per tile row
-  for (int tile = 0; tile * 32 < nrows; ++tile) {
-    __syncthreads();  // the previous tile's staging is no longer read
-    // Stage the tile's 32 (query, head) rows of Q and dO, row-major and transposed.
-    for (int c = tid; c < 32 * CPR * 2; c += 256) {
-      const int which = c / (32 * CPR);  // 0: Q, 1: dO
-      const int cc = c % (32 * CPR);
-      const int rr = cc / CPR, col = cc % CPR;
-      const int r = tile * 32 + rr;
-      const bool valid = r < nrows;
-      const TileRows t = rows_of(valid ? ent_lds[r >> a.gshift] : 0, valid, r, a.gshift, a.topk, a.topk_magic, g);
-      const T* src = (which ? dobase : qbase) + (((int64_t)b * a.Nq + t.qq) * a.Hq + t.h) * D;
-      u32x4 v = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(src) + col * 16);
-      if (!valid) v = u32x4{};
-      *reinterpret_cast<u32x4*>(lds + (which ? X::DO_OFF : X::Q_OFF) + rr * X::RPITCH + col * 16) = v;
-      T el[16 / sizeof(T)];
-      __builtin_memcpy(el, &v, 16);
-      char* tb = lds + (which ? X::DOT_OFF : X::QT_OFF);
+  __syncthreads();  // ent_lds
+  TileStage<T, D> stg;
+  stg.load(a, ent_lds, 0, nrows, b, g, tid);
+  stg.template store<BK>(lds, row_lse2, row_d, row_pos, row_prow, tid);
+  // Every load so far (the key rows included) has landed: without this the
+  // compiler's wait before the first use of kf / vf inside the loop also
+  // covers the next tile's fetch, which would then no longer overlap.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  const int ntiles = (nrows + 31) / 32;
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const bool more = tile + 1 < ntiles;
+    if (more) stg.load(a, ent_lds, tile + 1, nrows, b, g, tid);
+    const int my_pos = row_pos[lane & 31];
+    const int64_t my_prow = row_prow[lane & 31];
+    if (has_keys) {
+      // S = Q K^T, dP = dO V^T: lane = key, accumulator rows = tile rows
+      f32x16 s = f32x16{}, dp = f32x16{};
+      const T* qr = reinterpret_cast<const T*>(lds + X::Q_OFF + (lane & 31) * X::RPITCH) + 8 * half;
+      const T* dr = reinterpret_cast<const T*>(lds + X::DO_OFF + (lane & 31) * X::RPITCH) + 8 * half;
 #pragma unroll
-      for (int e = 0; e < (int)(16 / sizeof(T)); ++e)
-        *reinterpret_cast<T*>(tb + (col * (16 / (int)sizeof(T)) + e) * X::TPITCH + rr * (int)sizeof(T)) = el[e];
-      if (which == 0 && col == 0) {
-        const int64_t rowi = ((int64_t)b * a.Nq + t.qq) * a.Hq + t.h;
-        row_lse2[rr] = valid ? a.lse[rowi] * kLog2e : 0.f;
-        row_d[rr] = valid ? a.drow[rowi] : 0.f;
-        row_pos[rr] = valid ? (int)min(a.q_offset + t.qq, (int64_t)a.Nk - 1) : -1;
+      for (int ks = 0; ks < D / 16; ++ks) {
+        mma(load8(qr + 16 * ks), kf[ks], s);
+        mma(load8(dr + 16 * ks), vf[ks], dp);
+      }
+      // P and dS in place; accumulator position e is tile row 8(e/4) + 4h + e%4
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int r0 = 8 * q4 + 4 * half;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(row_lse2 + r0);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(row_d + r0);
+        const int4 p4 = *reinterpret_cast<const int4*>(row_pos + r0);
+        const int pp[4] = {p4.x, p4.y, p4.z, p4.w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int e = 4 * q4 + c;
+          const float p = my_key <= pp[c] ? exp2_fast(fmaf(s[e], a.c_log2, -l4[c])) : 0.f;
+          s[e] = p;
+          dp[e] = p * (dp[e] - d4[c]);
+          *reinterpret_cast<T*>(lds + X::DS_OFF + (r0 + c) * X::SPITCH + kk * (int)sizeof(T)) = from_f32<T>(dp[e]);
+        }
+      }
+      // dV += P^T dO, dK += dS^T Q
+#pragma unroll
+      for (int aa = 0; aa < 2; ++aa) {
+        frag_t<T> pa, sa;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pa[e] = from_f32<T>(s[8 * aa + e]);
+          sa[e] = from_f32<T>(dp[8 * aa + e]);
+        }
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+          mma(pa, tile_t_frag<T, X::TPITCH>(lds + X::DOT_OFF, 32 * dt + (lane & 31), aa, half), dvacc[dt]);
+          mma(sa, tile_t_frag<T, X::TPITCH>(lds + X::QT_OFF, 32 * dt + (lane & 31), aa, half), dkacc[dt]);
+        }
       }
     }
-    __syncthreads();
-    if (!has_keys) continue;
-    // S = Q K^T and dP = dO V^T for this wave's 32 keys: lane = key, rows in the accumulator
-    f32x16 s = f32x16{}, dp = f32x16{};
-    const T* qr = reinterpret_cast<const T*>(lds + X::Q_OFF + (lane & 31) * X::RPITCH) + 8 * half;
-    const T* dr = reinterpret_cast<const T*>(lds + X::DO_OFF + (lane & 31) * X::RPITCH) + 8 * half;
-    const int kk = wave * 32 + (lane & 31);  // this lane's key in the block
-    const int64_t kt = min(key0 + kk, (int64_t)a.Nk - 1);  // keys past n_k are masked below
-    const T* kr = X::KV_LDS ? reinterpret_cast<const T*>(lds + X::K_OFF + kk * L::KPITCH) + 8 * half
-                            : kb + kt * tok_stride + 8 * half;
-    const T* vr = X::KV_LDS ? reinterpret_cast<const T*>(lds + X::V_OFF + kk * L::KPITCH) + 8 * half
-                            : vb + kt * tok_stride + 8 * half;
+    __syncthreads();  // dS complete; the tile's rows are no longer read
+    if (more) stg.template store<BK>(lds, row_lse2, row_d, row_pos, row_prow, tid);
+    if (wave < D / 32) {
+      // dQ^T[c][row] = sum over the block's keys of K^T[c][key] dS^T[key][row]
+      f32x16 o = f32x16{};
+      const int c = 32 * wave + (lane & 31);
+      const T* srow = reinterpret_cast<const T*>(lds + X::DS_OFF + (lane & 31) * X::SPITCH);
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      mma(load8(qr + 16 * ks), load8(kr + 16 * ks), s);
-      mma(load8(dr + 16 * ks), load8(vr + 16 * ks), dp);
-    }
-    // P and dS; position e of the accumulator is tile row 8(e/4) + 4h + e%4
-    f32x16 pm, dsm;
+      for (int mt = 0; mt < BK / 32; ++mt)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int rr = 8 * (e / 4) + 4 * half + (e % 4);
-      const int pos = row_pos[rr];
-      const float p = (pos >= 0 && my_key <= pos) ? exp2_fast(fmaf(s[e], a.c_log2, -row_lse2[rr])) : 0.f;
-      pm[e] = p;
-      dsm[e] = p * (dp[e] - row_d[rr]);
-    }
-    // dV += P^T dO, dK += dS^T Q: A from the accumulators, B from the transposed tile
+        for (int aa = 0; aa < 2; ++aa) {
+          const frag_t<T> ka = vt_frag_at<T, D, BK>(lds + X::KT_OFF, c, mt, aa, half);
+          const int k0 = 32 * mt + 16 * aa + 4 * half;
+          const typename Pack4<T>::type lo = *reinterpret_cast<const typename Pack4<T>::type*>(srow + k0);
+          const typename Pack4<T>::type hi = *reinterpret_cast<const typename Pack4<T>::type*>(srow + k0 + 8);
+          frag_t<T> sb;
 #pragma unroll
-    for (int aa = 0; aa < 2; ++aa) {
-      frag_t<T> pa, sa;
+          for (int e = 0; e < 4; ++e) {
+            sb[e] = lo[e];
+            sb[4 + e] = hi[e];
+          }
+          mma(ka, sb, o);
+        }
+      if (my_pos >= 0) {
+        // o[e]: d = 32 w + 8(e/4) + 4h + e%4 of row lane%32
+        T* dst = static_cast<T*>(a.dq_part) + my_prow * D + 32 * wave + 4 * half;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pa[e] = from_f32<T>(pm[8 * aa + e]);
-        sa[e] = from_f32<T>(dsm[8 * aa + e]);
-      }
+        for (int i = 0; i < 4; ++i) {
+          typename Pack4<T>::type w;
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        mma(pa, tile_t_frag<T, D, BK>(lds + X::DOT_OFF, 32 * dt + (lane & 31), aa, half), dvacc[dt]);
-        mma(sa, tile_t_frag<T, D, BK>(lds + X::QT_OFF, 32 * dt + (lane & 31), aa, half), dkacc[dt]);
+          for (int e = 0; e < 4; ++e) w[e] = from_f32<T>(o[4 * i + e] * a.scale);
+          *reinterpret_cast<typename Pack4<T>::type*>(dst + 8 * i) = w;
+        }
       }
     }
+    __syncthreads();  // the next tile's rows are in LDS; dS is no longer read
   }
   if (!has_keys) return;
   // Partials of this item: lane holds key 32w + 8(e/4) + 4h + e%4, d = 32 dt + lane%32.
@@ -416,6 +341,40 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkdv(BwdArgs a) {
       dst[key * D + d] = dkacc[dt][e] * a.scale;
       dst[BK * D + key * D + d] = dvacc[dt][e];
     }
+}
+
+// ---- dq = sum of the slot partials, in slot order ---------------------------
+template <typename T, int D>
+__global__ void __launch_bounds__(256) k_bwd_dq_sum(const T* __restrict__ part, const int32_t* __restrict__ ids,
+                                                    T* __restrict__ dq, int Nq, int Hq, int Hkv, int G, int topk,
+                                                    int64_t nrows) {
+  constexpr int LPR = D / 8;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * (64 / LPR) + lane / LPR;  // (b, i, h)
+  if (row >= nrows) return;
+  const int h = (int)(row % Hq);
+  const int64_t bi = row / Hq;
+  const int32_t* sel = ids + (bi * Hkv + h / G) * topk;
+  const T* p = part + row * topk * D + (lane % LPR) * 8;
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int s = 0; s < topk; ++s) {
+    if (sel[s] < 0) continue;
+    const frag_t<T> x = load8(p + (int64_t)s * D);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += to_f32(x[e]);
+  }
+  frag_t<T> o;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = from_f32<T>(acc[e]);
+  T* dst = dq + row * D + (lane % LPR) * 8;
+  if constexpr (sizeof(T) == 2) {
+    *reinterpret_cast<frag_t<T>*>(dst) = o;
+  } else {
+    *reinterpret_cast<f32x4*>(dst) = f32x4{o[0], o[1], o[2], o[3]};
+    *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[4], o[5], o[6], o[7]};
+  }
 }
 
 // ---- dk, dv = sum of the item partials of each block, in item order ---------
@@ -472,21 +431,18 @@ __global__ void __launch_bounds__(256) k_bwd_dkdv_reduce(const float* __restrict
 
 template <typename T, int D, int BK>
 void bwd_launch_bk(const Shape& s, const BwdArgs& a, const InvertPlan& p, const void* ids, void* dq, void* dk, void* dv,
-                   hipStream_t st, int kid_dq, int kid_sum, int kid_dkdv, int kid_red) {
+                   hipStream_t st, int kid_main, int kid_sum, int kid_red) {
   const dim3 grid(p.items_cap, s.B * s.Hkv);
-  prof_begin(st, kid_dq);
-  hipLaunchKernelGGL((k_bwd_dq<T, D, BK>), grid, dim3(256), 0, st, a);
-  prof_end(st, kid_dq);
+  prof_begin(st, kid_main);
+  hipLaunchKernelGGL((k_bwd_fused<T, D, BK>), grid, dim3(256), 0, st, a);
+  prof_end(st, kid_main);
   const int64_t nrows = (int64_t)s.B * s.Nq * s.Hq;
   const int rpb = 4 * (64 / (D / 8));
   prof_begin(st, kid_sum);
-  hipLaunchKernelGGL((k_bwd_dq_sum<T, D>), dim3((unsigned)((nrows + rpb - 1) / rpb)), dim3(256), 0, st, a.dq_part,
-                     static_cast<const int32_t*>(ids), static_cast<T*>(dq), s.Nq, s.Hq, s.Hkv, s.Hq / s.Hkv, s.topk,
-                     nrows);
+  hipLaunchKernelGGL((k_bwd_dq_sum<T, D>), dim3((unsigned)((nrows + rpb - 1) / rpb)), dim3(256), 0, st,
+                     static_cast<const T*>(a.dq_part), static_cast<const int32_t*>(ids), static_cast<T*>(dq), s.Nq,
+                     s.Hq, s.Hkv, s.Hq / s.Hkv, s.topk, nrows);
   prof_end(st, kid_sum);
-  prof_begin(st, kid_dkdv);
-  hipLaunchKernelGGL((k_bwd_dkdv<T, D, BK>), grid, dim3(256), 0, st, a);
-  prof_end(st, kid_dkdv);
   const int64_t nthr = (int64_t)s.nblk * BK * (D / 8);
   prof_begin(st, kid_red);
   hipLaunchKernelGGL((k_bwd_dkdv_reduce<T, D, BK>), dim3((unsigned)((nthr + 255) / 256), s.B * s.Hkv), dim3(256), 0,
@@ -497,10 +453,10 @@ void bwd_launch_bk(const Shape& s, const BwdArgs& a, const InvertPlan& p, const 
 
 template <typename T, int D>
 void bwd_launch(const Shape& s, const BwdArgs& a, const InvertPlan& p, const void* ids, void* dq, void* dk, void* dv,
-                hipStream_t st, int k1, int k2, int k3, int k4) {
-  if (s.Bk == 32) bwd_launch_bk<T, D, 32>(s, a, p, ids, dq, dk, dv, st, k1, k2, k3, k4);
-  else if (s.Bk == 64) bwd_launch_bk<T, D, 64>(s, a, p, ids, dq, dk, dv, st, k1, k2, k3, k4);
-  else bwd_launch_bk<T, D, 128>(s, a, p, ids, dq, dk, dv, st, k1, k2, k3, k4);
+                hipStream_t st, int k1, int k2, int k3) {
+  if (s.Bk == 32) bwd_launch_bk<T, D, 32>(s, a, p, ids, dq, dk, dv, st, k1, k2, k3);
+  else if (s.Bk == 64) bwd_launch_bk<T, D, 64>(s, a, p, ids, dq, dk, dv, st, k1, k2, k3);
+  else bwd_launch_bk<T, D, 128>(s, a, p, ids, dq, dk, dv, st, k1, k2, k3);
 }
 
 }  // namespace
@@ -529,12 +485,11 @@ hipError_t launch_bwd_rowdot(const Shape& s, const void* out, const void* dout, 
 
 hipError_t launch_bwd_attention(const Shape& s, const InvertPlan& p, const void* q, const void* k, const void* v,
                                 const void* dout, const float* lse, const float* drow, const int32_t* ids,
-                                const InvertOut& inv, float* dq_part, float* dkv_part, void* trash, void* dq, void* dk,
+                                const InvertOut& inv, void* dq_part, float* dkv_part, void* trash, void* dq, void* dk,
                                 void* dv, hipStream_t st) {
-  static const int k1 = prof_register("bwd_dq");
+  static const int k1 = prof_register("bwd_fused");
   static const int k2 = prof_register("bwd_dq_sum");
-  static const int k3 = prof_register("bwd_dkdv");
-  static const int k4 = prof_register("bwd_dkdv_reduce");
+  static const int k3 = prof_register("bwd_dkdv_reduce");
   BwdArgs a;
   a.q = q;
   a.k = k;
@@ -561,11 +516,11 @@ hipError_t launch_bwd_attention(const Shape& s, const InvertPlan& p, const void*
   a.scale = s.scale;
   a.c_log2 = s.scale * kLog2e;
   if (s.dtype == kBF16) {
-    if (s.D == 64) bwd_launch<bf16_t, 64>(s, a, p, ids, dq, dk, dv, st, k1, k2, k3, k4);
-    else bwd_launch<bf16_t, 128>(s, a, p, ids, dq, dk, dv, st, k1, k2, k3, k4);
+    if (s.D == 64) bwd_launch<bf16_t, 64>(s, a, p, ids, dq, dk, dv, st, k1, k2, k3);
+    else bwd_launch<bf16_t, 128>(s, a, p, ids, dq, dk, dv, st, k1, k2, k3);
   } else {
-    if (s.D == 64) bwd_launch<float, 64>(s, a, p, ids, dq, dk, dv, st, k1, k2, k3, k4);
-    else bwd_launch<float, 128>(s, a, p, ids, dq, dk, dv, st, k1, k2, k3, k4);
+    if (s.D == 64) bwd_launch<float, 64>(s, a, p, ids, dq, dk, dv, st, k1, k2, k3);
+    else bwd_launch<float, 128>(s, a, p, ids, dq, dk, dv, st, k1, k2, k3);
   }
   return hipGetLastError();
 }

@@ -165,23 +165,6 @@ struct KlLds {
   static_assert(HC_FIT >= 1, "LDS budget");
 };
 
-// A fragment of a transposed 32-entry tile for k-step a: row c, entries
-// 16a + 4h + [0..3] and 16a + 8 + 4h + [0..3] (the accumulator order).
-template <typename T, int TPITCH>
-__device__ __forceinline__ frag_t<T> entries_t_frag(const char* base, int c, int a, int half) {
-  const T* row = reinterpret_cast<const T*>(base + c * TPITCH);
-  const int r0 = 16 * a + 4 * half;
-  const typename Pack4<T>::type lo = *reinterpret_cast<const typename Pack4<T>::type*>(row + r0);
-  const typename Pack4<T>::type hi = *reinterpret_cast<const typename Pack4<T>::type*>(row + r0 + 8);
-  frag_t<T> f;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    f[e] = lo[e];
-    f[4 + e] = hi[e];
-  }
-  return f;
-}
-
 template <typename T, int D, int DI, int BK>
 __global__ void __launch_bounds__(256, 1) k_kl_main(KlArgs a) {
   using X = KlLds<T, D, DI, BK>;
@@ -331,7 +314,7 @@ __global__ void __launch_bounds__(256, 1) k_kl_main(KlArgs a) {
         for (int e = 0; e < 8; ++e) ga[e] = from_f32<T>(gs[8 * aa + e]);
 #pragma unroll
         for (int dt = 0; dt < DI / 32; ++dt)
-          mma(ga, entries_t_frag<T, X::TPITCH>(lds + X::IQT_OFF, 32 * dt + (lane & 31), aa, half), dik[dt]);
+          mma(ga, tile_t_frag<T, X::TPITCH>(lds + X::IQT_OFF, 32 * dt + (lane & 31), aa, half), dik[dt]);
       }
     }
     __syncthreads();  // g and the KL partials of every wave are in LDS

@@ -156,7 +156,7 @@ BwdLayout bwd_layout(const msa::Shape& s) {
   L.inv_scratch = off;
   off += align_up(msa::invert_ws_bytes(s, p));
   L.dq_part = off;
-  off += align_up(rows * s.topk * s.D * 4);
+  off += align_up(rows * s.topk * s.D * elem_bytes(s));
   L.dkv_part = off;
   off += align_up(msa::bwd_dkv_bytes(s, p));
   L.trash = off;
@@ -447,7 +447,7 @@ msa_status_t msa_sparse_attention_backward(const msa_problem_t* prob, const void
   if (e == hipSuccess) e = msa::launch_invert(s, plan, block_ids, 0, s.Nq, inv, w + L.inv_scratch, st);
   if (e == hipSuccess)
     e = msa::launch_bwd_attention(s, plan, q, k, v, dout, lse, drow, block_ids, inv,
-                                  reinterpret_cast<float*>(w + L.dq_part), reinterpret_cast<float*>(w + L.dkv_part),
+                                  w + L.dq_part, reinterpret_cast<float*>(w + L.dkv_part),
                                   w + L.trash, dq, dk, dv, st);
   return e == hipSuccess ? MSA_OK : hip_fail(e);
 }

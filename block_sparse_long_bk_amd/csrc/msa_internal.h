@@ -98,11 +98,11 @@ hipError_t launch_combine(const Shape& s, int q0, int nq, const Partials& part, 
 hipError_t launch_bwd_rowdot(const Shape& s, const void* out, const void* dout, float* drow, hipStream_t st);
 // Bytes of the per-work-item fp32 dk/dv partials.
 size_t bwd_dkv_bytes(const Shape& s, const InvertPlan& p);
-// dq (via per-(row, slot) fp32 partials, [B, Nq, Hq, topk, D]) and dk, dv (via
-// per-item fp32 partials) for the work items of `inv` (whole problem, q0 = 0).
+// dq (via per-(row, slot) partials in the input type, [B, Nq, Hq, topk, D])
+// and dk, dv (via per-item fp32 partials) for the work items of `inv` (whole problem, q0 = 0).
 hipError_t launch_bwd_attention(const Shape& s, const InvertPlan& p, const void* q, const void* k, const void* v,
                                 const void* dout, const float* lse, const float* drow, const int32_t* ids,
-                                const InvertOut& inv, float* dq_part, float* dkv_part, void* trash, void* dq, void* dk,
+                                const InvertOut& inv, void* dq_part, float* dkv_part, void* trash, void* dq, void* dk,
                                 void* dv, hipStream_t st);
 
 // Index-Branch alignment loss -----------------------------------------------

@@ -124,3 +124,43 @@ def test_indexer_kl_is_deterministic():
     b = run_kl(wl, x, ids)
     for u, w, nm in zip(a, b, ("kl", "d_iq", "d_ik")):
         assert torch.equal(u.view(torch.uint8), w.view(torch.uint8)), nm
+
+
+def test_indexer_kl_full_size_prefill_32k():
+    """The prefill shape (32k tokens, Hq 64, Hkv 8, d = d_idx = 128, k 16,
+    bf16), whole problem in one call.  Checked against the oracle on a sample
+    of query rows (kl, d_iq) and on the last key block of every group (d_ik:
+    only the last Bk queries can select it, all of them sampled), with the
+    oracle's selection substituted for those rows.  Over all rows: kl >= 0,
+    and sum_t d_ik_t vanishes per group (sum_t (pi - pm) = 0 for every row)."""
+    wl = inputs.WORKLOADS["prefill_32k"]
+    print(f"[{wl.name}] generating", flush=True)
+    x = inputs.generate(wl, device="cuda")
+    p = api.problem_of(wl)
+    ids = api.index_topk(p, x["iq"], x["ik"])
+    Bk, N = wl.block_size, wl.n_q
+    last0 = (wl.nblk - 1) * Bk
+    qi = np.unique(np.concatenate([np.linspace(0, last0 - 1, 24).astype(np.int64), np.arange(last0, N)]))
+    rows = np.stack([np.zeros_like(qi), qi], axis=1)
+    prob = O.problem_of(wl)
+    hx = {k: host(v) for k, v in x.items()}
+    s = O.block_scores(prob, hx["iq"], hx["ik"], rows)
+    ids_o = O.select(prob, s, rows)
+    ids[0, qi] = torch.from_numpy(ids_o).cuda()
+    _, lse = api.sparse_attention(p, x["q"], x["k"], x["v"], ids)
+    kl, d_iq, d_ik = api.indexer_kl(p, x["q"], x["k"], x["iq"], x["ik"], lse, ids, loss_scale=LOSS_SCALE)
+    torch.cuda.synchronize()
+    print(f"[{wl.name}] GPU loss done", flush=True)
+    rkl, riq, rik = O.indexer_kl(prob, hx["q"], hx["k"], hx["iq"], hx["ik"], ids_o, rows=rows, loss_scale=LOSS_SCALE)
+    print(f"[{wl.name}] oracle done", flush=True)
+    got = host(kl[0, qi]).numpy().astype(np.float64)
+    err = float(np.max(np.abs(got - rkl)))
+    assert err <= 1e-4 * float(np.max(rkl)) + 1e-6, f"kl: max-abs {err:.3e}"
+    e_q = check(wl.dtype, d_iq[0, qi], riq, "d_iq (sampled rows)")
+    e_k = check(wl.dtype, d_ik[0, last0:], rik[0, last0:], "d_ik (last block)")
+    kmin = float(kl.min())
+    dsum = d_ik.double().sum(dim=1)
+    rel = float(dsum.norm() / d_ik.double().abs().sum(dim=1).norm())
+    print(f"[{wl.name}] kl max-abs {err:.2e}, d_iq {e_q}, d_ik {e_k}, min kl {kmin:.2e}, "
+          f"|sum d_ik| / sum |d_ik| {rel:.2e}", flush=True)
+    assert kmin >= -1e-5 and rel <= 1e-2
