@@ -133,9 +133,9 @@ def test_workspace_sizes():
     assert inv == inv_least > 0
     inv_pre, _ = api.workspace_size(pre, api.OP_INVERT)
     assert inv_pre >= 8 * 256 * 4  # at least one count per (group, block)
-    # backward: fp32 dq partials per (query, head, slot) dominate
+    # backward: dq partials per (query, head, slot) in the input type dominate
     bwd, bwd_least = api.workspace_size(pre, api.OP_BACKWARD)
-    assert bwd == bwd_least >= 32768 * 64 * 16 * 128 * 4
+    assert bwd == bwd_least >= 32768 * 64 * 16 * 128 * 2
     # indexer loss: fp32 d_iq partials per (query, group, slot)
     klw, klw_least = api.workspace_size(pre, api.OP_INDEXER_KL)
     assert klw == klw_least >= 32768 * 8 * 16 * 128 * 4
