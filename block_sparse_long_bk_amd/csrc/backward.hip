@@ -105,8 +105,6 @@ struct TileStage {
   // longer overlap the current tile's products.
   u32x4 v[NT][4];
   float lse[4], dr[4];
-  int pos[4];
-  int64_t prow[4];
   uint32_t valid_mask;
 
   __device__ __forceinline__ void load(const BwdArgs& a, const int32_t* ent_lds, int tile, int nrows, int b, int g,
@@ -131,15 +129,16 @@ struct TileStage {
         if (u == 0 && tensor == 0 && col == 0) {
           lse[r] = a.lse[rowi];
           dr[r] = a.drow[rowi];
-          pos[r] = valid ? (int)min(a.q_offset + t.qq, (int64_t)a.Nk - 1) : -1;
-          prow[r] = rowi * a.topk + t.slot;
         }
       }
     }
   }
 
+  // Row positions and partial rows are recomputed here from the entries
+  // rather than held in registers across the products.
   template <int BK>
-  __device__ __forceinline__ void store(char* lds, float* row_lse2, float* row_d, int* row_pos, int64_t* row_prow,
+  __device__ __forceinline__ void store(const BwdArgs& a, const int32_t* ent_lds, int tile, int b, int g, char* lds,
+                                        float* row_lse2, float* row_d, int* row_pos, int64_t* row_prow,
                                         int tid) const {
     using X = FusedLds<T, D, BK>;
 #pragma unroll
@@ -175,19 +174,31 @@ struct TileStage {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const bool ok = (valid_mask >> r) & 1;
+          const int rr = tile * 32 + 4 * rg + r;
+          const TileRows t = rows_of(ok ? ent_lds[rr >> a.gshift] : ent_lds[0], ok, rr, a.gshift, a.topk,
+                                     a.topk_magic, g);
           row_lse2[4 * rg + r] = ok ? lse[r] * kLog2e : 0.f;
           row_d[4 * rg + r] = ok ? dr[r] : 0.f;
-          row_pos[4 * rg + r] = pos[r];
-          row_prow[4 * rg + r] = prow[r];
+          row_pos[4 * rg + r] = ok ? (int)min(a.q_offset + t.qq, (int64_t)a.Nk - 1) : -1;
+          row_prow[4 * rg + r] = (((int64_t)b * a.Nq + t.qq) * a.Hq + t.h) * a.topk + t.slot;
         }
       }
     }
   }
 };
 
-template <typename T, int D, int BK>
-__global__ void __launch_bounds__(256, 1) k_bwd_fused(BwdArgs a) {
+// NW = 4: wave w owns keys [32w, 32w+32) and all of d.  NW = 8: waves w and
+// w+4 share keys [32(w%4), +32) -- both form S and dP for them, each keeps dK
+// and dV for half of d -- so that two waves per SIMD hide each other's
+// latencies (at 2x the S and dP products); waves 4..7 also stage the next
+// tile while waves 0..3 form dQ.
+template <typename T, int D, int BK, int NW>
+__global__ void __launch_bounds__(NW * 64, 1) k_bwd_fused(BwdArgs a) {
   using X = FusedLds<T, D, BK>;
+  constexpr int NTHR = NW * 64;
+  constexpr int DSPLIT = NW / 4;          // waves per key group
+  constexpr int DT = D / 32 / DSPLIT;     // dK / dV accumulator tiles per wave
+  constexpr int STG0 = NW == 8 ? 256 : 0;  // first staging thread
   __shared__ __attribute__((aligned(16))) char lds[X::BYTES];
   __shared__ int32_t ent_lds[kMaxItemEntries];
   __shared__ __attribute__((aligned(16))) float row_lse2[32];
@@ -206,19 +217,22 @@ __global__ void __launch_bounds__(256, 1) k_bwd_fused(BwdArgs a) {
   const int nrows = (e1 - e0) * a.G;
   const int nent = e1 - e0;
   const int32_t* ent = a.entries + (int64_t)bg * a.Nq * a.topk + e0;
-  for (int u = tid; u < nent; u += 256) ent_lds[u] = ent[u];
+  for (int u = tid; u < nent; u += NTHR) ent_lds[u] = ent[u];
 
   const int64_t tok_stride = (int64_t)a.Hkv * D;
   const T* kb = static_cast<const T*>(a.k) + (int64_t)b * a.Nk * tok_stride + g * D;
   const T* vb = static_cast<const T*>(a.v) + (int64_t)b * a.Nk * tok_stride + g * D;
-  {
+  if (tid < 256) {
     KvStage<T, D, BK> st;
     st.load_v(kb, tok_stride, j, a.Nk, tid);
     st.store_vt(lds + X::KT_OFF, tid);
   }
+  const int kg = wave % 4, dh = wave / 4;  // key group, half of d (NW = 8)
+  const bool stager = tid >= STG0 && tid < STG0 + 256;
+  const int stid = tid - STG0;
   const int64_t key0 = (int64_t)j * BK;
-  const bool has_keys = wave * 32 < BK;  // waves past the block's keys stage and form dQ only
-  const int kk = wave * 32 + (lane & 31);
+  const bool has_keys = kg * 32 < BK;  // waves past the block's keys stage and form dQ only
+  const int kk = kg * 32 + (lane & 31);
   const int64_t my_key = key0 + kk;
   const int64_t kt = min(my_key, (int64_t)a.Nk - 1);  // keys past n_k are masked below
   frag_t<T> kf[D / 16], vf[D / 16];
@@ -227,16 +241,18 @@ __global__ void __launch_bounds__(256, 1) k_bwd_fused(BwdArgs a) {
     kf[ks] = load8(kb + kt * tok_stride + 8 * half + 16 * ks);
     vf[ks] = load8(vb + kt * tok_stride + 8 * half + 16 * ks);
   }
-  f32x16 dkacc[D / 32], dvacc[D / 32];
+  f32x16 dkacc[DT], dvacc[DT];
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) {
+  for (int dt = 0; dt < DT; ++dt) {
     dkacc[dt] = f32x16{};
     dvacc[dt] = f32x16{};
   }
   __syncthreads();  // ent_lds
   TileStage<T, D> stg;
-  stg.load(a, ent_lds, 0, nrows, b, g, tid);
-  stg.template store<BK>(lds, row_lse2, row_d, row_pos, row_prow, tid);
+  if (stager) {
+    stg.load(a, ent_lds, 0, nrows, b, g, stid);
+    stg.template store<BK>(a, ent_lds, 0, b, g, lds, row_lse2, row_d, row_pos, row_prow, stid);
+  }
   // Every load so far (the key rows included) has landed: without this the
   // compiler's wait before the first use of kf / vf inside the loop also
   // covers the next tile's fetch, which would then no longer overlap.
@@ -246,7 +262,7 @@ __global__ void __launch_bounds__(256, 1) k_bwd_fused(BwdArgs a) {
   const int ntiles = (nrows + 31) / 32;
   for (int tile = 0; tile < ntiles; ++tile) {
     const bool more = tile + 1 < ntiles;
-    if (more) stg.load(a, ent_lds, tile + 1, nrows, b, g, tid);
+    if (more && stager) stg.load(a, ent_lds, tile + 1, nrows, b, g, stid);
     const int my_pos = row_pos[lane & 31];
     const int64_t my_prow = row_prow[lane & 31];
     if (has_keys) {
@@ -273,7 +289,8 @@ __global__ void __launch_bounds__(256, 1) k_bwd_fused(BwdArgs a) {
           const float p = my_key <= pp[c] ? exp2_fast(fmaf(s[e], a.c_log2, -l4[c])) : 0.f;
           s[e] = p;
           dp[e] = p * (dp[e] - d4[c]);
-          *reinterpret_cast<T*>(lds + X::DS_OFF + (r0 + c) * X::SPITCH + kk * (int)sizeof(T)) = from_f32<T>(dp[e]);
+          if (dh == 0)
+            *reinterpret_cast<T*>(lds + X::DS_OFF + (r0 + c) * X::SPITCH + kk * (int)sizeof(T)) = from_f32<T>(dp[e]);
         }
       }
       // dV += P^T dO, dK += dS^T Q
@@ -286,14 +303,15 @@ __global__ void __launch_bounds__(256, 1) k_bwd_fused(BwdArgs a) {
           sa[e] = from_f32<T>(dp[8 * aa + e]);
         }
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          mma(pa, tile_t_frag<T, X::TPITCH>(lds + X::DOT_OFF, 32 * dt + (lane & 31), aa, half), dvacc[dt]);
-          mma(sa, tile_t_frag<T, X::TPITCH>(lds + X::QT_OFF, 32 * dt + (lane & 31), aa, half), dkacc[dt]);
+        for (int i = 0; i < DT; ++i) {
+          const int c = 32 * (dh * DT + i) + (lane & 31);
+          mma(pa, tile_t_frag<T, X::TPITCH>(lds + X::DOT_OFF, c, aa, half), dvacc[i]);
+          mma(sa, tile_t_frag<T, X::TPITCH>(lds + X::QT_OFF, c, aa, half), dkacc[i]);
         }
       }
     }
     __syncthreads();  // dS complete; the tile's rows are no longer read
-    if (more) stg.template store<BK>(lds, row_lse2, row_d, row_pos, row_prow, tid);
+    if (more && stager) stg.template store<BK>(a, ent_lds, tile + 1, b, g, lds, row_lse2, row_d, row_pos, row_prow, stid);
     if (wave < D / 32) {
       // dQ^T[c][row] = sum over the block's keys of K^T[c][key] dS^T[key][row]
       f32x16 o = f32x16{};
@@ -330,16 +348,17 @@ __global__ void __launch_bounds__(256, 1) k_bwd_fused(BwdArgs a) {
     __syncthreads();  // the next tile's rows are in LDS; dS is no longer read
   }
   if (!has_keys) return;
-  // Partials of this item: lane holds key 32w + 8(e/4) + 4h + e%4, d = 32 dt + lane%32.
+  // Partials of this item: lane holds key 32 kg + 8(e/4) + 4h + e%4,
+  // d = 32 (dh DT + i) + lane%32.
   float* dst = a.dkv_part + ((int64_t)bg * a.items_cap + item) * 2 * BK * D;
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
+  for (int i = 0; i < DT; ++i)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int key = wave * 32 + 8 * (e / 4) + 4 * half + (e % 4);
-      const int d = 32 * dt + (lane & 31);
-      dst[key * D + d] = dkacc[dt][e] * a.scale;
-      dst[BK * D + key * D + d] = dvacc[dt][e];
+      const int key = kg * 32 + 8 * (e / 4) + 4 * half + (e % 4);
+      const int d = 32 * (dh * DT + i) + (lane & 31);
+      dst[key * D + d] = dkacc[i][e] * a.scale;
+      dst[BK * D + key * D + d] = dvacc[i][e];
     }
 }
 
@@ -434,7 +453,9 @@ void bwd_launch_bk(const Shape& s, const BwdArgs& a, const InvertPlan& p, const 
                    hipStream_t st, int kid_main, int kid_sum, int kid_red) {
   const dim3 grid(p.items_cap, s.B * s.Hkv);
   prof_begin(st, kid_main);
-  hipLaunchKernelGGL((k_bwd_fused<T, D, BK>), grid, dim3(256), 0, st, a);
+  // Eight waves where two per SIMD fit in the registers (16-bit inputs).
+  constexpr int NW = sizeof(T) == 2 ? 8 : 4;
+  hipLaunchKernelGGL((k_bwd_fused<T, D, BK, NW>), grid, dim3(NW * 64), 0, st, a);
   prof_end(st, kid_main);
   const int64_t nrows = (int64_t)s.B * s.Nq * s.Hq;
   const int rpb = 4 * (64 / (D / 8));
