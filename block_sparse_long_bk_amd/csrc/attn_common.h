@@ -78,12 +78,16 @@ struct KvStage {
 
   // V^T rows get four consecutive keys per store.
   __device__ __forceinline__ void store(char* lds, int tid) const {
+    store_k(lds, tid);
+    store_vt(lds + L::KBYTES, tid);
+  }
+  // The key rows alone, at lds (BK rows of KPITCH bytes).
+  __device__ __forceinline__ void store_k(char* lds, int tid) const {
 #pragma unroll
     for (int u = 0; u < KLD; ++u) {
       const int c = tid + u * 256;
       if (c < KCH) *reinterpret_cast<u32x4*>(lds + (c / CPR) * L::KPITCH + (c % CPR) * 16) = kr[u];
     }
-    store_vt(lds + L::KBYTES, tid);
   }
   // The transposed rows alone, at vt (D rows of VPITCH bytes).
   __device__ __forceinline__ void store_vt(char* vt, int tid) const {

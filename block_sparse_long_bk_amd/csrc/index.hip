@@ -149,14 +149,6 @@ __device__ __forceinline__ frag_t<T> dma_frag(const char* buf, int r, int e) {
   }
 }
 
-// s_waitcnt immediate: wait until at most n vector-memory operations of this
-// wave are outstanding (expcnt and lgkmcnt left at their maximum).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
 template <typename T, int DI, int NT, int KMAX, bool WRITE_S, bool TOPK, bool MX>
 __global__ void __launch_bounds__(kTileWaves * 64) k_index_tile(TileArgs a) {
   constexpr int WAVES = kTileWaves;

@@ -76,14 +76,9 @@ __global__ void __launch_bounds__(256) k_kl_lse(KlArgs a) {
   const int64_t tok_stride = (int64_t)a.Hkv * DI;
   const T* ikb = static_cast<const T*>(a.ik) + (int64_t)b * a.Nk * tok_stride + g * DI;
   {
-    constexpr int CPR = DI * (int)sizeof(T) / 16;
-    for (int c = tid; c < BK * CPR; c += 256) {
-      const int row = c / CPR, col = c % CPR;
-      const int64_t t = (int64_t)j * BK + row;
-      u32x4 v = u32x4{};
-      if (t < a.Nk) v = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(ikb + t * tok_stride) + col * 16);
-      *reinterpret_cast<u32x4*>(lds + row * L::KPITCH + col * 16) = v;
-    }
+    KvStage<T, DI, BK> st;  // all loads issued before the stores
+    st.load_k(ikb, tok_stride, j, a.Nk, tid);
+    st.store_k(lds, tid);
   }
   __syncthreads();
   const int64_t key0 = (int64_t)j * BK;
@@ -162,6 +157,8 @@ struct KlLds {
   static constexpr int HC_FIT = (BUDGET - FIXED) / (32 * QPITCH);
   static constexpr int HC = HC_FIT >= 8 ? 8 : HC_FIT >= 4 ? 4 : HC_FIT >= 2 ? 2 : 1;  // heads per staged chunk
   static constexpr int BYTES = Q_OFF + HC * 32 * QPITCH;
+  static constexpr int TPM = BK * 4 + 16;  // a row of fp32 KL terms, kept in the query-row area
+  static_assert(HC * 32 * QPITCH >= 32 * TPM, "KL terms fit in the query-row area");
   static_assert(HC_FIT >= 1, "LDS budget");
 };
 
@@ -171,9 +168,10 @@ __global__ void __launch_bounds__(256, 1) k_kl_main(KlArgs a) {
   constexpr int HC = X::HC;
   __shared__ __attribute__((aligned(16))) char lds[X::BYTES];
   __shared__ int32_t ent_lds[kMaxItemEntries];
-  __shared__ float row_lse_s[32], klw[4][32];
-  __shared__ int row_pos[32], row_q[32], row_slot[32];  // row_pos -1 past the item's end
-  __shared__ float row_lsm[HC][32];                      // Main Branch lse * log2(e) per (head, entry)
+  __shared__ float row_lse_s[32];
+  __shared__ __attribute__((aligned(16))) int row_pos[32];  // -1 past the item's end
+  __shared__ int row_q[32], row_slot[32];
+  __shared__ __attribute__((aligned(16))) float row_lsm[HC][32];  // Main Branch lse * log2(e) per (head, entry)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
   const int bg = blockIdx.y, b = bg / a.Hkv, g = bg % a.Hkv;
   const int n = a.item_count[bg];
@@ -217,28 +215,47 @@ __global__ void __launch_bounds__(256, 1) k_kl_main(KlArgs a) {
 
   for (int tile = 0; tile * 32 < nent; ++tile) {
     __syncthreads();  // the previous tile's LDS is no longer read
-    for (int c = tid; c < 32 * ICPR; c += 256) {
-      const int rr = c / ICPR, col = c % ICPR;
-      const int r = tile * 32 + rr;
-      const bool valid = r < nent;
-      int qq, slot;
-      split_entry(valid ? ent_lds[r] : ent_lds[0], a.topk, a.topk_magic, qq, slot);
-      u32x4 v = *reinterpret_cast<const u32x4*>(
-          reinterpret_cast<const char*>(iqb + (((int64_t)b * a.Nq + qq) * a.Hkv + g) * DI) + col * 16);
-      if (!valid) v = u32x4{};
-      *reinterpret_cast<u32x4*>(lds + X::IQ_OFF + rr * X::IPITCH + col * 16) = v;
-      T el[16 / sizeof(T)];
-      __builtin_memcpy(el, &v, 16);
+    // All of a thread's loads are issued before any of them is used, so the
+    // tile costs one memory latency rather than one per chunk.  Rows past the
+    // item's end read entry 0 and store zeros.
+    {
+      constexpr int NI = (32 * ICPR + 255) / 256;
+      u32x4 v[NI];
+      float ls[NI];
 #pragma unroll
-      for (int e = 0; e < (int)(16 / sizeof(T)); ++e)
-        *reinterpret_cast<T*>(lds + X::IQT_OFF + (col * (16 / (int)sizeof(T)) + e) * X::TPITCH +
-                              rr * (int)sizeof(T)) = el[e];
-      if (col == 0) {
+      for (int u = 0; u < NI; ++u) {
+        const int c = tid + 256 * u;
+        const int rr = min(c / ICPR, 31), col = c % ICPR;
+        const int r = tile * 32 + rr;
+        int qq, slot;
+        split_entry(r < nent ? ent_lds[r] : ent_lds[0], a.topk, a.topk_magic, qq, slot);
         const int64_t row = ((int64_t)b * a.Nq + qq) * a.Hkv + g;
-        row_lse_s[rr] = valid ? a.lse_s[row] : 0.f;
-        row_pos[rr] = valid ? (int)min(a.q_offset + qq, (int64_t)a.Nk - 1) : -1;
-        row_q[rr] = qq;
-        row_slot[rr] = slot;
+        v[u] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(iqb + row * DI) + col * 16);
+        ls[u] = a.lse_s[row];
+      }
+#pragma unroll
+      for (int u = 0; u < NI; ++u) {
+        const int c = tid + 256 * u;
+        if (c >= 32 * ICPR) continue;
+        const int rr = c / ICPR, col = c % ICPR;
+        const int r = tile * 32 + rr;
+        const bool valid = r < nent;
+        const u32x4 w = valid ? v[u] : u32x4{};
+        *reinterpret_cast<u32x4*>(lds + X::IQ_OFF + rr * X::IPITCH + col * 16) = w;
+        T el[16 / sizeof(T)];
+        __builtin_memcpy(el, &w, 16);
+#pragma unroll
+        for (int e = 0; e < (int)(16 / sizeof(T)); ++e)
+          *reinterpret_cast<T*>(lds + X::IQT_OFF + (col * (16 / (int)sizeof(T)) + e) * X::TPITCH +
+                                rr * (int)sizeof(T)) = el[e];
+        if (col == 0) {
+          int qq, slot;
+          split_entry(valid ? ent_lds[r] : ent_lds[0], a.topk, a.topk_magic, qq, slot);
+          row_lse_s[rr] = valid ? ls[u] : 0.f;
+          row_pos[rr] = valid ? (int)min(a.q_offset + qq, (int64_t)a.Nk - 1) : -1;
+          row_q[rr] = qq;
+          row_slot[rr] = slot;
+        }
       }
     }
     __syncthreads();
@@ -253,17 +270,29 @@ __global__ void __launch_bounds__(256, 1) k_kl_main(KlArgs a) {
     for (int h0 = 0; h0 < a.G; h0 += HC) {
       const int hn = min(HC, a.G - h0);
       __syncthreads();  // the previous chunk's query rows are no longer read
-      for (int c = tid; c < hn * 32 * QCPR; c += 256) {
-        const int hr = c / QCPR, col = c % QCPR;  // hr = hl * 32 + rr
-        const int hl = hr >> 5, rr = hr & 31;
-        const int r = tile * 32 + rr;
-        const bool valid = r < nent;
-        const int qq = row_q[rr];
-        const int64_t qrow = ((int64_t)b * a.Nq + qq) * a.Hq + g * a.G + h0 + hl;
-        u32x4 v = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(qb + qrow * D) + col * 16);
-        if (!valid) v = u32x4{};
-        *reinterpret_cast<u32x4*>(lds + X::Q_OFF + hr * X::QPITCH + col * 16) = v;
-        if (col == 0) row_lsm[hl][rr] = valid ? a.lse[qrow] * kLog2e : 0.f;
+      {
+        constexpr int NQ = (HC * 32 * QCPR + 255) / 256;
+        u32x4 v[NQ];
+        float ls[NQ];
+#pragma unroll
+        for (int u = 0; u < NQ; ++u) {
+          const int c = min(tid + 256 * u, hn * 32 * QCPR - 1);
+          const int hr = c / QCPR, col = c % QCPR;  // hr = hl * 32 + rr
+          const int hl = hr >> 5, rr = hr & 31;
+          const int64_t qrow = ((int64_t)b * a.Nq + row_q[rr]) * a.Hq + g * a.G + h0 + hl;
+          v[u] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(qb + qrow * D) + col * 16);
+          ls[u] = a.lse[qrow];
+        }
+#pragma unroll
+        for (int u = 0; u < NQ; ++u) {
+          const int c = tid + 256 * u;
+          if (c >= hn * 32 * QCPR) continue;
+          const int hr = c / QCPR, col = c % QCPR;
+          const int hl = hr >> 5, rr = hr & 31;
+          const bool valid = tile * 32 + rr < nent;
+          *reinterpret_cast<u32x4*>(lds + X::Q_OFF + hr * X::QPITCH + col * 16) = valid ? v[u] : u32x4{};
+          if (col == 0) row_lsm[hl][rr] = valid ? ls[u] * kLog2e : 0.f;
+        }
       }
       __syncthreads();
       if (has_keys) {
@@ -272,15 +301,25 @@ __global__ void __launch_bounds__(256, 1) k_kl_main(KlArgs a) {
           f32x16 s = mma0(load8(qr), kf[0]);
 #pragma unroll
           for (int ks = 1; ks < D / 16; ++ks) mma(load8(qr + 16 * ks), kf[ks], s);
+          // masked positions: the exponent is clamped at 0 (visible ones never
+          // exceed it) so that the product with the 0/1 mask stays finite
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int rr = 8 * (e / 4) + 4 * half + (e % 4);
-            const bool vis = row_pos[rr] >= 0 && my_key <= row_pos[rr];
-            pm[e] += vis ? exp2_fast(fmaf(s[e], a.c_log2, -row_lsm[hl][rr])) : 0.f;
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int r0 = 8 * q4 + 4 * half;
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(&row_lsm[hl][r0]);
+            const int4 p4 = *reinterpret_cast<const int4*>(row_pos + r0);
+            const int pp[4] = {p4.x, p4.y, p4.z, p4.w};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const int e = 4 * q4 + c;
+              const float m = my_key <= pp[c] ? 1.f : 0.f;
+              pm[e] = fmaf(m, exp2_fast(fminf(fmaf(s[e], a.c_log2, -l4[c]), 0.f)), pm[e]);
+            }
           }
         }
       }
     }
+    __syncthreads();  // every wave is past the heads: the query-row area is free
     if (has_keys) {
       // per element: KL term and gradient; g to LDS as [entry][key]
       f32x16 gs;
@@ -296,16 +335,12 @@ __global__ void __launch_bounds__(256, 1) k_kl_main(KlArgs a) {
         gs[e] = vis ? a.loss_scale * (pi - p) : 0.f;
         *reinterpret_cast<T*>(lds + X::G_OFF + rr * X::GPITCH + kk * (int)sizeof(T)) = from_f32<T>(gs[e]);
       }
-      // KL partial per entry over this wave's 32 keys
+      // the per-element KL terms go to LDS as [entry][key] (fp32, in the
+      // query-row area, free once every wave is past the heads: the barrier
+      // above the element loop) and are summed per entry after the barrier
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-#pragma unroll
-        for (int m = 1; m < 32; m <<= 1) term[e] += xor_shfl(term[e], m);
-      }
-      if ((lane & 31) == 0) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) klw[wave][8 * (e / 4) + 4 * half + (e % 4)] = term[e];
-      }
+      for (int e = 0; e < 16; ++e)
+        *reinterpret_cast<float*>(lds + X::Q_OFF + (8 * (e / 4) + 4 * half + (e % 4)) * X::TPM + kk * 4) = term[e];
       // d ik[key][c] += sum over entries g^T[key][e] iq[e][c]
 #pragma unroll
       for (int aa = 0; aa < 2; ++aa) {
@@ -349,10 +384,22 @@ __global__ void __launch_bounds__(256, 1) k_kl_main(KlArgs a) {
               f32x4{o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]};
       }
     }
-    if (tid < 32 && row_pos[tid] >= 0) {
+    {
+      // KL partial per entry: 8 threads per entry, BK / 8 keys each, then a
+      // fixed-order combination of the 8 sums
+      const int rr = tid >> 3, part = tid & 7;
+      const float* trow = reinterpret_cast<const float*>(lds + X::Q_OFF + rr * X::TPM) + part * (BK / 8);
       float acc = 0.f;
-      for (int w = 0; w < 4 && w * 32 < BK; ++w) acc += klw[w][tid];
-      a.kl_part[(((int64_t)b * a.Nq + row_q[tid]) * a.Hkv + g) * a.topk + row_slot[tid]] = acc;
+#pragma unroll
+      for (int u = 0; u < BK / 8; u += 4) {
+        const f32x4 t4 = *reinterpret_cast<const f32x4*>(trow + u);
+        acc += (t4[0] + t4[1]) + (t4[2] + t4[3]);
+      }
+      acc += xor_shfl(acc, 1);
+      acc += xor_shfl(acc, 2);
+      acc += xor_shfl(acc, 4);
+      if (part == 0 && row_pos[rr] >= 0)
+        a.kl_part[(((int64_t)b * a.Nq + row_q[rr]) * a.Hkv + g) * a.topk + row_slot[rr]] = acc;
     }
   }
   if (!has_keys) return;

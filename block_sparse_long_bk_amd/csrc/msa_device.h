@@ -68,6 +68,16 @@ __device__ __forceinline__ float to_f32(float x) { return x; }
 
 // Hardware base-2 exponential / logarithm (v_exp_f32, v_log_f32).
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// s_waitcnt immediate: wait until at most N vector-memory operations of this
+// wave are outstanding (expcnt and lgkmcnt left at their maximum).  Loads
+// complete in issue order, so after it every load but the N most recent has
+// landed, whatever stores are still in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
 
 // Running max over 16 values as a chain of three-input maxima (v_max3_f32).
