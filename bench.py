@@ -1,14 +1,16 @@
 """Benchmark of the MSA forward hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill_32k]
-                    [--sched auto|kv_outer|q_outer] [--no-cpu] [--no-decode]
+                    [--sched auto|kv_outer|q_outer] [--no-cpu] [--no-decode] [--no-train]
 
 One step = msa_forward (index scores + Top-k, inversion, attention, combine)
 over one batch of the seeded synthetic workload, inputs already in HBM.
 Prints one JSON line.  ``value`` is effective TFLOP/s over the selected,
 unmasked tokens, 4*d per (query head, key), divided by the whole forward
 step time.  The decode leg (16 sequences x 1M cached tokens, one new token
-each) reports microseconds per generated token.  Per-kernel times come from
+each) reports microseconds per generated token.  The training legs time the
+Main Branch backward and the Index-Branch KL loss on the same workload and
+selection.  Per-kernel times come from
 hipEvents that libmsa records around each launch on the launch stream.
 """
 import argparse
@@ -160,9 +162,54 @@ def run_prefill(args):
     nbytes = attention_bytes(wl, ids)
     ms, wall_ms, kern = time_steps(step, args.steps, args.warmup)
     res = dict(wl=wl, x=x, ms=ms, wall_ms=wall_ms, kern=kern, fl_attn=fl_attn, fl_idx=fl_idx, ws=ws.numel(),
-               bytes=nbytes)
-    del ws, out, lse
+               bytes=nbytes, ids=ids, out=out, lse=lse)
+    del ws
     return res
+
+
+def run_training(args, r):
+    """The training-side kernels on the same workload and selection: the
+    Main Branch backward (msa_sparse_attention_backward) and the Index-Branch
+    KL loss with its gradients (msa_indexer_kl).  Effective TFLOP/s count the
+    products over the selected, unmasked tokens: backward 5 x 2d per (query
+    head, key) (S, dP, dV, dK, dQ); KL 2d per (query head, key) for the Main
+    Branch probabilities plus 4 x 2 d_idx per (query group, key) (index
+    scores twice, d iq, d ik)."""
+    wl, x, ids = r["wl"], r["x"], r["ids"]
+    p = api.problem_of(wl, sched=args.sched)
+    dout = inputs.generate(wl, device="cuda", tensors=("dout",))["dout"]
+    sel = selected_tokens(wl, ids)
+    G = wl.h_q // wl.h_kv
+    ws = api.alloc_workspace(p, api.OP_BACKWARD)
+    dq, dk, dv = torch.empty_like(x["q"]), torch.empty_like(x["k"]), torch.empty_like(x["v"])
+
+    def bwd():
+        api.sparse_attention_backward(p, x["q"], x["k"], x["v"], r["out"], r["lse"], dout, ids, dq, dk, dv, ws=ws)
+
+    bwd()
+    ms_b, _, kern_b = time_steps(bwd, max(3, args.steps // 2), 1)
+    fl_b = 10.0 * wl.d * G * sel
+    del ws, dq, dk, dv, dout
+    torch.cuda.empty_cache()
+    ws = api.alloc_workspace(p, api.OP_INDEXER_KL)
+    kl = torch.empty((wl.batch, wl.n_q, wl.h_kv), dtype=torch.float32, device="cuda")
+    d_iq, d_ik = torch.empty_like(x["iq"]), torch.empty_like(x["ik"])
+
+    def klstep():
+        api.indexer_kl(p, x["q"], x["k"], x["iq"], x["ik"], r["lse"], ids, 1.0, kl, d_iq, d_ik, ws=ws)
+
+    klstep()
+    ms_k, _, kern_k = time_steps(klstep, max(3, args.steps // 2), 1)
+    fl_k = (2.0 * wl.d * G + 8.0 * wl.d_idx) * sel
+    del ws, kl, d_iq, d_ik
+    torch.cuda.empty_cache()
+    return {
+        "backward": {"ms_per_step": ms_b, "effective_TFLOPs": fl_b / ms_b / 1e9, "tflops_per_step": fl_b / 1e12,
+                     "mfma_frac": fl_b / ms_b / 1e9 / PEAK_BF16_TFLOPS,
+                     "kernels_ms": {k: round(v[0], 4) for k, v in kern_b.items()}},
+        "indexer_kl": {"ms_per_step": ms_k, "effective_TFLOPs": fl_k / ms_k / 1e9, "tflops_per_step": fl_k / 1e12,
+                       "kernels_ms": {k: round(v[0], 4) for k, v in kern_k.items()}},
+    }
 
 
 def run_decode(args, idx_format="plain"):
@@ -248,6 +295,7 @@ def main():
     ap.add_argument("--sched", default="auto", choices=["auto", "kv_outer", "q_outer"])
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-train", action="store_true", help="skip the backward and indexer-loss legs")
     ap.add_argument("--cpu-sample", type=int, default=8192)
     ap.add_argument("--crossover", action="store_true",
                     help="also time both attention schedules on query chunks at the end of a 1M-token cache")
@@ -318,6 +366,10 @@ def main():
         line["index_TFLOPs"] = r["fl_idx"] / kern[it[0]][0] / 1e9
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(wl, r["x"], args.cpu_sample)
+    if not args.no_train:
+        # training-side kernels on the same workload (reported beside the
+        # forward figure, never as `value`)
+        line.update(run_training(args, r))
     del r
     torch.cuda.empty_cache()
     if args.crossover:
