@@ -21,6 +21,8 @@
 //    128-token block of all groups is one contiguous span), VALU dot products
 //    against the few index queries kept in LDS; writes block scores, which
 //    k_topk_rows then selects from.
+#include <type_traits>
+
 #include "msa_device.h"
 #include "msa_internal.h"
 
@@ -362,6 +364,9 @@ __global__ void __launch_bounds__(kScanThreads) k_index_scan(ScanArgs a) {
       }
       __syncthreads();
     }
+    // Full chunks (all but possibly the last) skip the per-row liveness test.
+    auto sweep = [&](auto full_tag) {
+    constexpr bool FULL = decltype(full_tag)::value;
     for (int it0 = 0; it0 < iters; it0 += kScanUnroll) {
       frag_t<T> x[kScanUnroll];
       u32x4 xc[kScanUnroll];
@@ -369,7 +374,7 @@ __global__ void __launch_bounds__(kScanThreads) k_index_scan(ScanArgs a) {
 #pragma unroll
       for (int u = 0; u < kScanUnroll; ++u) {
         const int row = (it0 + u) * ROWS_IT + rsub;
-        const bool live = it0 + u < iters && row < ntok * H;
+        const bool live = it0 + u < iters && (FULL || row < ntok * H);
         if constexpr (MX) {
           xc[u] = u32x4{};
           xs[u] = 127;
@@ -410,6 +415,9 @@ __global__ void __launch_bounds__(kScanThreads) k_index_scan(ScanArgs a) {
         }
       }
     }
+    };
+    if (ntok == kChunk) sweep(std::true_type{});
+    else sweep(std::false_type{});
     __syncthreads();
     // max over the Bk tokens of each block of chunk j, for every (query, group):
     // lane l holds tokens l and 64 + l; blocks of 128 / 64 / 32 tokens are
