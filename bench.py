@@ -212,17 +212,21 @@ def run_training(args, r):
     }
 
 
-def run_decode(args, idx_format="plain"):
+def run_decode(args, idx_format="plain", kv_format="plain"):
     """decode_16x1m forward steps.  idx_format "mxfp8": the idx_k cache is
     quantised once (untimed) to MXFP8 by msa_mxfp8_quantize and the index scan
-    reads codes + scales (d_idx + d_idx/32 bytes per key) instead of bf16."""
+    reads codes + scales (d_idx + d_idx/32 bytes per key) instead of bf16;
+    kv_format "mxfp8": K and V too (d + d/32 bytes per key and tensor)."""
     wl = inputs.WORKLOADS["decode_16x1m"]
     x = inputs.generate(wl, device="cuda")
-    p = api.problem_of(wl, sched="auto", idx_format=idx_format)
+    p = api.problem_of(wl, sched="auto", idx_format=idx_format, kv_format=kv_format)
     ik = x["ik"]
     if idx_format == "mxfp8":
         ik = api.mxfp8_quantize(x["ik"])
         del x["ik"]
+    if kv_format == "mxfp8":
+        for t in ("k", "v"):
+            x[t] = api.mxfp8_quantize(x[t])
     ws = api.alloc_workspace(p, api.OP_FORWARD)
     ids = torch.empty((wl.batch, wl.n_q, wl.h_kv, wl.topk), dtype=torch.int32, device="cuda")
     out = torch.empty_like(x["q"])
@@ -241,12 +245,12 @@ def run_decode(args, idx_format="plain"):
     key_bytes = wl.d_idx + wl.d_idx // 32 if idx_format == "mxfp8" else wl.d_idx * e
     b_idx = wl.batch * L * wl.block_size * wl.h_kv * key_bytes
     sel = selected_tokens(wl, ids)
-    b_kv = sel * wl.d * 2 * e
+    b_kv = sel * (wl.d + wl.d // 32 if kv_format == "mxfp8" else wl.d * e) * 2
     b_small = wl.batch * (wl.h_kv * wl.d_idx + 2 * wl.h_q * wl.d) * e + wl.batch * wl.h_kv * L * 4 * 2
     total = b_idx + b_kv + b_small
     del x, ws, ik
     torch.cuda.empty_cache()
-    return {"workload": wl.name, "idx_format": idx_format, "us_per_token": ms * 1e3 / (wl.batch * wl.n_q), "ms_per_step": ms,
+    return {"workload": wl.name, "idx_format": idx_format, "kv_format": kv_format, "us_per_token": ms * 1e3 / (wl.batch * wl.n_q), "ms_per_step": ms,
             "algorithmic_bytes": total, "hbm_GBs": total / ms / 1e6, "hbm_frac": total / ms / 1e6 / PEAK_HBM_GBS,
             "kernels_ms": {k: round(v[0], 4) for k, v in kern.items()}}
 
@@ -379,6 +383,8 @@ def main():
         # the same decode step over an MXFP8 index-key cache (a different
         # cache format, reported beside the bf16 figure, never as `value`)
         line["decode_mxfp8"] = run_decode(args, idx_format="mxfp8")
+        # and over an all-MXFP8 cache (index keys, K and V)
+        line["decode_mxfp8_cache"] = run_decode(args, idx_format="mxfp8", kv_format="mxfp8")
     print(json.dumps(line), flush=True)
 
 

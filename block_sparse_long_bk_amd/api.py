@@ -29,7 +29,7 @@ class Problem(ctypes.Structure):
         ("h_q", ctypes.c_int32), ("h_kv", ctypes.c_int32), ("d", ctypes.c_int32),
         ("d_idx", ctypes.c_int32), ("block_size", ctypes.c_int32), ("topk", ctypes.c_int32),
         ("dtype", ctypes.c_int32), ("q_offset", ctypes.c_int64), ("softmax_scale", ctypes.c_float),
-        ("sched", ctypes.c_int32), ("idx_format", ctypes.c_int32),
+        ("sched", ctypes.c_int32), ("idx_format", ctypes.c_int32), ("kv_format", ctypes.c_int32),
     ]
 
 
@@ -90,11 +90,12 @@ def lib():
 
 
 def problem(batch, n_q, n_k, h_q, h_kv, d, d_idx, topk, dtype="bf16", q_offset=0, block_size=128,
-            softmax_scale=0.0, sched="auto", idx_format="plain"):
+            softmax_scale=0.0, sched="auto", idx_format="plain", kv_format="plain"):
     return Problem(batch, n_q, n_k, h_q, h_kv, d, d_idx, block_size, topk,
                    BF16 if dtype in ("bf16", torch.bfloat16) else F32, q_offset, softmax_scale,
                    _SCHED[sched] if isinstance(sched, str) else int(sched),
-                   _IDXF[idx_format] if isinstance(idx_format, str) else int(idx_format))
+                   _IDXF[idx_format] if isinstance(idx_format, str) else int(idx_format),
+                   _IDXF[kv_format] if isinstance(kv_format, str) else int(kv_format))
 
 
 def problem_of(wl, sched="auto", **kw):
@@ -141,6 +142,20 @@ def _expect_ik(p, ik):
         _expect(ik, (n + n // 32,), torch.uint8, "idx_k (MXFP8 codes + scales)")
     else:
         _expect(ik, (p.batch, p.n_k, p.h_kv, p.d_idx), _tdtype(p), "idx_k")
+
+
+def _expect_kv(p, t, name):
+    """K or V in the problem's dtype, or an MXFP8 cache (codes then scales, uint8)."""
+    if p.kv_format == IDX_MXFP8:
+        n = p.batch * p.n_k * p.h_kv * p.d
+        _expect(t, (n + n // 32,), torch.uint8, f"{name} (MXFP8 codes + scales)")
+    else:
+        _expect(t, (p.batch, p.n_k, p.h_kv, p.d), _tdtype(p), name)
+
+
+def _expect_plain_kv(p, what):
+    if p.kv_format != IDX_PLAIN:
+        raise ValueError(f"{what} needs plain K and V")
 
 
 def mxfp8_quantize(x, out=None):
@@ -229,8 +244,8 @@ def invert(p, ids, ws=None):
 def sparse_attention(p, q, k, v, ids, out=None, lse=None, want_lse=True, ws=None):
     dt = _tdtype(p)
     _expect(q, (p.batch, p.n_q, p.h_q, p.d), dt, "q")
-    _expect(k, (p.batch, p.n_k, p.h_kv, p.d), dt, "k")
-    _expect(v, (p.batch, p.n_k, p.h_kv, p.d), dt, "v")
+    _expect_kv(p, k, "k")
+    _expect_kv(p, v, "v")
     _expect(ids, (p.batch, p.n_q, p.h_kv, p.topk), torch.int32, "block_ids")
     if out is None:
         out = torch.empty_like(q)
@@ -248,6 +263,7 @@ def sparse_attention_backward(p, q, k, v, out, lse, dout, ids, dq=None, dk=None,
     """Gradients (dq, dk, dv) of the Main Branch for the fixed selection ids,
     given the forward's out and lse and the upstream gradient dout."""
     dt = _tdtype(p)
+    _expect_plain_kv(p, "sparse_attention_backward")
     _expect(q, (p.batch, p.n_q, p.h_q, p.d), dt, "q")
     _expect(k, (p.batch, p.n_k, p.h_kv, p.d), dt, "k")
     _expect(v, (p.batch, p.n_k, p.h_kv, p.d), dt, "v")
@@ -277,6 +293,7 @@ def indexer_kl(p, q, k, iq, ik, lse, ids, loss_scale=1.0, kl=None, d_iq=None, d_
     dt = _tdtype(p)
     if p.idx_format != IDX_PLAIN:
         raise ValueError("indexer_kl needs plain index keys")
+    _expect_plain_kv(p, "indexer_kl")
     _expect(q, (p.batch, p.n_q, p.h_q, p.d), dt, "q")
     _expect(k, (p.batch, p.n_k, p.h_kv, p.d), dt, "k")
     _expect(iq, (p.batch, p.n_q, p.h_kv, p.d_idx), dt, "idx_q")
@@ -301,8 +318,8 @@ def indexer_kl(p, q, k, iq, ik, lse, ids, loss_scale=1.0, kl=None, d_iq=None, d_
 def forward(p, q, k, v, iq, ik, ids=None, out=None, lse=None, want_lse=True, ws=None):
     dt = _tdtype(p)
     _expect(q, (p.batch, p.n_q, p.h_q, p.d), dt, "q")
-    _expect(k, (p.batch, p.n_k, p.h_kv, p.d), dt, "k")
-    _expect(v, (p.batch, p.n_k, p.h_kv, p.d), dt, "v")
+    _expect_kv(p, k, "k")
+    _expect_kv(p, v, "v")
     _expect(iq, (p.batch, p.n_q, p.h_kv, p.d_idx), dt, "idx_q")
     _expect_ik(p, ik)
     if ids is None:

@@ -26,6 +26,8 @@
 //    the group's query heads resident and walks its selected blocks; the four
 //    waves split each block's 128 keys and merge their states at the end.
 //  * k_combine -- log-sum-exp merge of the partials into the output.
+#include <type_traits>
+
 #include "attn_common.h"
 
 namespace msa {
@@ -94,8 +96,10 @@ __device__ __forceinline__ void block_tile(const char* lds, const frag_t<T> (&qf
 
 struct KvArgs {
   const void* q;
-  const void* k;
+  const void* k;    // K rows, or MXFP8 codes
   const void* v;
+  const uint8_t* ksc;  // MXFP8 scale rows of K and V (KVMX kernels only)
+  const uint8_t* vsc;
   const int32_t* entries;
   const int32_t* item_count;
   const int4* items;
@@ -179,7 +183,8 @@ __device__ __forceinline__ void kv_tile(const KvArgs& a, const char* lds, const 
   }
 }
 
-template <typename T, int D, bool NT, int BK>
+// KVMX: K and V are MXFP8 caches, decoded while staged.
+template <typename T, int D, bool NT, int BK, bool KVMX>
 __global__ void __launch_bounds__(256, 2) k_attn_kvouter(KvArgs a) {
   using L = KvLds<T, D, BK>;
   __shared__ __attribute__((aligned(16))) char lds[L::BYTES];
@@ -218,8 +223,14 @@ __global__ void __launch_bounds__(256, 2) k_attn_kvouter(KvArgs a) {
 #pragma unroll
   for (int u = 0; u < EPT; ++u) e_mine[u] = tid + 256 * u < nent ? ent[tid + 256 * u] : 0;
   __builtin_amdgcn_sched_barrier(0);
-  KvStage<T, D, BK> stg;
-  stg.load(kb, vb, tok_stride, j, a.Nk, tid);
+  std::conditional_t<KVMX, KvStageMx<T, D, BK>, KvStage<T, D, BK>> stg;
+  if constexpr (KVMX) {
+    const int64_t r0 = (int64_t)b * a.Nk * a.Hkv + g;  // first (token, group) row of this (b, g)
+    stg.load(static_cast<const uint8_t*>(a.k) + r0 * D, static_cast<const uint8_t*>(a.v) + r0 * D,
+             a.ksc + r0 * (D / 32), a.vsc + r0 * (D / 32), (int64_t)a.Hkv * D, j, a.Nk, tid);
+  } else {
+    stg.load(kb, vb, tok_stride, j, a.Nk, tid);
+  }
   __builtin_amdgcn_sched_barrier(0);
   // Gathered query rows of tile t: row r = t*32 + lane%32 <-> (entry r/G, head r%G).
   TileRows cur = rows_of(e_first, r0 < nrows, r0, a.gshift, a.topk, a.topk_magic, g);
@@ -252,8 +263,10 @@ __global__ void __launch_bounds__(256, 2) k_attn_kvouter(KvArgs a) {
 
 struct QoArgs {
   const void* q;
-  const void* k;
+  const void* k;    // K rows, or MXFP8 codes
   const void* v;
+  const uint8_t* ksc;  // MXFP8 scale rows of K and V (KVMX kernels only)
+  const uint8_t* vsc;
   const int32_t* ids;
   void* out;
   float* lse;
@@ -266,7 +279,7 @@ struct QoArgs {
 
 // grid: x = nq * Hkv, y = nsplit, z = B.  256 threads; wave w owns keys
 // [32w, 32w + 32) of every block (waves past the block's BK / 32 tiles idle).
-template <typename T, int D, int BK>
+template <typename T, int D, int BK, bool KVMX>
 __global__ void __launch_bounds__(256, 2) k_attn_qouter(QoArgs a) {
   using L = KvLds<T, D, BK>;
   constexpr int MERGE_BYTES = 4 * D * 32 * (int)sizeof(float);  // the final merge reuses the staging area
@@ -303,7 +316,15 @@ __global__ void __launch_bounds__(256, 2) k_attn_qouter(QoArgs a) {
     const int j = sel[s];
     if (j < 0) continue;  // uniform across the workgroup
     __syncthreads();
-    stage_kv<T, D, BK>(lds, kb, vb, tok_stride, j, a.Nk, tid);
+    if constexpr (KVMX) {
+      const int64_t r0 = (int64_t)b * a.Nk * a.Hkv + g;
+      KvStageMx<T, D, BK> stg;
+      stg.load(static_cast<const uint8_t*>(a.k) + r0 * D, static_cast<const uint8_t*>(a.v) + r0 * D,
+               a.ksc + r0 * (D / 32), a.vsc + r0 * (D / 32), (int64_t)a.Hkv * D, j, a.Nk, tid);
+      stg.store(lds, tid);
+    } else {
+      stage_kv<T, D, BK>(lds, kb, vb, tok_stride, j, a.Nk, tid);
+    }
     __syncthreads();
     if (wave * 32 >= BK) continue;  // no keys for this wave (uniform per wave)
     // wave's 32 keys: S^T tile for M-tile `wave`
@@ -487,24 +508,41 @@ __global__ void __launch_bounds__(256) k_combine(CombArgs a) {
     a.lse[((int64_t)b * a.Nq + a.q0 + qq) * a.Hq + h] = W > 0.f ? M + log2_fast(W) * kLn2 : -__builtin_huge_valf();
 }
 
-template <typename T, int D, int BK>
+template <typename T, int D, int BK, bool KVMX>
 void kvouter_launch_bk(bool nt, dim3 grid, hipStream_t st, const KvArgs& a) {
-  if (nt) hipLaunchKernelGGL((k_attn_kvouter<T, D, true, BK>), grid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((k_attn_kvouter<T, D, false, BK>), grid, dim3(256), 0, st, a);
+  if (nt) hipLaunchKernelGGL((k_attn_kvouter<T, D, true, BK, KVMX>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((k_attn_kvouter<T, D, false, BK, KVMX>), grid, dim3(256), 0, st, a);
+}
+
+template <typename T, int D, bool KVMX>
+void kvouter_launch_mx(int bk, bool nt, dim3 grid, hipStream_t st, const KvArgs& a) {
+  if (bk == 32) kvouter_launch_bk<T, D, 32, KVMX>(nt, grid, st, a);
+  else if (bk == 64) kvouter_launch_bk<T, D, 64, KVMX>(nt, grid, st, a);
+  else kvouter_launch_bk<T, D, 128, KVMX>(nt, grid, st, a);
 }
 
 template <typename T, int D>
-void kvouter_launch(int bk, bool nt, dim3 grid, hipStream_t st, const KvArgs& a) {
-  if (bk == 32) kvouter_launch_bk<T, D, 32>(nt, grid, st, a);
-  else if (bk == 64) kvouter_launch_bk<T, D, 64>(nt, grid, st, a);
-  else kvouter_launch_bk<T, D, 128>(nt, grid, st, a);
+void kvouter_launch(int bk, bool kv_mx, bool nt, dim3 grid, hipStream_t st, const KvArgs& a) {
+  if (kv_mx) kvouter_launch_mx<T, D, true>(bk, nt, grid, st, a);
+  else kvouter_launch_mx<T, D, false>(bk, nt, grid, st, a);
+}
+
+template <typename T, int D, bool KVMX>
+void qouter_launch_mx(int bk, dim3 grid, hipStream_t st, const QoArgs& a) {
+  if (bk == 32) hipLaunchKernelGGL((k_attn_qouter<T, D, 32, KVMX>), grid, dim3(256), 0, st, a);
+  else if (bk == 64) hipLaunchKernelGGL((k_attn_qouter<T, D, 64, KVMX>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((k_attn_qouter<T, D, 128, KVMX>), grid, dim3(256), 0, st, a);
 }
 
 template <typename T, int D>
-void qouter_launch(int bk, dim3 grid, hipStream_t st, const QoArgs& a) {
-  if (bk == 32) hipLaunchKernelGGL((k_attn_qouter<T, D, 32>), grid, dim3(256), 0, st, a);
-  else if (bk == 64) hipLaunchKernelGGL((k_attn_qouter<T, D, 64>), grid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((k_attn_qouter<T, D, 128>), grid, dim3(256), 0, st, a);
+void qouter_launch(int bk, bool kv_mx, dim3 grid, hipStream_t st, const QoArgs& a) {
+  if (kv_mx) qouter_launch_mx<T, D, true>(bk, grid, st, a);
+  else qouter_launch_mx<T, D, false>(bk, grid, st, a);
+}
+
+// MXFP8 K / V caches: the codes [B, Nk, Hkv, D] are followed by the scales.
+const uint8_t* mx_scales_of(const Shape& s, const void* codes) {
+  return s.kv_mx ? static_cast<const uint8_t*>(codes) + (size_t)s.B * s.Nk * s.Hkv * s.D : nullptr;
 }
 
 }  // namespace
@@ -516,6 +554,8 @@ hipError_t launch_attn_kvouter(const Shape& s, const InvertPlan& p, int q0, int 
   a.q = q;
   a.k = k;
   a.v = v;
+  a.ksc = mx_scales_of(s, k);
+  a.vsc = mx_scales_of(s, v);
   a.entries = inv.entries;
   a.item_count = inv.item_count;
   a.items = inv.items;
@@ -543,11 +583,11 @@ hipError_t launch_attn_kvouter(const Shape& s, const InvertPlan& p, int q0, int 
   const bool nt = (double)nq * s.topk * a.G >= (double)kItemRows * s.nblk;
   prof_begin(st, kid);
   if (s.dtype == kBF16) {
-    if (s.D == 64) kvouter_launch<bf16_t, 64>(s.Bk, nt, grid, st, a);
-    else kvouter_launch<bf16_t, 128>(s.Bk, nt, grid, st, a);
+    if (s.D == 64) kvouter_launch<bf16_t, 64>(s.Bk, s.kv_mx, nt, grid, st, a);
+    else kvouter_launch<bf16_t, 128>(s.Bk, s.kv_mx, nt, grid, st, a);
   } else {
-    if (s.D == 64) kvouter_launch<float, 64>(s.Bk, nt, grid, st, a);
-    else kvouter_launch<float, 128>(s.Bk, nt, grid, st, a);
+    if (s.D == 64) kvouter_launch<float, 64>(s.Bk, s.kv_mx, nt, grid, st, a);
+    else kvouter_launch<float, 128>(s.Bk, s.kv_mx, nt, grid, st, a);
   }
   const hipError_t e = hipGetLastError();
   prof_end(st, kid);
@@ -562,6 +602,8 @@ hipError_t launch_attn_qouter(const Shape& s, int q0, int nq, int nsplit, const 
   a.q = q;
   a.k = k;
   a.v = v;
+  a.ksc = mx_scales_of(s, k);
+  a.vsc = mx_scales_of(s, v);
   a.ids = ids;
   a.out = out;
   a.lse = lse;
@@ -581,11 +623,11 @@ hipError_t launch_attn_qouter(const Shape& s, int q0, int nq, int nsplit, const 
   const dim3 grid(nq * s.Hkv, nsplit, s.B);
   prof_begin(st, kid);
   if (s.dtype == kBF16) {
-    if (s.D == 64) qouter_launch<bf16_t, 64>(s.Bk, grid, st, a);
-    else qouter_launch<bf16_t, 128>(s.Bk, grid, st, a);
+    if (s.D == 64) qouter_launch<bf16_t, 64>(s.Bk, s.kv_mx, grid, st, a);
+    else qouter_launch<bf16_t, 128>(s.Bk, s.kv_mx, grid, st, a);
   } else {
-    if (s.D == 64) qouter_launch<float, 64>(s.Bk, grid, st, a);
-    else qouter_launch<float, 128>(s.Bk, grid, st, a);
+    if (s.D == 64) qouter_launch<float, 64>(s.Bk, s.kv_mx, grid, st, a);
+    else qouter_launch<float, 128>(s.Bk, s.kv_mx, grid, st, a);
   }
   const hipError_t e = hipGetLastError();
   prof_end(st, kid);

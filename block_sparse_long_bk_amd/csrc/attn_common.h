@@ -14,6 +14,17 @@ template <typename T> struct Pack4;
 template <> struct Pack4<bf16_t> { using type = bf16x4; };
 template <> struct Pack4<float> { using type = f32x4; };
 
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) { return static_cast<bf16_t>(x); }
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+
+// Eight elements to (16-byte aligned) memory.
+__device__ __forceinline__ void store8(bf16_t* p, const bf16x8& v) { *reinterpret_cast<bf16x8*>(p) = v; }
+__device__ __forceinline__ void store8(float* p, const f32x8& v) {
+  *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
+  *reinterpret_cast<f32x4*>(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
+}
+
 // LDS geometry of one staged key block of BK tokens: K row-major [BK][D], V
 // transposed [D][BK].  Pitches are padded so the 32 rows read by a half-wave
 // fall on distinct banks.
@@ -122,6 +133,90 @@ struct KvStage {
   }
 };
 
+// The same staging from MXFP8 K and V caches (OCP MX v1.0: E4M3 codes, one
+// E8M0 scale byte per 32 elements of a row).  The loads keep the codes and
+// scale bytes; the stores decode them exactly (fp8 conversion, then a power
+// of two) into the dtype layout of KvLds, so the products are unchanged.
+// kc / vc: code rows (D bytes) and ks / vs: scale rows (D/32 bytes) of this
+// (b, g) at token strides of cstride / cstride/32 bytes.
+template <typename T, int D, int BK>
+struct KvStageMx {
+  using L = KvLds<T, D, BK>;
+  static constexpr int KT = BK * (D / 16);  // K tasks: 16 codes of one row
+  static constexpr int KLD = (KT + 255) / 256;
+  static constexpr int DCH = D / 8;
+  static constexpr int KG = 256 / DCH;
+  static constexpr int PASSES = (BK + 4 * KG - 1) / (4 * KG);
+  u32x4 kc[KLD];
+  uint32_t ksc[KLD];
+  uint2 vc[PASSES][4];
+  uint32_t vsc[PASSES][4];
+
+  __device__ __forceinline__ void load(const uint8_t* kcb, const uint8_t* vcb, const uint8_t* ksb,
+                                       const uint8_t* vsb, int64_t cstride, int j, int n_k, int tid) {
+    const int64_t sstride = cstride / 32;
+#pragma unroll
+    for (int u = 0; u < KLD; ++u) {
+      const int c = tid + u * 256;
+      const int row = c / (D / 16), col = c % (D / 16);
+      const int64_t t = (int64_t)j * BK + row;
+      kc[u] = u32x4{};
+      ksc[u] = 127;
+      if (c < KT && t < n_k) {
+        kc[u] = *reinterpret_cast<const u32x4*>(kcb + t * cstride + col * 16);
+        ksc[u] = ksb[t * sstride + col / 2];
+      }
+    }
+    const int dch = tid % DCH, kg = tid / DCH;
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = (ps * KG + kg) * 4 + r;
+        const int64_t t = (int64_t)j * BK + key;
+        vc[ps][r] = make_uint2(0, 0);
+        vsc[ps][r] = 127;
+        if (key < BK && t < n_k) {
+          vc[ps][r] = *reinterpret_cast<const uint2*>(vcb + t * cstride + dch * 8);
+          vsc[ps][r] = vsb[t * sstride + dch / 4];
+        }
+      }
+  }
+
+  __device__ __forceinline__ void store(char* lds, int tid) const {
+#pragma unroll
+    for (int u = 0; u < KLD; ++u) {
+      const int c = tid + u * 256;
+      if (c >= KT) continue;
+      const int row = c / (D / 16), col = c % (D / 16);
+      float f[16];
+      e4m3_decode16(kc[u], f);
+      const int sh = (int)ksc[u] - 127;
+      T* dst = reinterpret_cast<T*>(lds + row * L::KPITCH) + col * 16;
+      frag_t<T> lo, hi;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        lo[e] = from_f32<T>(__builtin_ldexpf(f[e], sh));
+        hi[e] = from_f32<T>(__builtin_ldexpf(f[8 + e], sh));
+      }
+      store8(dst, lo);
+      store8(dst + 8, hi);
+    }
+    KvStage<T, D, BK> tmp;  // V^T through the plain stager's transposing store
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float f[8];
+        e4m3_decode8(vc[ps][r], f);
+        const int sh = (int)vsc[ps][r] - 127;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) tmp.vr[ps][r][e] = from_f32<T>(__builtin_ldexpf(f[e], sh));
+      }
+    tmp.store_vt(lds + L::KBYTES, tid);
+  }
+};
+
 template <typename T, int D, int BK>
 __device__ __forceinline__ void stage_kv(char* lds, const T* kbase, const T* vbase, int64_t tok_stride, int j,
                                          int n_k, int tid) {
@@ -150,9 +245,6 @@ __device__ __forceinline__ frag_t<T> vt_frag(const char* lds, int d, int mt, int
   return vt_frag_at<T, D, BK>(lds + KvLds<T, D, BK>::KBYTES, d, mt, a, half);
 }
 
-template <typename T> __device__ __forceinline__ T from_f32(float x);
-template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) { return static_cast<bf16_t>(x); }
-template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 
 // A fragment of a transposed 32-row tile (rows of TPITCH bytes, one per
 // column) for k-step a: column c, tile rows 16a + 4h + [0..3] and

@@ -39,6 +39,7 @@ msa_status_t validate(const msa_problem_t* p) {
     return MSA_ERR_INVALID_ARG;
   if (!std::isfinite(p->softmax_scale)) return MSA_ERR_INVALID_ARG;
   if (p->idx_format != MSA_IDX_PLAIN && p->idx_format != MSA_IDX_MXFP8) return MSA_ERR_INVALID_ARG;
+  if (p->kv_format != MSA_IDX_PLAIN && p->kv_format != MSA_IDX_MXFP8) return MSA_ERR_INVALID_ARG;
   // Valid but outside what the kernels are built for.
   if (p->block_size != 32 && p->block_size != 64 && p->block_size != 128) return MSA_ERR_UNSUPPORTED;
   if (p->d != 64 && p->d != 128) return MSA_ERR_UNSUPPORTED;
@@ -66,6 +67,7 @@ msa::Shape shape_of(const msa_problem_t* p) {
   s.topk = p->topk;
   s.dtype = p->dtype == MSA_BF16 ? msa::kBF16 : msa::kF32;
   s.idx_mx = p->idx_format == MSA_IDX_MXFP8;
+  s.kv_mx = p->kv_format == MSA_IDX_MXFP8;
   s.q_offset = p->q_offset;
   s.Bk = p->block_size;
   s.nblk = (p->n_k + s.Bk - 1) / s.Bk;
@@ -428,6 +430,7 @@ msa_status_t msa_sparse_attention_backward(const msa_problem_t* prob, const void
                                            size_t ws_bytes, void* stream) {
   msa_status_t rc = validate(prob);
   if (rc != MSA_OK) return rc;
+  if (prob->kv_format != MSA_IDX_PLAIN) return MSA_ERR_UNSUPPORTED;
   const void* ptrs[] = {q, k, v, out, lse, dout, block_ids, dq, dk, dv, ws};
   for (const void* x : ptrs)
     if (!x || !aligned16(x)) return MSA_ERR_INVALID_ARG;
@@ -457,7 +460,7 @@ msa_status_t msa_indexer_kl(const msa_problem_t* prob, const void* q, const void
                             float* kl, void* d_iq, void* d_ik, void* ws, size_t ws_bytes, void* stream) {
   msa_status_t rc = validate(prob);
   if (rc != MSA_OK) return rc;
-  if (prob->idx_format != MSA_IDX_PLAIN) return MSA_ERR_UNSUPPORTED;
+  if (prob->idx_format != MSA_IDX_PLAIN || prob->kv_format != MSA_IDX_PLAIN) return MSA_ERR_UNSUPPORTED;
   if (!std::isfinite(loss_scale)) return MSA_ERR_INVALID_ARG;
   const void* ptrs[] = {q, k, idx_q, idx_k, lse, block_ids, kl, d_iq, d_ik, ws};
   for (const void* x : ptrs)

@@ -102,6 +102,20 @@ __device__ __forceinline__ void e4m3_decode16(const u32x4& c, float (&out)[16]) 
   }
 }
 
+// Eight E4M3 codes (8 bytes, little-endian) decoded exactly to fp32.
+__device__ __forceinline__ void e4m3_decode8(const uint2& c, float (&out)[8]) {
+  const uint32_t w[2] = {c.x, c.y};
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);
+    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);
+    out[4 * i + 0] = lo[0];
+    out[4 * i + 1] = lo[1];
+    out[4 * i + 2] = hi[0];
+    out[4 * i + 3] = hi[1];
+  }
+}
+
 // Lanes of one wave that exchange data through LDS without a workgroup
 // barrier must separate the writes from the reads with this: the wave runs in
 // lockstep and LDS accesses of one wave complete in order, but without a fence

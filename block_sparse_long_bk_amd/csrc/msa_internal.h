@@ -14,6 +14,7 @@ enum DType { kF32 = 0, kBF16 = 1 };
 struct Shape {
   int B, Nq, Nk, Hq, Hkv, D, DI, topk, dtype;
   bool idx_mx;  // idx_k is an MXFP8 cache: codes, then one scale byte per 32 elements
+  bool kv_mx;   // K and V are MXFP8 caches (same layout)
   int64_t q_offset;
   int Bk;       // key block size: 32, 64 or 128
   int nblk;     // ceil(Nk / Bk)

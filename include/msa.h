@@ -56,6 +56,15 @@
  * B*Nk*Hkv*d_idx bytes after idx_k.  idx_q stays in `dtype`; scores are
  * computed from the exactly decoded keys in fp32.  msa_mxfp8_quantize writes
  * such a cache.
+ *
+ * K and V may likewise be MXFP8 caches (kv_format = MSA_IDX_MXFP8, the same
+ * write-up's MXFP8 KV cache): the k (v) pointer holds the codes [B, Nk, Hkv, d]
+ * followed by the scales [B, Nk, Hkv, d/32].  The attention entry points
+ * (msa_sparse_attention, msa_forward) decode them exactly into `dtype` while
+ * staging a key block, so the products are those of the decoded cache; q, the
+ * output and lse stay in `dtype` / fp32.  The training entry points
+ * (msa_sparse_attention_backward, msa_indexer_kl) need plain K and V
+ * (MSA_ERR_UNSUPPORTED otherwise).
  */
 #ifndef MSA_H
 #define MSA_H
@@ -87,7 +96,8 @@ typedef enum { MSA_F32 = 0, MSA_BF16 = 1 } msa_dtype_t;
  * (the note quotes 2.85 for its Blackwell kernels) -- and Q_OUTER otherwise. */
 typedef enum { MSA_SCHED_AUTO = 0, MSA_SCHED_KV_OUTER = 1, MSA_SCHED_Q_OUTER = 2 } msa_sched_t;
 
-/* How idx_k is stored: in `dtype` like the other tensors, or as an MXFP8 cache. */
+/* How idx_k (idx_format) or K and V (kv_format) are stored: in `dtype` like the
+ * other tensors, or as an MXFP8 cache. */
 typedef enum { MSA_IDX_PLAIN = 0, MSA_IDX_MXFP8 = 1 } msa_idx_format_t;
 
 typedef struct {
@@ -97,6 +107,7 @@ typedef struct {
   float softmax_scale;   /* <= 0 means 1/sqrt(d) */
   int32_t sched;         /* msa_sched_t */
   int32_t idx_format;    /* msa_idx_format_t */
+  int32_t kv_format;     /* msa_idx_format_t, for K and V */
 } msa_problem_t;
 
 typedef enum {

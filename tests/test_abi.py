@@ -54,6 +54,8 @@ def test_status_strings():
     (dict(idx_format=2), api.MSA_ERR_INVALID_ARG),
     (dict(idx_format="mxfp8"), api.MSA_OK),
     (dict(idx_format="mxfp8", dtype="bf16", d=128, d_idx=32, h_q=64, h_kv=8, topk=16), api.MSA_OK),
+    (dict(kv_format="mxfp8"), api.MSA_OK),
+    (dict(kv_format=3), api.MSA_ERR_INVALID_ARG),
     (dict(block_size=64), api.MSA_OK),
     (dict(block_size=32), api.MSA_OK),
     (dict(block_size=96), api.MSA_ERR_UNSUPPORTED),
@@ -103,6 +105,10 @@ def test_entry_points_reject_before_any_hip_call():
     assert kl(ctypes.byref(p), x, x, x, x, x, x, 1.0, x, null, x, x, 1 << 30, null) == api.MSA_ERR_INVALID_ARG
     mx = good(idx_format="mxfp8")
     assert kl(ctypes.byref(mx), x, x, x, x, x, x, 1.0, x, x, x, x, 1 << 30, null) == api.MSA_ERR_UNSUPPORTED
+    # the training entry points need plain K and V
+    kvmx = good(kv_format="mxfp8")
+    assert kl(ctypes.byref(kvmx), x, x, x, x, x, x, 1.0, x, x, x, x, 1 << 30, null) == api.MSA_ERR_UNSUPPORTED
+    assert bw(ctypes.byref(kvmx), x, x, x, x, x, x, x, x, x, x, x, 1 << 30, null) == api.MSA_ERR_UNSUPPORTED
     # MXFP8 quantiser: sizes, dtype and pointers are checked before any launch
     q = L.msa_mxfp8_quantize
     assert q(x, api.BF16, 4, 48, x, x, null) == api.MSA_ERR_INVALID_ARG   # row length not a multiple of 32

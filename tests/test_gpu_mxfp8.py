@@ -9,6 +9,12 @@ codes) against the oracle.
   tie band (both index kernels: the MFMA tile for prefill, the scan for
   decode), block scores within 1e-5 of the largest, and the forward pass must
   give the same attention as the oracle on that selection.
+* Attention over MXFP8 K and V caches (both schedules, Bk 32/64/128): the
+  caches are built by the oracle's quantiser and the oracle attends over the
+  exactly dequantised keys and values; the GPU decodes them while staging a
+  block, so the usual attention tolerance applies.  A forward over an
+  all-MXFP8 cache (index keys too) must select as the MX index path does and
+  attend exactly as the attention call on that selection.
 """
 import numpy as np
 import pytest
@@ -144,3 +150,57 @@ def test_decode_16x1m_over_mxfp8_cache():
         print(f"decode_16x1m/mxfp8 b={b}: {res}", flush=True)
         assert res["fail"] == 0, res
         del cache
+
+
+# ---- MXFP8 K / V caches: attention over the exactly decoded keys and values.
+KV_CASES = {
+    "kv_bf16_kvouter": dict(dtype="bf16", n_q=1000, n_k=1000, h_q=16, h_kv=4, d=128, d_idx=128, topk=6,
+                            sched="kv_outer"),
+    "kv_f32_kvouter": dict(n_q=600, n_k=600, h_q=8, h_kv=2, d=64, d_idx=32, topk=4, sched="kv_outer"),
+    "kv_f32_d128_kvouter": dict(n_q=700, n_k=700, h_q=8, h_kv=2, d=128, d_idx=64, topk=5, sched="kv_outer"),
+    "kv_bf16_qouter": dict(dtype="bf16", n_q=300, n_k=2000, q_offset=1700, h_q=8, h_kv=2, d=64, d_idx=64,
+                           topk=5, sched="q_outer"),
+    "kv_bf16_decode": dict(dtype="bf16", batch=3, n_q=1, n_k=5000, q_offset=4999, h_q=16, h_kv=2, d=128,
+                           d_idx=128, topk=8, sched="auto"),
+    "kv_bf16_bk64": dict(dtype="bf16", n_q=700, n_k=700, h_q=8, h_kv=2, d=64, d_idx=128, topk=8, block_size=64,
+                         sched="kv_outer"),
+    "kv_f32_bk32_qouter": dict(n_q=5, n_k=3000, q_offset=2995, topk=4, block_size=32, sched="q_outer"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(KV_CASES))
+def test_attention_over_mxfp8_kv_cache(name):
+    kw = dict(KV_CASES[name])
+    sched = kw.pop("sched")
+    wl = inputs.small(name, seed=3500 + sorted(KV_CASES).index(name), **kw)
+    x = inputs.generate(wl, device="cuda")
+    prob = O.problem_of(wl)
+    # the oracle builds both caches and decodes them exactly
+    kv = {}
+    for t in ("k", "v"):
+        codes, scales = O.mx_quantize(host(x[t]))
+        kv[t] = (torch.from_numpy(np.concatenate([codes.reshape(-1), scales.reshape(-1)])).cuda(),
+                 O.mx_dequantize(codes, scales).reshape(wl.batch, wl.n_k, wl.h_kv, wl.d))
+    s_o = O.block_scores(prob, host(x["iq"]), host(x["ik"]))
+    ids_o = O.select(prob, s_o)
+    ids = torch.from_numpy(ids_o.reshape(wl.batch, wl.n_q, wl.h_kv, wl.topk)).cuda()
+    p = api.problem_of(wl, sched=sched, kv_format="mxfp8")
+    out, lse = api.sparse_attention(p, x["q"], kv["k"][0], kv["v"][0], ids)
+    torch.cuda.synchronize()
+    q64 = to_f64(x["q"])
+    o_o, l_o = O.attend(prob, q64, np.ascontiguousarray(kv["k"][1]), np.ascontiguousarray(kv["v"][1]), ids_o)
+    mx, rl = assert_attention(wl.dtype, to_f64(out).reshape(o_o.shape), o_o, host(lse).numpy().reshape(l_o.shape),
+                              l_o, what=f"{name}/attention")
+    # the whole forward over an all-MXFP8 cache (index keys too) selects as the
+    # MX index path does and attends as above
+    pa = api.problem_of(wl, sched=sched, idx_format="mxfp8", kv_format="mxfp8")
+    ik_cache = api.mxfp8_quantize(x["ik"])
+    ids_a, out_a, _ = api.forward(pa, x["q"], kv["k"][0], kv["v"][0], x["iq"], ik_cache)
+    ids_i, _, _ = api.forward(api.problem_of(wl, sched=sched, idx_format="mxfp8"), x["q"], x["k"], x["v"], x["iq"],
+                              ik_cache)
+    out_b, _ = api.sparse_attention(p, x["q"], kv["k"][0], kv["v"][0], ids_a)
+    torch.cuda.synchronize()
+    assert torch.equal(ids_a, ids_i)
+    assert torch.equal(out_a.view(torch.uint8) if out_a.dtype == torch.bfloat16 else out_a,
+                       out_b.view(torch.uint8) if out_b.dtype == torch.bfloat16 else out_b)
+    print(f"{name}: attention max-abs {mx:.2e} rel-L2 {rl:.2e}")
