@@ -247,24 +247,46 @@ __global__ void __launch_bounds__(kTileWaves * 64) k_index_tile(TileArgs a) {
         if constexpr (DMA) return dma_frag<T>(bufc, mt * 32 + arow, 16 * ks + 8 * half);
         else return load8(reinterpret_cast<const T*>(bufc + (mt * 32 + arow) * PITCH) + 8 * half + 16 * ks);
       };
+      // Software pipeline over the four M-tiles: the products of M-tile mt+1
+      // are issued before the max-pool of mt, so the VALU work of one tile
+      // runs while the matrix core works on the next (two accumulator sets;
+      // with the longest Top-k lists the second set would not fit in the
+      // registers, and the tiles run one after the other).
+      constexpr bool PIPE = KMAX <= 16;
       frag_t<T> A[2][KSTEPS];
+      f32x16 acc[2][NT];
+      auto products = [&](int mt) {
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) A[0][ks] = frag(0, ks);
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        if (mt + 1 < 4) {
-#pragma unroll
-          for (int ks = 0; ks < KSTEPS; ++ks) A[(mt + 1) & 1][ks] = frag(mt + 1, ks);
-        }
-        f32x16 acc[NT];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[nt] = mma0(A[mt & 1][0], bq[nt][0]);
+        for (int nt = 0; nt < NT; ++nt) acc[mt & 1][nt] = mma0(A[mt & 1][0], bq[nt][0]);
 #pragma unroll
         for (int ks = 1; ks < KSTEPS; ++ks)
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt) mma(A[mt & 1][ks], bq[nt][ks], acc[nt]);
+          for (int nt = 0; nt < NT; ++nt) mma(A[mt & 1][ks], bq[nt][ks], acc[mt & 1][nt]);
+      };
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) run[nt] = max16(acc[nt], run[nt]);
+      for (int ks = 0; ks < KSTEPS; ++ks) A[0][ks] = frag(0, ks);
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) A[1][ks] = frag(1, ks);
+      products(0);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        if constexpr (PIPE) {
+          if (mt + 1 < 4) {
+            products(mt + 1);
+            if (mt + 2 < 4) {
+#pragma unroll
+              for (int ks = 0; ks < KSTEPS; ++ks) A[mt & 1][ks] = frag(mt + 2, ks);
+            }
+          }
+        } else if (mt > 0) {
+          products(mt);
+          if (mt + 1 < 4) {
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks) A[(mt + 1) & 1][ks] = frag(mt + 1, ks);
+          }
+        }
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) run[nt] = max16(acc[mt & 1][nt], run[nt]);
         if (((mt + 1) & (bpm - 1)) == 0) {
           // Last M-tile of a key block.  Each half of the wave saw half of the
           // block's keys; swap halves so that lane l ends with the full block
