@@ -357,6 +357,10 @@ def main():
         "attention_tflops_per_step": r["fl_attn"] / 1e12, "index_tflops_per_step": r["fl_idx"] / 1e12,
         "index_TFLOPs": None, "wall_ms_per_step": r["wall_ms"],
         "attn_kvouter_TFLOPs": (r["fl_attn"] / kern["attn_kvouter"][0] / 1e9) if "attn_kvouter" in kern else None,
+        # the same work over the attention part of the step alone (inversion, attention, combine: the
+        # msa_sparse_attention calls), i.e. without the index scoring and selection
+        "sparse_attention_TFLOPs": r["fl_attn"] / sum(v[0] * v[1] for k, v in kern.items()
+                                                      if k.startswith(("inv_", "attn_")) or k == "combine") / 1e9,
         "attn_kvouter_GBs": (r["bytes"]["attn_kvouter"] / kern["attn_kvouter"][0] / 1e6)
         if "attn_kvouter" in kern else None,
         "combine_GBs": (r["bytes"]["combine"] / kern["combine"][0] / 1e6) if "combine" in kern else None,

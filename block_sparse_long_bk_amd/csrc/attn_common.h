@@ -246,16 +246,28 @@ __device__ __forceinline__ frag_t<T> vt_frag(const char* lds, int d, int mt, int
 }
 
 
+// Position of the 4-row chunk q (rows 4q..4q+3) in column c of a transposed
+// 32-row tile.  With SWZ (16-bit types) the chunks of columns 32 apart are
+// XOR-permuted by ((c / 32) % 4) * 2: the staging stores write columns 8
+// apart from neighbouring lanes, which would otherwise fall on 4 banks per
+// 64; the fragment reads take 32 consecutive columns, which share the swizzle.
+template <bool SWZ>
+__device__ __forceinline__ int tile_t_chunk(int c, int q) {
+  return SWZ ? q ^ (((c >> 5) & 3) << 1) : q;
+}
+
 // A fragment of a transposed 32-row tile (rows of TPITCH bytes, one per
 // column) for k-step a: column c, tile rows 16a + 4h + [0..3] and
 // 16a + 8 + 4h + [0..3] -- the order of an accumulator's rows, so that a
 // product whose other operand comes straight from an accumulator lines up.
-template <typename T, int TPITCH>
+template <typename T, int TPITCH, bool SWZ = false>
 __device__ __forceinline__ frag_t<T> tile_t_frag(const char* base, int c, int a, int half) {
+  static_assert(!SWZ || sizeof(T) == 2, "the chunk swizzle is laid out for 16-bit tiles");
   const T* row = reinterpret_cast<const T*>(base + c * TPITCH);
-  const int r0 = 16 * a + 4 * half;
-  const typename Pack4<T>::type lo = *reinterpret_cast<const typename Pack4<T>::type*>(row + r0);
-  const typename Pack4<T>::type hi = *reinterpret_cast<const typename Pack4<T>::type*>(row + r0 + 8);
+  const int q0 = 4 * a + half;
+  const typename Pack4<T>::type lo = *reinterpret_cast<const typename Pack4<T>::type*>(row + 4 * tile_t_chunk<SWZ>(c, q0));
+  const typename Pack4<T>::type hi =
+      *reinterpret_cast<const typename Pack4<T>::type*>(row + 4 * tile_t_chunk<SWZ>(c, q0 + 2));
   frag_t<T> f;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {

@@ -81,7 +81,10 @@ struct FusedLds {
   using L = KvLds<T, D, BK>;
   static constexpr int RPITCH = D * (int)sizeof(T) + 16;                          // a tile row
   static constexpr int TPITCH = 32 * (int)sizeof(T) + (sizeof(T) == 2 ? 8 : 16);  // a transposed tile row
-  static constexpr int SPITCH = BK * (int)sizeof(T) + 16;                         // a dS row [row][key]
+  // a dS row [row][key]: for 16-bit types an odd multiple of 8 bytes past BK keys, so that the 32 rows read by a
+  // half-wave fall on distinct banks, and 3 mod 8 of them so that the two half-waves' writes (4 rows apart) do too
+  static constexpr int SPITCH = BK * (int)sizeof(T) + (sizeof(T) == 2 ? 24 : 16);
+  static constexpr bool SWZ = sizeof(T) == 2;  // transposed tiles use the chunk swizzle
   static constexpr int KT_OFF = 0;                                                 // K^T [D][BK]
   static constexpr int Q_OFF = KT_OFF + D * L::VPITCH;
   static constexpr int DO_OFF = Q_OFF + 32 * RPITCH;
@@ -161,8 +164,10 @@ struct TileStage {
           const uint32_t x0 = vv[0][w], x1 = vv[1][w], x2 = vv[2][w], x3 = vv[3][w];
           const uint2 lo = make_uint2(__builtin_amdgcn_perm(x1, x0, 0x05040100u), __builtin_amdgcn_perm(x3, x2, 0x05040100u));
           const uint2 hi = make_uint2(__builtin_amdgcn_perm(x1, x0, 0x07060302u), __builtin_amdgcn_perm(x3, x2, 0x07060302u));
-          *reinterpret_cast<uint2*>(tr + (col * EPC + 2 * w) * X::TPITCH + 4 * rg * 2) = lo;
-          *reinterpret_cast<uint2*>(tr + (col * EPC + 2 * w + 1) * X::TPITCH + 4 * rg * 2) = hi;
+          const int c0 = col * EPC + 2 * w;  // columns c0 and c0 + 1 share the swizzle
+          const int pos = tile_t_chunk<X::SWZ>(c0, rg) * 8;
+          *reinterpret_cast<uint2*>(tr + c0 * X::TPITCH + pos) = lo;
+          *reinterpret_cast<uint2*>(tr + (c0 + 1) * X::TPITCH + pos) = hi;
         }
       } else {
 #pragma unroll
@@ -305,8 +310,8 @@ __global__ void __launch_bounds__(NW * 64, 1) k_bwd_fused(BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < DT; ++i) {
           const int c = 32 * (dh * DT + i) + (lane & 31);
-          mma(pa, tile_t_frag<T, X::TPITCH>(lds + X::DOT_OFF, c, aa, half), dvacc[i]);
-          mma(sa, tile_t_frag<T, X::TPITCH>(lds + X::QT_OFF, c, aa, half), dkacc[i]);
+          mma(pa, tile_t_frag<T, X::TPITCH, X::SWZ>(lds + X::DOT_OFF, c, aa, half), dvacc[i]);
+          mma(sa, tile_t_frag<T, X::TPITCH, X::SWZ>(lds + X::QT_OFF, c, aa, half), dkacc[i]);
         }
       }
     }

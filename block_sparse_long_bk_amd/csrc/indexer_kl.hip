@@ -146,7 +146,10 @@ struct KlLds {
   static constexpr int QPITCH = D * (int)sizeof(T) + 16;    // a Main Branch query row
   static constexpr int IPITCH = DI * (int)sizeof(T) + 16;   // an index query row
   static constexpr int TPITCH = 32 * (int)sizeof(T) + (sizeof(T) == 2 ? 8 : 16);  // 32 entries, transposed
-  static constexpr int GPITCH = BK * (int)sizeof(T) + 16;   // g row [entry][key]
+  // g row [entry][key]: for 16-bit types an odd multiple of 8 bytes past BK keys, so that the 32 rows read by a
+  // half-wave fall on distinct banks, and 3 mod 8 of them so that the two half-waves' writes (4 rows apart) do too
+  static constexpr int GPITCH = BK * (int)sizeof(T) + (sizeof(T) == 2 ? 24 : 16);
+  static constexpr bool SWZ = sizeof(T) == 2;  // the transposed tile uses the chunk swizzle
   static constexpr int IKT_OFF = 0;                          // ik^T [DI][BK]
   static constexpr int IQ_OFF = IKT_OFF + DI * LI::VPITCH;   // iq tile [32][DI]
   static constexpr int IQT_OFF = IQ_OFF + 32 * IPITCH;       // iq^T tile [DI][32]
@@ -216,45 +219,66 @@ __global__ void __launch_bounds__(256, 1) k_kl_main(KlArgs a) {
   for (int tile = 0; tile * 32 < nent; ++tile) {
     __syncthreads();  // the previous tile's LDS is no longer read
     // All of a thread's loads are issued before any of them is used, so the
-    // tile costs one memory latency rather than one per chunk.  Rows past the
-    // item's end read entry 0 and store zeros.
+    // tile costs one memory latency rather than one per chunk.  A task is one
+    // 16-byte column chunk of two consecutive rows, so that the transposed
+    // copy gets both rows per store.  Rows past the item's end read entry 0
+    // and store zeros.
     {
-      constexpr int NI = (32 * ICPR + 255) / 256;
-      u32x4 v[NI];
-      float ls[NI];
+      constexpr int NI = (16 * ICPR + 255) / 256;
+      constexpr int EPC = 16 / (int)sizeof(T);  // elements per chunk
+      u32x4 v[NI][2];
+      float ls[NI][2];
 #pragma unroll
       for (int u = 0; u < NI; ++u) {
-        const int c = tid + 256 * u;
-        const int rr = min(c / ICPR, 31), col = c % ICPR;
-        const int r = tile * 32 + rr;
-        int qq, slot;
-        split_entry(r < nent ? ent_lds[r] : ent_lds[0], a.topk, a.topk_magic, qq, slot);
-        const int64_t row = ((int64_t)b * a.Nq + qq) * a.Hkv + g;
-        v[u] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(iqb + row * DI) + col * 16);
-        ls[u] = a.lse_s[row];
+        const int c = min(tid + 256 * u, 16 * ICPR - 1);
+        const int rp = c / ICPR, col = c % ICPR;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int r = tile * 32 + 2 * rp + h;
+          int qq, slot;
+          split_entry(r < nent ? ent_lds[r] : ent_lds[0], a.topk, a.topk_magic, qq, slot);
+          const int64_t row = ((int64_t)b * a.Nq + qq) * a.Hkv + g;
+          v[u][h] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(iqb + row * DI) + col * 16);
+          ls[u][h] = a.lse_s[row];
+        }
       }
 #pragma unroll
       for (int u = 0; u < NI; ++u) {
         const int c = tid + 256 * u;
-        if (c >= 32 * ICPR) continue;
-        const int rr = c / ICPR, col = c % ICPR;
-        const int r = tile * 32 + rr;
-        const bool valid = r < nent;
-        const u32x4 w = valid ? v[u] : u32x4{};
-        *reinterpret_cast<u32x4*>(lds + X::IQ_OFF + rr * X::IPITCH + col * 16) = w;
-        T el[16 / sizeof(T)];
-        __builtin_memcpy(el, &w, 16);
+        if (c >= 16 * ICPR) continue;
+        const int rp = c / ICPR, col = c % ICPR;
+        u32x4 w[2];
 #pragma unroll
-        for (int e = 0; e < (int)(16 / sizeof(T)); ++e)
-          *reinterpret_cast<T*>(lds + X::IQT_OFF + (col * (16 / (int)sizeof(T)) + e) * X::TPITCH +
-                                rr * (int)sizeof(T)) = el[e];
-        if (col == 0) {
-          int qq, slot;
-          split_entry(valid ? ent_lds[r] : ent_lds[0], a.topk, a.topk_magic, qq, slot);
-          row_lse_s[rr] = valid ? ls[u] : 0.f;
-          row_pos[rr] = valid ? (int)min(a.q_offset + qq, (int64_t)a.Nk - 1) : -1;
-          row_q[rr] = qq;
-          row_slot[rr] = slot;
+        for (int h = 0; h < 2; ++h) {
+          const int rr = 2 * rp + h, r = tile * 32 + rr;
+          const bool valid = r < nent;
+          w[h] = valid ? v[u][h] : u32x4{};
+          *reinterpret_cast<u32x4*>(lds + X::IQ_OFF + rr * X::IPITCH + col * 16) = w[h];
+          if (col == 0) {
+            int qq, slot;
+            split_entry(valid ? ent_lds[r] : ent_lds[0], a.topk, a.topk_magic, qq, slot);
+            row_lse_s[rr] = valid ? ls[u][h] : 0.f;
+            row_pos[rr] = valid ? (int)min(a.q_offset + qq, (int64_t)a.Nk - 1) : -1;
+            row_q[rr] = qq;
+            row_slot[rr] = slot;
+          }
+        }
+        if constexpr (sizeof(T) == 2) {
+          // element pairs 2i, 2i+1 of the two rows: 2x2 transposes
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int c0 = col * EPC + 2 * i;  // columns c0 and c0 + 1 share the swizzle
+            const int pos = tile_t_chunk<X::SWZ>(c0, rp >> 1) * 8 + (rp & 1) * 4;
+            *reinterpret_cast<uint32_t*>(lds + X::IQT_OFF + c0 * X::TPITCH + pos) =
+                __builtin_amdgcn_perm(w[1][i], w[0][i], 0x05040100u);
+            *reinterpret_cast<uint32_t*>(lds + X::IQT_OFF + (c0 + 1) * X::TPITCH + pos) =
+                __builtin_amdgcn_perm(w[1][i], w[0][i], 0x07060302u);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < EPC; ++e)
+            *reinterpret_cast<uint2*>(lds + X::IQT_OFF + (col * EPC + e) * X::TPITCH + rp * 8) =
+                make_uint2(w[0][e], w[1][e]);
         }
       }
     }
@@ -349,7 +373,7 @@ __global__ void __launch_bounds__(256, 1) k_kl_main(KlArgs a) {
         for (int e = 0; e < 8; ++e) ga[e] = from_f32<T>(gs[8 * aa + e]);
 #pragma unroll
         for (int dt = 0; dt < DI / 32; ++dt)
-          mma(ga, tile_t_frag<T, X::TPITCH>(lds + X::IQT_OFF, 32 * dt + (lane & 31), aa, half), dik[dt]);
+          mma(ga, tile_t_frag<T, X::TPITCH, X::SWZ>(lds + X::IQT_OFF, 32 * dt + (lane & 31), aa, half), dik[dt]);
       }
     }
     __syncthreads();  // g and the KL partials of every wave are in LDS
