@@ -64,7 +64,7 @@ __device__ __forceinline__ void block_tile(const char* lds, const frag_t<T> (&qf
   float mx = -__builtin_huge_valf();
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) mx = max16(s[mt], mx);
-  mx = fmaxf(mx, xor_shfl(mx, 32));
+  mx = pair32_max(mx);
   const float mref = mx == -__builtin_huge_valf() ? 0.f : mx * c_log2;
   float sum = 0.f;
 #pragma unroll
@@ -75,7 +75,7 @@ __device__ __forceinline__ void block_tile(const char* lds, const frag_t<T> (&qf
       s[mt][e] = p;
       sum += p;
     }
-  sum += xor_shfl(sum, 32);
+  sum = pair32_sum(sum);
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -339,7 +339,7 @@ __global__ void __launch_bounds__(256, 2) k_attn_qouter(QoArgs a) {
       if (t >= vis_end) sc[e] = -__builtin_huge_valf();
     }
     float mx = max16(sc);
-    mx = fmaxf(mx, xor_shfl(mx, 32));
+    mx = pair32_max(mx);
     const float mnew = fmaxf(m, mx == -__builtin_huge_valf() ? -__builtin_huge_valf() : mx * a.c_log2);
     const float mref = mnew == -__builtin_huge_valf() ? 0.f : mnew;
     const float alpha = exp2_fast(m - mref);
@@ -350,7 +350,7 @@ __global__ void __launch_bounds__(256, 2) k_attn_qouter(QoArgs a) {
       sc[e] = p;
       sum += p;
     }
-    sum += xor_shfl(sum, 32);
+    sum = pair32_sum(sum);
     l = l * alpha + sum;
     m = mnew;
 #pragma unroll

@@ -293,10 +293,13 @@ __global__ void __launch_bounds__(kTileWaves * 64) k_index_tile(TileArgs a) {
           // max of query q0 + wave*NT*32 + l.
           float own;
           if (NT == 2) {
-            const float give = half ? run[0] : run[1];
-            own = fmaxf(half ? run[1] : run[0], xor_shfl(give, 32));
+            // one v_permlane32_swap: lane l < 32 pairs run[0] of lanes l and
+            // l + 32, lane l >= 32 pairs run[1] of lanes l - 32 and l
+            const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(run[0]), __float_as_uint(run[1]), false,
+                                                            false);
+            own = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
           } else {
-            own = fmaxf(run[0], xor_shfl(run[0], 32));
+            own = pair32_max(run[0]);
           }
           const int jb = j * bpc + mt / bpm;  // blocks arrive in increasing order
           if (jb < L_own) {

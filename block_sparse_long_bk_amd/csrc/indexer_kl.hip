@@ -116,9 +116,9 @@ __global__ void __launch_bounds__(256) k_kl_lse(KlArgs a) {
       }
     // merge the two halves' keys; token 0 of the block is always visible, so
     // half 0 holds a finite maximum
-    const float mo = xor_shfl(m, 32), lo = xor_shfl(l, 32);
-    const float mm = fmaxf(m, mo);
-    const float lt = l * exp2_fast((m - mm) * kLog2e) + lo * exp2_fast((mo - mm) * kLog2e);
+    const float2 mp = lane_pair32(m), lp = lane_pair32(l);  // (half 0's, half 1's)
+    const float mm = fmaxf(mp.x, mp.y);
+    const float lt = lp.x * exp2_fast((mp.x - mm) * kLog2e) + lp.y * exp2_fast((mp.y - mm) * kLog2e);
     if (half == 0 && valid) a.plse[(((int64_t)b * a.Nq + qq) * a.Hkv + g) * a.topk + slot] = mm + __logf(lt);
   }
 }

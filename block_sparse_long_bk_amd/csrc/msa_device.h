@@ -130,6 +130,25 @@ __device__ __forceinline__ void wave_lds_sync() {
 __device__ __forceinline__ float xor_shfl(float v, int mask) { return __shfl_xor(v, mask, kWave); }
 __device__ __forceinline__ int xor_shfl(int v, int mask) { return __shfl_xor(v, mask, kWave); }
 
+// v of lanes l and l ^ 32 as (lower-half lane's, upper-half lane's), from one
+// v_permlane32_swap: lane l < 32 gets (v[l], v[l + 32]), lane l >= 32 gets
+// (v[l - 32], v[l]), with no LDS round trip (a shuffle through ds_bpermute
+// would also make the next LDS wait cover every LDS read in flight).  Both
+// lanes of a pair see the same pair in the same order, so a sum of the two
+// is bitwise equal on both.
+__device__ __forceinline__ float2 lane_pair32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair32_max(float v) {
+  const float2 p = lane_pair32(v);
+  return fmaxf(p.x, p.y);
+}
+__device__ __forceinline__ float pair32_sum(float v) {
+  const float2 p = lane_pair32(v);
+  return p.x + p.y;
+}
+
 // Per-lane list of the KMAX best (score, block id) pairs seen so far, best
 // first; order = score descending, id ascending.  Ids must be offered in
 // increasing order, so a newcomer only passes an entry with a strictly lower
