@@ -18,7 +18,8 @@
 // the (query, head) rows that chose it; msa_invert's lists) with a lane owning
 // a key of the block: S = Q K^T and dP = dO V^T per 32-row tile, dV += P^T dO
 // and dK += dS^T Q accumulated in registers over the item's tiles, and
-// dQ = dS K formed per tile from dS passed through LDS (k_bwd_fused).  dq goes
+// dQ = dS K formed per tile from dS passed through LDS (k_bwd_split for
+// 16-bit inputs, k_bwd_fused for fp32).  dq goes
 // out as one partial per (row, slot), summed in slot order (k_bwd_dq_sum); dk
 // and dv as fp32 partials per item, summed per block in item order
 // (k_bwd_dkdv_reduce).  No atomics.
@@ -192,18 +193,12 @@ struct TileStage {
   }
 };
 
-// NW = 4: wave w owns keys [32w, 32w+32) and all of d.  NW = 8: waves w and
-// w+4 share keys [32(w%4), +32) -- both form S and dP for them, each keeps dK
-// and dV for half of d -- so that two waves per SIMD hide each other's
-// latencies (at 2x the S and dP products); waves 4..7 also stage the next
-// tile while waves 0..3 form dQ.
-template <typename T, int D, int BK, int NW>
-__global__ void __launch_bounds__(NW * 64, 1) k_bwd_fused(BwdArgs a) {
+// fp32 inputs: four waves, wave w owns keys [32w, 32w+32) and all of d.
+template <typename T, int D, int BK>
+__global__ void __launch_bounds__(256, 1) k_bwd_fused(BwdArgs a) {
   using X = FusedLds<T, D, BK>;
-  constexpr int NTHR = NW * 64;
-  constexpr int DSPLIT = NW / 4;          // waves per key group
-  constexpr int DT = D / 32 / DSPLIT;     // dK / dV accumulator tiles per wave
-  constexpr int STG0 = NW == 8 ? 256 : 0;  // first staging thread
+  constexpr int NTHR = 256;
+  constexpr int DT = D / 32;  // dK / dV accumulator tiles per wave
   __shared__ __attribute__((aligned(16))) char lds[X::BYTES];
   __shared__ int32_t ent_lds[kMaxItemEntries];
   __shared__ __attribute__((aligned(16))) float row_lse2[32];
@@ -232,9 +227,7 @@ __global__ void __launch_bounds__(NW * 64, 1) k_bwd_fused(BwdArgs a) {
     st.load_v(kb, tok_stride, j, a.Nk, tid);
     st.store_vt(lds + X::KT_OFF, tid);
   }
-  const int kg = wave % 4, dh = wave / 4;  // key group, half of d (NW = 8)
-  const bool stager = tid >= STG0 && tid < STG0 + 256;
-  const int stid = tid - STG0;
+  const int kg = wave;  // key group
   const int64_t key0 = (int64_t)j * BK;
   const bool has_keys = kg * 32 < BK;  // waves past the block's keys stage and form dQ only
   const int kk = kg * 32 + (lane & 31);
@@ -254,10 +247,8 @@ __global__ void __launch_bounds__(NW * 64, 1) k_bwd_fused(BwdArgs a) {
   }
   __syncthreads();  // ent_lds
   TileStage<T, D> stg;
-  if (stager) {
-    stg.load(a, ent_lds, 0, nrows, b, g, stid);
-    stg.template store<BK>(a, ent_lds, 0, b, g, lds, row_lse2, row_d, row_pos, row_prow, stid);
-  }
+  stg.load(a, ent_lds, 0, nrows, b, g, tid);
+  stg.template store<BK>(a, ent_lds, 0, b, g, lds, row_lse2, row_d, row_pos, row_prow, tid);
   // Every load so far (the key rows included) has landed: without this the
   // compiler's wait before the first use of kf / vf inside the loop also
   // covers the next tile's fetch, which would then no longer overlap.
@@ -267,7 +258,7 @@ __global__ void __launch_bounds__(NW * 64, 1) k_bwd_fused(BwdArgs a) {
   const int ntiles = (nrows + 31) / 32;
   for (int tile = 0; tile < ntiles; ++tile) {
     const bool more = tile + 1 < ntiles;
-    if (more && stager) stg.load(a, ent_lds, tile + 1, nrows, b, g, stid);
+    if (more) stg.load(a, ent_lds, tile + 1, nrows, b, g, tid);
     const int my_pos = row_pos[lane & 31];
     const int64_t my_prow = row_prow[lane & 31];
     if (has_keys) {
@@ -294,8 +285,7 @@ __global__ void __launch_bounds__(NW * 64, 1) k_bwd_fused(BwdArgs a) {
           const float p = my_key <= pp[c] ? exp2_fast(fmaf(s[e], a.c_log2, -l4[c])) : 0.f;
           s[e] = p;
           dp[e] = p * (dp[e] - d4[c]);
-          if (dh == 0)
-            *reinterpret_cast<T*>(lds + X::DS_OFF + (r0 + c) * X::SPITCH + kk * (int)sizeof(T)) = from_f32<T>(dp[e]);
+          *reinterpret_cast<T*>(lds + X::DS_OFF + (r0 + c) * X::SPITCH + kk * (int)sizeof(T)) = from_f32<T>(dp[e]);
         }
       }
       // dV += P^T dO, dK += dS^T Q
@@ -309,14 +299,14 @@ __global__ void __launch_bounds__(NW * 64, 1) k_bwd_fused(BwdArgs a) {
         }
 #pragma unroll
         for (int i = 0; i < DT; ++i) {
-          const int c = 32 * (dh * DT + i) + (lane & 31);
+          const int c = 32 * i + (lane & 31);
           mma(pa, tile_t_frag<T, X::TPITCH, X::SWZ>(lds + X::DOT_OFF, c, aa, half), dvacc[i]);
           mma(sa, tile_t_frag<T, X::TPITCH, X::SWZ>(lds + X::QT_OFF, c, aa, half), dkacc[i]);
         }
       }
     }
     __syncthreads();  // dS complete; the tile's rows are no longer read
-    if (more && stager) stg.template store<BK>(a, ent_lds, tile + 1, b, g, lds, row_lse2, row_d, row_pos, row_prow, stid);
+    if (more) stg.template store<BK>(a, ent_lds, tile + 1, b, g, lds, row_lse2, row_d, row_pos, row_prow, tid);
     if (wave < D / 32) {
       // dQ^T[c][row] = sum over the block's keys of K^T[c][key] dS^T[key][row]
       f32x16 o = f32x16{};
@@ -354,16 +344,193 @@ __global__ void __launch_bounds__(NW * 64, 1) k_bwd_fused(BwdArgs a) {
   }
   if (!has_keys) return;
   // Partials of this item: lane holds key 32 kg + 8(e/4) + 4h + e%4,
-  // d = 32 (dh DT + i) + lane%32.
+  // d = 32 i + lane%32.
   float* dst = a.dkv_part + ((int64_t)bg * a.items_cap + item) * 2 * BK * D;
 #pragma unroll
   for (int i = 0; i < DT; ++i)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int key = kg * 32 + 8 * (e / 4) + 4 * half + (e % 4);
-      const int d = 32 * (dh * DT + i) + (lane & 31);
+      const int d = 32 * i + (lane & 31);
       dst[key * D + d] = dkacc[i][e] * a.scale;
       dst[BK * D + key * D + d] = dvacc[i][e];
+    }
+}
+
+// 16-bit inputs: eight waves, where waves w and w + 4 share keys
+// [32 (w % 4), +32) and split the work by product rather than by d.  Wave w
+// (the P wave) holds the block's K rows, forms S = Q K^T and P, and keeps dV
+// for all of d; wave w + 4 (the dS wave) holds the V rows, forms dP = dO V^T,
+// takes P from LDS (accumulator layout, fp32), forms dS = P (dP - D) and keeps
+// dK for all of d.  Each product is formed once, and each wave holds one set of
+// key rows and one set of accumulators.  Waves 0..3 form dQ after each tile
+// while waves 4..7 write the next tile's rows, fetched before the products.
+template <typename T, int D, int BK>
+__global__ void __launch_bounds__(512, 1) k_bwd_split(BwdArgs a) {
+  static_assert(sizeof(T) == 2, "the split schedule is laid out for 16-bit inputs");
+  using X = FusedLds<T, D, BK>;
+  constexpr int DT = D / 32;  // dK or dV accumulator tiles per wave
+  __shared__ __attribute__((aligned(16))) char lds[X::BYTES];
+  __shared__ int32_t ent_lds[kMaxItemEntries];
+  __shared__ __attribute__((aligned(16))) float row_lse2[32];
+  __shared__ __attribute__((aligned(16))) float row_d[32];
+  __shared__ __attribute__((aligned(16))) int row_pos[32];  // -1 for rows past the item's end
+  __shared__ int64_t row_prow[32];                           // dq partial row: (b, i, h) * topk + slot
+  __shared__ float pex[4][16][64];                           // P of each key group, [e][lane] of the P wave
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
+  const int bg = blockIdx.y, b = bg / a.Hkv, g = bg % a.Hkv;
+  const int n = a.item_count[bg];
+  const int per = (n + 7) / 8;
+  const int x = blockIdx.x;
+  const int item = (x % 8) * per + x / 8;  // each XCD runs a contiguous run of items
+  if (x / 8 >= per || item >= n) return;
+  const int4 it = a.items[(int64_t)bg * a.items_cap + item];
+  const int j = it.x, e0 = it.y, e1 = it.z;
+  const int nrows = (e1 - e0) * a.G;
+  const int nent = e1 - e0;
+  const int32_t* ent = a.entries + (int64_t)bg * a.Nq * a.topk + e0;
+  for (int u = tid; u < nent; u += 512) ent_lds[u] = ent[u];
+
+  const int64_t tok_stride = (int64_t)a.Hkv * D;
+  const T* kb = static_cast<const T*>(a.k) + (int64_t)b * a.Nk * tok_stride + g * D;
+  const T* vb = static_cast<const T*>(a.v) + (int64_t)b * a.Nk * tok_stride + g * D;
+  if (tid < 256) {
+    KvStage<T, D, BK> st;
+    st.load_v(kb, tok_stride, j, a.Nk, tid);
+    st.store_vt(lds + X::KT_OFF, tid);
+  }
+  const int kg = wave % 4, role = wave / 4;  // key group; 0 = P wave, 1 = dS wave
+  const bool stager = role == 1;
+  const int stid = tid - 256;
+  const int64_t key0 = (int64_t)j * BK;
+  const bool has_keys = kg * 32 < BK;  // waves past the block's keys stage and form dQ only
+  const int kk = kg * 32 + (lane & 31);
+  const int64_t my_key = key0 + kk;
+  const int64_t kt = min(my_key, (int64_t)a.Nk - 1);  // keys past n_k are masked below
+  const T* rb = role ? vb : kb;
+  frag_t<T> kv[D / 16];  // K rows (P wave) or V rows (dS wave) as B operands
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) kv[ks] = load8(rb + kt * tok_stride + 8 * half + 16 * ks);
+  f32x16 acc[DT];  // dV (P wave) or dK (dS wave)
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
+  __syncthreads();  // ent_lds
+  TileStage<T, D> stg;
+  if (stager) {
+    stg.load(a, ent_lds, 0, nrows, b, g, stid);
+    stg.template store<BK>(a, ent_lds, 0, b, g, lds, row_lse2, row_d, row_pos, row_prow, stid);
+  }
+  // Every load so far (the key rows included) has landed: without this the
+  // compiler's wait before the first use of kv inside the loop also covers
+  // the next tile's fetch, which would then no longer overlap.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  const int ntiles = (nrows + 31) / 32;
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const bool more = tile + 1 < ntiles;
+    if (more && stager) stg.load(a, ent_lds, tile + 1, nrows, b, g, stid);
+    const int my_pos = row_pos[lane & 31];
+    const int64_t my_prow = row_prow[lane & 31];
+    // S = Q K^T (P wave) or dP = dO V^T (dS wave): lane = key, accumulator rows = tile rows
+    f32x16 xs = f32x16{};
+    if (has_keys) {
+      const T* xr = reinterpret_cast<const T*>(lds + (role ? X::DO_OFF : X::Q_OFF) + (lane & 31) * X::RPITCH) + 8 * half;
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) mma(load8(xr + 16 * ks), kv[ks], xs);
+      if (role == 0) {
+        // P in place; accumulator position e is tile row 8(e/4) + 4h + e%4
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int r0 = 8 * q4 + 4 * half;
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(row_lse2 + r0);
+          const int4 p4 = *reinterpret_cast<const int4*>(row_pos + r0);
+          const int pp[4] = {p4.x, p4.y, p4.z, p4.w};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int e = 4 * q4 + c;
+            const float p = my_key <= pp[c] ? exp2_fast(fmaf(xs[e], a.c_log2, -l4[c])) : 0.f;
+            xs[e] = p;
+            pex[kg][e][lane] = p;
+          }
+        }
+      }
+    }
+    __syncthreads();  // P of every key group is in LDS
+    if (has_keys) {
+      if (role == 1) {
+        // dS = P (dP - D) in place, and to LDS as [row][key] for dQ
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int r0 = 8 * q4 + 4 * half;
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(row_d + r0);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int e = 4 * q4 + c;
+            xs[e] = pex[kg][e][lane] * (xs[e] - d4[c]);
+            *reinterpret_cast<T*>(lds + X::DS_OFF + (r0 + c) * X::SPITCH + kk * (int)sizeof(T)) = from_f32<T>(xs[e]);
+          }
+        }
+      }
+      // dV += P^T dO (P wave), dK += dS^T Q (dS wave)
+      const char* tt = lds + (role ? X::QT_OFF : X::DOT_OFF);
+#pragma unroll
+      for (int aa = 0; aa < 2; ++aa) {
+        frag_t<T> xa;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xa[e] = from_f32<T>(xs[8 * aa + e]);
+#pragma unroll
+        for (int i = 0; i < DT; ++i)
+          mma(xa, tile_t_frag<T, X::TPITCH, X::SWZ>(tt, 32 * i + (lane & 31), aa, half), acc[i]);
+      }
+    }
+    __syncthreads();  // dS complete; the tile's rows and P are no longer read
+    if (more && stager) stg.template store<BK>(a, ent_lds, tile + 1, b, g, lds, row_lse2, row_d, row_pos, row_prow, stid);
+    if (wave < D / 32) {
+      // dQ^T[c][row] = sum over the block's keys of K^T[c][key] dS^T[key][row]
+      f32x16 o = f32x16{};
+      const int c = 32 * wave + (lane & 31);
+      const T* srow = reinterpret_cast<const T*>(lds + X::DS_OFF + (lane & 31) * X::SPITCH);
+#pragma unroll
+      for (int mt = 0; mt < BK / 32; ++mt)
+#pragma unroll
+        for (int aa = 0; aa < 2; ++aa) {
+          const frag_t<T> ka = vt_frag_at<T, D, BK>(lds + X::KT_OFF, c, mt, aa, half);
+          const int k0 = 32 * mt + 16 * aa + 4 * half;
+          const typename Pack4<T>::type lo = *reinterpret_cast<const typename Pack4<T>::type*>(srow + k0);
+          const typename Pack4<T>::type hi = *reinterpret_cast<const typename Pack4<T>::type*>(srow + k0 + 8);
+          frag_t<T> sb;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            sb[e] = lo[e];
+            sb[4 + e] = hi[e];
+          }
+          mma(ka, sb, o);
+        }
+      if (my_pos >= 0) {
+        // o[e]: d = 32 w + 8(e/4) + 4h + e%4 of row lane%32
+        T* dst = static_cast<T*>(a.dq_part) + my_prow * D + 32 * wave + 4 * half;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          typename Pack4<T>::type w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = from_f32<T>(o[4 * i + e] * a.scale);
+          *reinterpret_cast<typename Pack4<T>::type*>(dst + 8 * i) = w;
+        }
+      }
+    }
+    __syncthreads();  // the next tile's rows are in LDS; dS is no longer read
+  }
+  if (!has_keys) return;
+  // Partials of this item: lane holds key 32 kg + 8(e/4) + 4h + e%4, d = 32 i + lane%32.
+  float* dst = a.dkv_part + ((int64_t)bg * a.items_cap + item) * 2 * BK * D + (role ? 0 : BK * D);
+  const float f = role ? a.scale : 1.f;
+#pragma unroll
+  for (int i = 0; i < DT; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int key = kg * 32 + 8 * (e / 4) + 4 * half + (e % 4);
+      dst[key * D + 32 * i + (lane & 31)] = acc[i][e] * f;
     }
 }
 
@@ -458,9 +625,8 @@ void bwd_launch_bk(const Shape& s, const BwdArgs& a, const InvertPlan& p, const 
                    hipStream_t st, int kid_main, int kid_sum, int kid_red) {
   const dim3 grid(p.items_cap, s.B * s.Hkv);
   prof_begin(st, kid_main);
-  // Eight waves where two per SIMD fit in the registers (16-bit inputs).
-  constexpr int NW = sizeof(T) == 2 ? 8 : 4;
-  hipLaunchKernelGGL((k_bwd_fused<T, D, BK, NW>), grid, dim3(NW * 64), 0, st, a);
+  if constexpr (sizeof(T) == 2) hipLaunchKernelGGL((k_bwd_split<T, D, BK>), grid, dim3(512), 0, st, a);
+  else hipLaunchKernelGGL((k_bwd_fused<T, D, BK>), grid, dim3(256), 0, st, a);
   prof_end(st, kid_main);
   const int64_t nrows = (int64_t)s.B * s.Nq * s.Hq;
   const int rpb = 4 * (64 / (D / 8));
