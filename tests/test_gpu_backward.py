@@ -49,6 +49,8 @@ CASES = {
     "f32_d128_bk64": dict(n_q=900, n_k=900, h_q=8, h_kv=2, d=128, d_idx=32, topk=6, block_size=64),
     "bf16_bk32_offset": dict(dtype="bf16", n_q=300, n_k=2050, q_offset=1750, h_q=8, h_kv=1, d=128, d_idx=64,
                              topk=12, block_size=32),
+    "bf16_g1_d128": dict(dtype="bf16", n_q=700, n_k=700, h_q=4, h_kv=4, d=128, d_idx=128, topk=5),
+    "bf16_g16_d128": dict(dtype="bf16", n_q=600, n_k=600, h_q=16, h_kv=1, d=128, d_idx=64, topk=4),
 }
 NAMES = sorted(CASES)
 _cache = {}

@@ -47,6 +47,11 @@ CASES = {
     "f32_bk32": dict(n_q=700, n_k=700, h_q=8, h_kv=2, d=64, d_idx=32, topk=6, block_size=32),
     "bf16_bk32_offset": dict(dtype="bf16", n_q=300, n_k=2050, q_offset=1750, h_q=8, h_kv=1, d=128, d_idx=64,
                              topk=12, block_size=32),
+    # group sizes around the head chunks of the 16-bit pass: one head (the odd-head waves idle), two heads, and
+    # sixteen heads of d 128 (several chunks per tile)
+    "bf16_g1_d128": dict(dtype="bf16", n_q=700, n_k=700, h_q=4, h_kv=4, d=128, d_idx=128, topk=5),
+    "bf16_g2_bk64": dict(dtype="bf16", n_q=800, n_k=800, h_q=4, h_kv=2, d=64, d_idx=128, topk=6, block_size=64),
+    "bf16_g16_d128": dict(dtype="bf16", n_q=600, n_k=600, h_q=16, h_kv=1, d=128, d_idx=64, topk=4),
 }
 NAMES = sorted(CASES)
 LOSS_SCALE = 0.5
