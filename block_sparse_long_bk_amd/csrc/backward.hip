@@ -537,7 +537,7 @@ __global__ void __launch_bounds__(512, 1) k_bwd_split(BwdArgs a) {
 // ---- dq = sum of the slot partials, in slot order ---------------------------
 template <typename T, int D>
 __global__ void __launch_bounds__(256) k_bwd_dq_sum(const T* __restrict__ part, const int32_t* __restrict__ ids,
-                                                    T* __restrict__ dq, int Nq, int Hq, int Hkv, int G, int topk,
+                                                    T* __restrict__ dq, int Hq, int Hkv, int G, int topk,
                                                     int64_t nrows) {
   constexpr int LPR = D / 8;
   const int lane = threadIdx.x & 63;
@@ -632,8 +632,8 @@ void bwd_launch_bk(const Shape& s, const BwdArgs& a, const InvertPlan& p, const 
   const int rpb = 4 * (64 / (D / 8));
   prof_begin(st, kid_sum);
   hipLaunchKernelGGL((k_bwd_dq_sum<T, D>), dim3((unsigned)((nrows + rpb - 1) / rpb)), dim3(256), 0, st,
-                     static_cast<const T*>(a.dq_part), static_cast<const int32_t*>(ids), static_cast<T*>(dq), s.Nq,
-                     s.Hq, s.Hkv, s.Hq / s.Hkv, s.topk, nrows);
+                     static_cast<const T*>(a.dq_part), static_cast<const int32_t*>(ids), static_cast<T*>(dq), s.Hq,
+                     s.Hkv, s.Hq / s.Hkv, s.topk, nrows);
   prof_end(st, kid_sum);
   const int64_t nthr = (int64_t)s.nblk * BK * (D / 8);
   prof_begin(st, kid_red);

@@ -547,7 +547,6 @@ __global__ void __launch_bounds__(512, 1) k_kl_main8(KlArgs a) {
   const bool has_keys = kg * 32 < BK;
   const int kk = kg * 32 + (lane & 31);                 // this lane's key in the block
   const int64_t my_key = key0 + kk;
-  const int64_t kt = min(my_key, (int64_t)a.Nk - 1);    // keys past n_k are masked below
   // this lane's Main Branch key row in LDS (B operands of the score products;
   // the index keys are read from the transposed copy when needed)
   const T* krow = reinterpret_cast<const T*>(lds + X::K_OFF + kk * X::KPITCH) + 8 * half;
