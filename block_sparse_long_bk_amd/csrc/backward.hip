@@ -550,11 +550,22 @@ __global__ void __launch_bounds__(256) k_bwd_dq_sum(const T* __restrict__ part, 
   float acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-  for (int s = 0; s < topk; ++s) {
-    if (sel[s] < 0) continue;
-    const frag_t<T> x = load8(p + (int64_t)s * D);
+  // Eight slots per round, all their loads issued before any is used (a
+  // slot past topk re-reads the last one, an unselected slot is read and not
+  // added); the sum runs in slot order.
+  for (int s0 = 0; s0 < topk; s0 += 8) {
+    frag_t<T> x[8];
+    bool ok[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] += to_f32(x[e]);
+    for (int u = 0; u < 8; ++u) {
+      const int sl = min(s0 + u, topk - 1);
+      ok[u] = s0 + u < topk && sel[sl] >= 0;
+      x[u] = load8(p + (int64_t)sl * D);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = ok[u] ? acc[e] + to_f32(x[u][e]) : acc[e];
   }
   frag_t<T> o;
 #pragma unroll
