@@ -414,7 +414,16 @@ __global__ void __launch_bounds__(512, 1) k_bwd_split(BwdArgs a) {
   f32x16 acc[DT];  // dV (P wave) or dK (dS wave)
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
-  __syncthreads();  // ent_lds
+  __syncthreads();  // ent_lds, K^T
+  // The P waves (0..3) also form dQ^T = K^T dS^T; their K^T fragments (A
+  // operands, columns 32 w.. of d) are the same for every tile of the item.
+  frag_t<T> ktf[BK / 32][2];
+  if (wave < D / 32) {
+#pragma unroll
+    for (int mt = 0; mt < BK / 32; ++mt)
+#pragma unroll
+      for (int aa = 0; aa < 2; ++aa) ktf[mt][aa] = vt_frag_at<T, D, BK>(lds + X::KT_OFF, 32 * wave + (lane & 31), mt, aa, half);
+  }
   TileStage<T, D> stg;
   if (stager) {
     stg.load(a, ent_lds, 0, nrows, b, g, stid);
@@ -495,7 +504,7 @@ __global__ void __launch_bounds__(512, 1) k_bwd_split(BwdArgs a) {
       for (int mt = 0; mt < BK / 32; ++mt)
 #pragma unroll
         for (int aa = 0; aa < 2; ++aa) {
-          const frag_t<T> ka = vt_frag_at<T, D, BK>(lds + X::KT_OFF, c, mt, aa, half);
+          const frag_t<T> ka = ktf[mt][aa];
           const int k0 = 32 * mt + 16 * aa + 4 * half;
           const typename Pack4<T>::type lo = *reinterpret_cast<const typename Pack4<T>::type*>(srow + k0);
           const typename Pack4<T>::type hi = *reinterpret_cast<const typename Pack4<T>::type*>(srow + k0 + 8);
