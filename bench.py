@@ -307,8 +307,8 @@ def main():
                     help="also run one plain device copy of this many MiB (reference for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: the MSA forward path here is a single-GPU build "
-              "(see DESIGN.md for how it would shard); --gpus must be 1", file=sys.stderr)
+        print("bench.py runs on exactly one GPU: this MSA forward path is built and measured on a single GPU "
+              "(one GPU's share of the work at its real shape); --gpus must be 1", file=sys.stderr)
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
 
