@@ -61,8 +61,7 @@ __global__ void __launch_bounds__(256) k_bwd_rowdot(const T* __restrict__ out, c
   float acc = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc = fmaf(to_f32(o[e]), to_f32(g[e]), acc);
-#pragma unroll
-  for (int m = LPR / 2; m >= 1; m >>= 1) acc += xor_shfl(acc, m);
+  acc = group_sum<LPR>(acc);
   if (lane % LPR == 0) drow[row] = acc;
 }
 

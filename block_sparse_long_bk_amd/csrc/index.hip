@@ -433,8 +433,7 @@ __global__ void __launch_bounds__(kScanThreads) k_index_scan(ScanArgs a) {
 #pragma unroll
             for (int e = 0; e < EPL; ++e) acc = fmaf(kf[e], qv[e], acc);
             if constexpr (MX) acc = __builtin_ldexpf(acc, (int)xs[u] - 127);
-#pragma unroll
-            for (int m = C / 2; m >= 1; m >>= 1) acc += xor_shfl(acc, m);
+            acc = group_sum<C>(acc);
             if (c == 0 && it0 + u < iters) dots[(qi * H + grp) * kChunk + tok] = acc;
           }
         }

@@ -420,9 +420,7 @@ __global__ void __launch_bounds__(256, 1) k_kl_main(KlArgs a) {
         const f32x4 t4 = *reinterpret_cast<const f32x4*>(trow + u);
         acc += (t4[0] + t4[1]) + (t4[2] + t4[3]);
       }
-      acc += xor_shfl(acc, 1);
-      acc += xor_shfl(acc, 2);
-      acc += xor_shfl(acc, 4);
+      acc = group_sum<8>(acc);
       if (part == 0 && row_pos[rr] >= 0)
         a.kl_part[(((int64_t)b * a.Nq + row_q[rr]) * a.Hkv + g) * a.topk + row_slot[rr]] = acc;
     }
@@ -801,9 +799,7 @@ __global__ void __launch_bounds__(512, 1) k_kl_main8(KlArgs a) {
         const f32x4 t4 = *reinterpret_cast<const f32x4*>(trow + u);
         acc += (t4[0] + t4[1]) + (t4[2] + t4[3]);
       }
-      acc += xor_shfl(acc, 1);
-      acc += xor_shfl(acc, 2);
-      acc += xor_shfl(acc, 4);
+      acc = group_sum<8>(acc);
       if (part == 0 && row_pos[rr] >= 0)
         a.kl_part[(((int64_t)b * a.Nq + row_q[rr]) * a.Hkv + g) * a.topk + row_slot[rr]] = acc;
     }

@@ -149,6 +149,21 @@ __device__ __forceinline__ float pair32_sum(float v) {
   return p.x + p.y;
 }
 
+// Sum over aligned groups of C lanes (C in {1, 2, 4, 8, 16}); every lane of a
+// group gets the group's total.  DPP lane moves within rows of 16 lanes (no
+// LDS): swap neighbours, swap lane pairs, then add the mirror image within 8
+// and within 16 lanes -- the mirror of a lane lies in the other half of its
+// group, whose total it already holds, and both lanes add the same two values.
+template <int C>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(C == 1 || C == 2 || C == 4 || C == 8 || C == 16, "groups of 1..16 lanes");
+  if constexpr (C >= 2) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
+  if constexpr (C >= 4) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
+  if constexpr (C >= 8) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true));
+  if constexpr (C >= 16) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, true));
+  return v;
+}
+
 // Per-lane list of the KMAX best (score, block id) pairs seen so far, best
 // first; order = score descending, id ascending.  Ids must be offered in
 // increasing order, so a newcomer only passes an entry with a strictly lower
