@@ -451,15 +451,29 @@ __global__ void __launch_bounds__(256) k_combine(CombArgs a) {
   const int64_t prow = ((int64_t)b * a.nq + qq) * a.Hq + h;
   const int32_t* sel = a.ids + (((int64_t)b * a.Nq + a.q0 + qq) * a.Hkv + g) * a.topk;
   const float* pl = a.part_lse + ((int64_t)b * a.nq + qq) * a.S * a.Hq + h;
-  // All slot statistics are loaded at once (S <= SMAX).
+  // All slot statistics are loaded at once (S <= SMAX); the slot ids four at
+  // a time where a row of them is 16-byte aligned (topk a multiple of 4).
+  int idv[SMAX];
+  if (a.ids_slots && (a.topk & 3) == 0) {
+#pragma unroll
+    for (int s4 = 0; s4 < SMAX / 4; ++s4) {
+      const int4 t = 4 * s4 < a.S ? *reinterpret_cast<const int4*>(sel + 4 * s4) : int4{0, 0, 0, 0};
+      idv[4 * s4] = t.x;
+      idv[4 * s4 + 1] = t.y;
+      idv[4 * s4 + 2] = t.z;
+      idv[4 * s4 + 3] = t.w;
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < SMAX; ++s) idv[s] = a.ids_slots && s < a.S ? sel[s] : 0;
+  }
   float ls[SMAX];
 #pragma unroll
   for (int s = 0; s < SMAX; ++s) {
     ls[s] = -__builtin_huge_valf();
     if (s < a.S) {
-      const int id = a.ids_slots ? sel[s] : 0;
       const float x = pl[(int64_t)s * a.Hq];
-      if (id >= 0) ls[s] = x;
+      if (idv[s] >= 0) ls[s] = x;
     }
   }
   float M = -__builtin_huge_valf();
