@@ -83,38 +83,58 @@ __global__ void __launch_bounds__(256) k_kl_lse(KlArgs a) {
   }
   __syncthreads();
   const int64_t key0 = (int64_t)j * BK;
+  // The index query rows of a wave's next tile are fetched while the current
+  // one is scored (rows past the item's end read entry 0's row).
+  auto fetch = [&](int tile, frag_t<T> (&qf)[DI / 16]) {
+    const int r = tile * 32 + (lane & 31);
+    int qq, slot;
+    split_entry(r < nent ? ent_lds[r] : ent_lds[0], a.topk, a.topk_magic, qq, slot);
+    const T* iqr = static_cast<const T*>(a.iq) + (((int64_t)b * a.Nq + qq) * a.Hkv + g) * DI + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < DI / 16; ++ks) qf[ks] = load8(iqr + 16 * ks);
+  };
+  frag_t<T> qnext[DI / 16];
+  if (wave * 32 < nent) fetch(wave, qnext);
   for (int tile = wave; tile * 32 < nent; tile += 4) {
     const int r = tile * 32 + (lane & 31);
     const bool valid = r < nent;
     int qq, slot;
     split_entry(valid ? ent_lds[r] : ent_lds[0], a.topk, a.topk_magic, qq, slot);
-    const T* iqr = static_cast<const T*>(a.iq) + (((int64_t)b * a.Nq + qq) * a.Hkv + g) * DI + 8 * half;
     frag_t<T> qf[DI / 16];
 #pragma unroll
-    for (int ks = 0; ks < DI / 16; ++ks) qf[ks] = load8(iqr + 16 * ks);
+    for (int ks = 0; ks < DI / 16; ++ks) qf[ks] = qnext[ks];
+    if ((tile + 4) * 32 < nent) fetch(tile + 4, qnext);
     const int64_t pos = a.q_offset + qq;
     const int vis = (int)max((int64_t)0, min((int64_t)BK, min(pos + 1, (int64_t)a.Nk) - key0));
+    // online over the M-tiles (one 32-key tile of scores live at a time); the
+    // key fragments are read anew per tile (kept over the loop they would
+    // hold 128 registers and leave one wave per SIMD)
+    asm volatile("" ::: "memory");
     float m = -__builtin_huge_valf(), l = 0.f;
-    f32x16 s[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const T* kr = reinterpret_cast<const T*>(lds + (mt * 32 + (lane & 31)) * L::KPITCH) + 8 * half;
-      s[mt] = mma0(load8(kr), qf[0]);
+      f32x16 s = mma0(load8(kr), qf[0]);
 #pragma unroll
-      for (int ks = 1; ks < DI / 16; ++ks) mma(load8(kr + 16 * ks), qf[ks], s[mt]);
+      for (int ks = 1; ks < DI / 16; ++ks) mma(load8(kr + 16 * ks), qf[ks], s);
+      float mt_max = -__builtin_huge_valf();
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int t = 32 * mt + 8 * (e / 4) + 4 * half + (e % 4);
-        if (t < vis) m = fmaxf(m, s[mt][e]);
+        if (t < vis) mt_max = fmaxf(mt_max, s[e]);
+      }
+      const float mn = fmaxf(m, mt_max);
+      if (mn != -__builtin_huge_valf()) {
+        float add = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int t = 32 * mt + 8 * (e / 4) + 4 * half + (e % 4);
+          if (t < vis) add += exp2_fast((s[e] - mn) * kLog2e);
+        }
+        l = (m == -__builtin_huge_valf() ? 0.f : l * exp2_fast((m - mn) * kLog2e)) + add;
+        m = mn;
       }
     }
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int t = 32 * mt + 8 * (e / 4) + 4 * half + (e % 4);
-        if (t < vis) l += exp2_fast((s[mt][e] - m) * kLog2e);
-      }
     // merge the two halves' keys; token 0 of the block is always visible, so
     // half 0 holds a finite maximum
     const float2 mp = lane_pair32(m), lp = lane_pair32(l);  // (half 0's, half 1's)
