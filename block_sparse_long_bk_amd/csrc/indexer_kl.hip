@@ -42,7 +42,7 @@ struct KlArgs {
   float* plse;           // [B, Nq, Hkv, topk] partial index lse per slot
   float* lse_s;          // [B, Nq, Hkv]
   float* kl_part;        // [B, Nq, Hkv, topk]
-  float* diq_part;       // [B, Nq, Hkv, topk, DI]
+  void* diq_part;        // [B, Nq, Hkv, topk, DI] in the input type
   float* dik_part;       // [B*Hkv][items_cap][BK][DI]
   int Nq, Nk, Hq, Hkv, G, topk, items_cap;
   int64_t q_offset;
@@ -422,11 +422,15 @@ __global__ void __launch_bounds__(256, 1) k_kl_main(KlArgs a) {
         }
       const int rr = lane & 31;
       if (row_pos[rr] >= 0) {
-        float* dst = a.diq_part + ((((int64_t)b * a.Nq + row_q[rr]) * a.Hkv + g) * a.topk + row_slot[rr]) * DI;
+        T* dst = static_cast<T*>(a.diq_part) +
+                 ((((int64_t)b * a.Nq + row_q[rr]) * a.Hkv + g) * a.topk + row_slot[rr]) * DI;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          *reinterpret_cast<f32x4*>(dst + 32 * wave + 8 * i + 4 * half) =
-              f32x4{o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]};
+        for (int i = 0; i < 4; ++i) {
+          typename Pack4<T>::type w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = from_f32<T>(o[4 * i + e]);
+          *reinterpret_cast<typename Pack4<T>::type*>(dst + 32 * wave + 8 * i + 4 * half) = w;
+        }
       }
     }
     {
@@ -801,11 +805,15 @@ __global__ void __launch_bounds__(512, 1) k_kl_main8(KlArgs a) {
         }
       const int rr = lane & 31;
       if (row_pos[rr] >= 0) {
-        float* dst = a.diq_part + ((((int64_t)b * a.Nq + row_q[rr]) * a.Hkv + g) * a.topk + row_slot[rr]) * DI;
+        T* dst = static_cast<T*>(a.diq_part) +
+                 ((((int64_t)b * a.Nq + row_q[rr]) * a.Hkv + g) * a.topk + row_slot[rr]) * DI;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          *reinterpret_cast<f32x4*>(dst + 32 * kg + 8 * i + 4 * half) =
-              f32x4{o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]};
+        for (int i = 0; i < 4; ++i) {
+          typename Pack4<T>::type w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = from_f32<T>(o[4 * i + e]);
+          *reinterpret_cast<typename Pack4<T>::type*>(dst + 32 * kg + 8 * i + 4 * half) = w;
+        }
       }
     }
     if (tid < 256) {
@@ -842,7 +850,7 @@ __global__ void __launch_bounds__(512, 1) k_kl_main8(KlArgs a) {
 // ---- kl and d iq per (query, group): slot partials in slot order ------------
 template <typename T, int DI>
 __global__ void __launch_bounds__(256) k_kl_finish(const float* __restrict__ kl_part,
-                                                   const float* __restrict__ diq_part,
+                                                   const T* __restrict__ diq_part,
                                                    const int32_t* __restrict__ ids, float* __restrict__ kl,
                                                    T* __restrict__ d_iq, int topk, int64_t nrows) {
   constexpr int LPR = DI / 8;
@@ -850,20 +858,16 @@ __global__ void __launch_bounds__(256) k_kl_finish(const float* __restrict__ kl_
   const int64_t row = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * (64 / LPR) + lane / LPR;  // (b, i, g)
   if (row >= nrows) return;
   const int32_t* sel = ids + row * topk;
-  const float* p = diq_part + row * topk * DI + (lane % LPR) * 8;
+  const T* p = diq_part + row * topk * DI + (lane % LPR) * 8;
   float acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
   float kacc = 0.f;
   for (int s = 0; s < topk; ++s) {
     if (sel[s] < 0) continue;
-    const f32x4 lo = *reinterpret_cast<const f32x4*>(p + (int64_t)s * DI);
-    const f32x4 hi = *reinterpret_cast<const f32x4*>(p + (int64_t)s * DI + 4);
+    const frag_t<T> x = load8(p + (int64_t)s * DI);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc[e] += lo[e];
-      acc[4 + e] += hi[e];
-    }
+    for (int e = 0; e < 8; ++e) acc[e] += to_f32(x[e]);
     kacc += kl_part[row * topk + s];
   }
   if (lane % LPR == 0) kl[row] = kacc;
@@ -943,7 +947,7 @@ void kl_launch_bk(const Shape& s, const KlArgs& a, const InvertPlan& p, float* k
   const int rpb = 4 * (64 / (DI / 8));
   prof_begin(st, kid.finish);
   hipLaunchKernelGGL((k_kl_finish<T, DI>), dim3((unsigned)((nrows + rpb - 1) / rpb)), dim3(256), 0, st, a.kl_part,
-                     a.diq_part, a.ids, kl, static_cast<T*>(d_iq), s.topk, nrows);
+                     static_cast<const T*>(a.diq_part), a.ids, kl, static_cast<T*>(d_iq), s.topk, nrows);
   prof_end(st, kid.finish);
   const int64_t nthr = (int64_t)s.nblk * BK * (DI / 8);
   prof_begin(st, kid.reduce);
@@ -982,7 +986,7 @@ size_t kl_bytes(const Shape& s, const InvertPlan& p, KlWorkspace* w) {
   L.kl_part = off;
   off += up(rows * s.topk * 4);
   L.diq_part = off;
-  off += up(rows * s.topk * s.DI * 4);
+  off += up(rows * s.topk * s.DI * (s.dtype == kBF16 ? 2 : 4));  // in the input type
   L.dik_part = off;
   off += up((size_t)s.B * s.Hkv * p.items_cap * s.Bk * s.DI * 4);
   if (w) *w = L;
@@ -1009,7 +1013,7 @@ hipError_t launch_indexer_kl(const Shape& s, const InvertPlan& p, const void* q,
   a.plse = reinterpret_cast<float*>(ws + L.plse);
   a.lse_s = reinterpret_cast<float*>(ws + L.lse_s);
   a.kl_part = reinterpret_cast<float*>(ws + L.kl_part);
-  a.diq_part = reinterpret_cast<float*>(ws + L.diq_part);
+  a.diq_part = ws + L.diq_part;
   a.dik_part = reinterpret_cast<float*>(ws + L.dik_part);
   a.Nq = s.Nq;
   a.Nk = s.Nk;

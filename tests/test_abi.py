@@ -144,4 +144,4 @@ def test_workspace_sizes():
     assert bwd == bwd_least >= 32768 * 64 * 16 * 128 * 2
     # indexer loss: fp32 d_iq partials per (query, group, slot)
     klw, klw_least = api.workspace_size(pre, api.OP_INDEXER_KL)
-    assert klw == klw_least >= 32768 * 8 * 16 * 128 * 4
+    assert klw == klw_least >= 32768 * 8 * 16 * 128 * 2  # d idx_q partials in bf16
