@@ -39,7 +39,7 @@ struct BwdArgs {
   const int32_t* item_count;
   const int4* items;
   void* dq_part;         // [B, Nq, Hq, topk, D] in the input type
-  float* dkv_part;       // [B*Hkv][items_cap][2][BK][D] fp32 (dk, then dv)
+  void* dkv_part;        // [B*Hkv][items_cap][2][BK][D] in the input type (dk, then dv)
   void* trash;           // scratch line for the stores of rows past an item's end
   int Nq, Nk, Hq, Hkv, G, topk, items_cap, gshift;
   int64_t q_offset;
@@ -344,15 +344,15 @@ __global__ void __launch_bounds__(256, 1) k_bwd_fused(BwdArgs a) {
   if (!has_keys) return;
   // Partials of this item: lane holds key 32 kg + 8(e/4) + 4h + e%4,
   // d = 32 i + lane%32.
-  float* dst = a.dkv_part + ((int64_t)bg * a.items_cap + item) * 2 * BK * D;
+  T* dst = static_cast<T*>(a.dkv_part) + ((int64_t)bg * a.items_cap + item) * 2 * BK * D;
 #pragma unroll
   for (int i = 0; i < DT; ++i)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int key = kg * 32 + 8 * (e / 4) + 4 * half + (e % 4);
       const int d = 32 * i + (lane & 31);
-      dst[key * D + d] = dkacc[i][e] * a.scale;
-      dst[BK * D + key * D + d] = dvacc[i][e];
+      dst[key * D + d] = from_f32<T>(dkacc[i][e] * a.scale);
+      dst[BK * D + key * D + d] = from_f32<T>(dvacc[i][e]);
     }
 }
 
@@ -531,14 +531,14 @@ __global__ void __launch_bounds__(512, 1) k_bwd_split(BwdArgs a) {
   }
   if (!has_keys) return;
   // Partials of this item: lane holds key 32 kg + 8(e/4) + 4h + e%4, d = 32 i + lane%32.
-  float* dst = a.dkv_part + ((int64_t)bg * a.items_cap + item) * 2 * BK * D + (role ? 0 : BK * D);
+  T* dst = static_cast<T*>(a.dkv_part) + ((int64_t)bg * a.items_cap + item) * 2 * BK * D + (role ? 0 : BK * D);
   const float f = role ? a.scale : 1.f;
 #pragma unroll
   for (int i = 0; i < DT; ++i)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int key = kg * 32 + 8 * (e / 4) + 4 * half + (e % 4);
-      dst[key * D + 32 * i + (lane & 31)] = acc[i][e] * f;
+      dst[key * D + 32 * i + (lane & 31)] = from_f32<T>(acc[i][e] * f);
     }
 }
 
@@ -591,7 +591,7 @@ __global__ void __launch_bounds__(256) k_bwd_dq_sum(const T* __restrict__ part, 
 // One thread per (token of the block, 8 channels); blocks no query selected
 // (and tokens no query can see) get zeros.
 template <typename T, int D, int BK>
-__global__ void __launch_bounds__(256) k_bwd_dkdv_reduce(const float* __restrict__ part, const int4* __restrict__ items,
+__global__ void __launch_bounds__(256) k_bwd_dkdv_reduce(const T* __restrict__ part, const int4* __restrict__ items,
                                                          const int32_t* __restrict__ item_count, T* __restrict__ dk,
                                                          T* __restrict__ dv, int Nk, int Hkv, int nblk, int items_cap) {
   constexpr int CH = D / 8;
@@ -614,11 +614,12 @@ __global__ void __launch_bounds__(256) k_bwd_dkdv_reduce(const float* __restrict
 #pragma unroll
   for (int e = 0; e < 8; ++e) ak[e] = av[e] = 0.f;
   for (int u = lo; u < n && its[u].x == j; ++u) {
-    const float* p = part + ((int64_t)bg * items_cap + u) * 2 * BK * D + tk * D + c * 8;
+    const T* p = part + ((int64_t)bg * items_cap + u) * 2 * BK * D + tk * D + c * 8;
+    const frag_t<T> xk = load8(p), xv = load8(p + BK * D);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      ak[e] += p[e];
-      av[e] += p[BK * D + e];
+      ak[e] += to_f32(xk[e]);
+      av[e] += to_f32(xv[e]);
     }
   }
   frag_t<T> ok, ov;
@@ -657,7 +658,7 @@ void bwd_launch_bk(const Shape& s, const BwdArgs& a, const InvertPlan& p, const 
   const int64_t nthr = (int64_t)s.nblk * BK * (D / 8);
   prof_begin(st, kid_red);
   hipLaunchKernelGGL((k_bwd_dkdv_reduce<T, D, BK>), dim3((unsigned)((nthr + 255) / 256), s.B * s.Hkv), dim3(256), 0,
-                     st, a.dkv_part, a.items, a.item_count, static_cast<T*>(dk), static_cast<T*>(dv), s.Nk, s.Hkv,
+                     st, static_cast<const T*>(a.dkv_part), a.items, a.item_count, static_cast<T*>(dk), static_cast<T*>(dv), s.Nk, s.Hkv,
                      s.nblk, p.items_cap);
   prof_end(st, kid_red);
 }
@@ -673,7 +674,7 @@ void bwd_launch(const Shape& s, const BwdArgs& a, const InvertPlan& p, const voi
 }  // namespace
 
 size_t bwd_dkv_bytes(const Shape& s, const InvertPlan& p) {
-  return (size_t)s.B * s.Hkv * p.items_cap * 2 * s.Bk * s.D * sizeof(float);
+  return (size_t)s.B * s.Hkv * p.items_cap * 2 * s.Bk * s.D * (s.dtype == kBF16 ? 2 : 4);  // in the input type
 }
 
 hipError_t launch_bwd_rowdot(const Shape& s, const void* out, const void* dout, float* drow, hipStream_t st) {
@@ -696,7 +697,7 @@ hipError_t launch_bwd_rowdot(const Shape& s, const void* out, const void* dout, 
 
 hipError_t launch_bwd_attention(const Shape& s, const InvertPlan& p, const void* q, const void* k, const void* v,
                                 const void* dout, const float* lse, const float* drow, const int32_t* ids,
-                                const InvertOut& inv, void* dq_part, float* dkv_part, void* trash, void* dq, void* dk,
+                                const InvertOut& inv, void* dq_part, void* dkv_part, void* trash, void* dq, void* dk,
                                 void* dv, hipStream_t st) {
   static const int k1 = prof_register("bwd_fused");
   static const int k2 = prof_register("bwd_dq_sum");

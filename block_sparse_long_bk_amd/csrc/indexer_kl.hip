@@ -43,7 +43,7 @@ struct KlArgs {
   float* lse_s;          // [B, Nq, Hkv]
   float* kl_part;        // [B, Nq, Hkv, topk]
   void* diq_part;        // [B, Nq, Hkv, topk, DI] in the input type
-  float* dik_part;       // [B*Hkv][items_cap][BK][DI]
+  void* dik_part;        // [B*Hkv][items_cap][BK][DI] in the input type
   int Nq, Nk, Hq, Hkv, G, topk, items_cap;
   int64_t q_offset;
   uint64_t topk_magic;
@@ -451,13 +451,13 @@ __global__ void __launch_bounds__(256, 1) k_kl_main(KlArgs a) {
   }
   if (!has_keys) return;
   // this item's d ik: lane holds key 32w + 8(e/4) + 4h + e%4, c = 32 dt + lane%32
-  float* dst = a.dik_part + ((int64_t)bg * a.items_cap + item) * BK * DI;
+  T* dst = static_cast<T*>(a.dik_part) + ((int64_t)bg * a.items_cap + item) * BK * DI;
 #pragma unroll
   for (int dt = 0; dt < DI / 32; ++dt)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int key = wave * 32 + 8 * (e / 4) + 4 * half + (e % 4);
-      dst[key * DI + 32 * dt + (lane & 31)] = dik[dt][e];
+      dst[key * DI + 32 * dt + (lane & 31)] = from_f32<T>(dik[dt][e]);
     }
 }
 
@@ -834,7 +834,7 @@ __global__ void __launch_bounds__(512, 1) k_kl_main8(KlArgs a) {
   }
   if (!has_keys) return;
   // this item's d ik: lane holds key 32 kg + 8(e/4) + 4h + e%4, c = 32 dt + lane%32
-  float* dst = a.dik_part + ((int64_t)bg * a.items_cap + item) * BK * DI;
+  T* dst = static_cast<T*>(a.dik_part) + ((int64_t)bg * a.items_cap + item) * BK * DI;
 #pragma unroll
   for (int i = 0; i < DT0; ++i) {
     const int dt = hs * DT0 + i;
@@ -842,7 +842,7 @@ __global__ void __launch_bounds__(512, 1) k_kl_main8(KlArgs a) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int key = kg * 32 + 8 * (e / 4) + 4 * half + (e % 4);
-      dst[key * DI + 32 * dt + (lane & 31)] = dik[i][e];
+      dst[key * DI + 32 * dt + (lane & 31)] = from_f32<T>(dik[i][e]);
     }
   }
 }
@@ -885,7 +885,7 @@ __global__ void __launch_bounds__(256) k_kl_finish(const float* __restrict__ kl_
 
 // ---- d ik: item partials of each block in item order ------------------------
 template <typename T, int DI, int BK>
-__global__ void __launch_bounds__(256) k_kl_dik_reduce(const float* __restrict__ part, const int4* __restrict__ items,
+__global__ void __launch_bounds__(256) k_kl_dik_reduce(const T* __restrict__ part, const int4* __restrict__ items,
                                                        const int32_t* __restrict__ item_count, T* __restrict__ d_ik,
                                                        int Nk, int Hkv, int nblk, int items_cap) {
   constexpr int CH = DI / 8;
@@ -908,9 +908,9 @@ __global__ void __launch_bounds__(256) k_kl_dik_reduce(const float* __restrict__
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
   for (int u = lo; u < n && its[u].x == j; ++u) {
-    const float* p = part + ((int64_t)bg * items_cap + u) * BK * DI + tk * DI + c * 8;
+    const frag_t<T> x = load8(part + ((int64_t)bg * items_cap + u) * BK * DI + tk * DI + c * 8);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] += p[e];
+    for (int e = 0; e < 8; ++e) acc[e] += to_f32(x[e]);
   }
   frag_t<T> o;
 #pragma unroll
@@ -952,7 +952,7 @@ void kl_launch_bk(const Shape& s, const KlArgs& a, const InvertPlan& p, float* k
   const int64_t nthr = (int64_t)s.nblk * BK * (DI / 8);
   prof_begin(st, kid.reduce);
   hipLaunchKernelGGL((k_kl_dik_reduce<T, DI, BK>), dim3((unsigned)((nthr + 255) / 256), s.B * s.Hkv), dim3(256), 0,
-                     st, a.dik_part, a.items, a.item_count, static_cast<T*>(d_ik), s.Nk, s.Hkv, s.nblk, p.items_cap);
+                     st, static_cast<const T*>(a.dik_part), a.items, a.item_count, static_cast<T*>(d_ik), s.Nk, s.Hkv, s.nblk, p.items_cap);
   prof_end(st, kid.reduce);
 }
 
@@ -988,7 +988,7 @@ size_t kl_bytes(const Shape& s, const InvertPlan& p, KlWorkspace* w) {
   L.diq_part = off;
   off += up(rows * s.topk * s.DI * (s.dtype == kBF16 ? 2 : 4));  // in the input type
   L.dik_part = off;
-  off += up((size_t)s.B * s.Hkv * p.items_cap * s.Bk * s.DI * 4);
+  off += up((size_t)s.B * s.Hkv * p.items_cap * s.Bk * s.DI * (s.dtype == kBF16 ? 2 : 4));  // in the input type
   if (w) *w = L;
   return off;
 }
@@ -1014,7 +1014,7 @@ hipError_t launch_indexer_kl(const Shape& s, const InvertPlan& p, const void* q,
   a.lse_s = reinterpret_cast<float*>(ws + L.lse_s);
   a.kl_part = reinterpret_cast<float*>(ws + L.kl_part);
   a.diq_part = ws + L.diq_part;
-  a.dik_part = reinterpret_cast<float*>(ws + L.dik_part);
+  a.dik_part = ws + L.dik_part;
   a.Nq = s.Nq;
   a.Nk = s.Nk;
   a.Hq = s.Hq;

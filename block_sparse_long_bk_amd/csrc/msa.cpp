@@ -450,7 +450,7 @@ msa_status_t msa_sparse_attention_backward(const msa_problem_t* prob, const void
   if (e == hipSuccess) e = msa::launch_invert(s, plan, block_ids, 0, s.Nq, inv, w + L.inv_scratch, st);
   if (e == hipSuccess)
     e = msa::launch_bwd_attention(s, plan, q, k, v, dout, lse, drow, block_ids, inv,
-                                  w + L.dq_part, reinterpret_cast<float*>(w + L.dkv_part),
+                                  w + L.dq_part, w + L.dkv_part,
                                   w + L.trash, dq, dk, dv, st);
   return e == hipSuccess ? MSA_OK : hip_fail(e);
 }

@@ -103,7 +103,7 @@ size_t bwd_dkv_bytes(const Shape& s, const InvertPlan& p);
 // and dk, dv (via per-item fp32 partials) for the work items of `inv` (whole problem, q0 = 0).
 hipError_t launch_bwd_attention(const Shape& s, const InvertPlan& p, const void* q, const void* k, const void* v,
                                 const void* dout, const float* lse, const float* drow, const int32_t* ids,
-                                const InvertOut& inv, void* dq_part, float* dkv_part, void* trash, void* dq, void* dk,
+                                const InvertOut& inv, void* dq_part, void* dkv_part, void* trash, void* dq, void* dk,
                                 void* dv, hipStream_t st);
 
 // Index-Branch alignment loss -----------------------------------------------
