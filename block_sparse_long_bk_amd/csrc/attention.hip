@@ -428,7 +428,7 @@ struct CombArgs {
   const int32_t* ids;
   void* out;
   float* lse;
-  int Nq, Hq, Hkv, G, topk, S, q0, nq, ids_slots;
+  int Nq, Hq, Hkv, G, topk, S, q0, nq, ids_slots, nblk;
 };
 
 template <typename T> struct Pack8;
@@ -436,8 +436,9 @@ template <> struct Pack8<bf16_t> { using type = bf16x8; };
 template <> struct Pack8<float> { using type = f32x8; };
 
 // D/8 lanes per (b, query, head) row, 8 output values per lane: merge the S
-// partials of the row by log-sum-exp weights.  Slots with block id -1
-// (KV-outer) or lse = -inf (empty query-outer split) carry no weight.
+// partials of the row by log-sum-exp weights.  Slots whose block id lies
+// outside [0, nblk) (KV-outer: the inversion gave them no partial) or whose
+// lse is -inf (no visible key, or an empty query-outer split) carry no weight.
 template <typename T, int D, int SMAX>
 __global__ void __launch_bounds__(256) k_combine(CombArgs a) {
   constexpr int LPH = D / 8;     // lanes per row
@@ -473,7 +474,7 @@ __global__ void __launch_bounds__(256) k_combine(CombArgs a) {
     ls[s] = -__builtin_huge_valf();
     if (s < a.S) {
       const float x = pl[(int64_t)s * a.Hq];
-      if (idv[s] >= 0) ls[s] = x;
+      if ((unsigned)idv[s] < (unsigned)a.nblk) ls[s] = x;
     }
   }
   float M = -__builtin_huge_valf();
@@ -677,6 +678,7 @@ hipError_t launch_combine(const Shape& s, int q0, int nq, const Partials& part, 
   a.q0 = q0;
   a.nq = nq;
   a.ids_slots = ids_slots ? 1 : 0;
+  a.nblk = s.nblk;
   const int64_t rows = (int64_t)nq * s.Hq;
   const int rows_per_wg = 4 * (64 / (s.D / 8));
   const dim3 grid((unsigned)((rows + rows_per_wg - 1) / rows_per_wg), s.B);

@@ -546,7 +546,7 @@ __global__ void __launch_bounds__(512, 1) k_bwd_split(BwdArgs a) {
 template <typename T, int D>
 __global__ void __launch_bounds__(256) k_bwd_dq_sum(const T* __restrict__ part, const int32_t* __restrict__ ids,
                                                     T* __restrict__ dq, int Hq, int Hkv, int G, int topk,
-                                                    int64_t nrows) {
+                                                    int nblk, int64_t nrows) {
   constexpr int LPR = D / 8;
   const int lane = threadIdx.x & 63;
   const int64_t row = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * (64 / LPR) + lane / LPR;  // (b, i, h)
@@ -567,7 +567,7 @@ __global__ void __launch_bounds__(256) k_bwd_dq_sum(const T* __restrict__ part, 
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int sl = min(s0 + u, topk - 1);
-      ok[u] = s0 + u < topk && sel[sl] >= 0;
+      ok[u] = s0 + u < topk && (unsigned)sel[sl] < (unsigned)nblk;  // ids outside [0, nblk) have no partial
       x[u] = load8(p + (int64_t)sl * D);
     }
 #pragma unroll
@@ -653,7 +653,7 @@ void bwd_launch_bk(const Shape& s, const BwdArgs& a, const InvertPlan& p, const 
   prof_begin(st, kid_sum);
   hipLaunchKernelGGL((k_bwd_dq_sum<T, D>), dim3((unsigned)((nrows + rpb - 1) / rpb)), dim3(256), 0, st,
                      static_cast<const T*>(a.dq_part), static_cast<const int32_t*>(ids), static_cast<T*>(dq), s.Hq,
-                     s.Hkv, s.Hq / s.Hkv, s.topk, nrows);
+                     s.Hkv, s.Hq / s.Hkv, s.topk, s.nblk, nrows);
   prof_end(st, kid_sum);
   const int64_t nthr = (int64_t)s.nblk * BK * (D / 8);
   prof_begin(st, kid_red);

@@ -135,29 +135,33 @@ __global__ void __launch_bounds__(256) k_kl_lse(KlArgs a) {
         m = mn;
       }
     }
-    // merge the two halves' keys; token 0 of the block is always visible, so
-    // half 0 holds a finite maximum
+    // merge the two halves' keys (a block that lies wholly past the query --
+    // only a caller's table can name one -- has no visible key: -inf)
     const float2 mp = lane_pair32(m), lp = lane_pair32(l);  // (half 0's, half 1's)
     const float mm = fmaxf(mp.x, mp.y);
     const float lt = lp.x * exp2_fast((mp.x - mm) * kLog2e) + lp.y * exp2_fast((mp.y - mm) * kLog2e);
-    if (half == 0 && valid) a.plse[(((int64_t)b * a.Nq + qq) * a.Hkv + g) * a.topk + slot] = mm + __logf(lt);
+    const float pl = mm == -__builtin_huge_valf() ? -__builtin_huge_valf() : mm + __logf(lt);
+    if (half == 0 && valid) a.plse[(((int64_t)b * a.Nq + qq) * a.Hkv + g) * a.topk + slot] = pl;
   }
 }
 
 // ---- lse_s per (query, group) over its selected slots -----------------------
+// Slots whose id lies outside [0, nblk) have no partial; a row with no
+// visible selected key (every partial -inf) gets -inf.
 __global__ void __launch_bounds__(256) k_kl_lse_sum(const float* __restrict__ plse, const int32_t* __restrict__ ids,
-                                                    float* __restrict__ lse_s, int topk, int64_t nrows) {
+                                                    float* __restrict__ lse_s, int topk, int nblk, int64_t nrows) {
   const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (row >= nrows) return;
   const int32_t* sel = ids + row * topk;
   const float* p = plse + row * topk;
   float m = -__builtin_huge_valf();
   for (int s = 0; s < topk; ++s)
-    if (sel[s] >= 0) m = fmaxf(m, p[s]);
+    if ((unsigned)sel[s] < (unsigned)nblk) m = fmaxf(m, p[s]);
   float l = 0.f;
-  for (int s = 0; s < topk; ++s)
-    if (sel[s] >= 0) l += exp2_fast((p[s] - m) * kLog2e);
-  lse_s[row] = m + __logf(l);
+  if (m != -__builtin_huge_valf())
+    for (int s = 0; s < topk; ++s)
+      if ((unsigned)sel[s] < (unsigned)nblk) l += exp2_fast((p[s] - m) * kLog2e);
+  lse_s[row] = l > 0.f ? m + __logf(l) : -__builtin_huge_valf();
 }
 
 // ---- the main pass: a lane owns a key ---------------------------------------
@@ -852,7 +856,7 @@ template <typename T, int DI>
 __global__ void __launch_bounds__(256) k_kl_finish(const float* __restrict__ kl_part,
                                                    const T* __restrict__ diq_part,
                                                    const int32_t* __restrict__ ids, float* __restrict__ kl,
-                                                   T* __restrict__ d_iq, int topk, int64_t nrows) {
+                                                   T* __restrict__ d_iq, int topk, int nblk, int64_t nrows) {
   constexpr int LPR = DI / 8;
   const int lane = threadIdx.x & 63;
   const int64_t row = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * (64 / LPR) + lane / LPR;  // (b, i, g)
@@ -864,7 +868,7 @@ __global__ void __launch_bounds__(256) k_kl_finish(const float* __restrict__ kl_
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
   float kacc = 0.f;
   for (int s = 0; s < topk; ++s) {
-    if (sel[s] < 0) continue;
+    if ((unsigned)sel[s] >= (unsigned)nblk) continue;  // no partial for ids outside [0, nblk)
     const frag_t<T> x = load8(p + (int64_t)s * DI);
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] += to_f32(x[e]);
@@ -938,7 +942,7 @@ void kl_launch_bk(const Shape& s, const KlArgs& a, const InvertPlan& p, float* k
   prof_end(st, kid.lse);
   prof_begin(st, kid.lse_sum);
   hipLaunchKernelGGL(k_kl_lse_sum, dim3((unsigned)((nrows + 255) / 256)), dim3(256), 0, st, a.plse, a.ids, a.lse_s,
-                     s.topk, nrows);
+                     s.topk, s.nblk, nrows);
   prof_end(st, kid.lse_sum);
   prof_begin(st, kid.main);
   if constexpr (sizeof(T) == 2) hipLaunchKernelGGL((k_kl_main8<T, D, DI, BK>), grid, dim3(512), 0, st, a);
@@ -947,7 +951,7 @@ void kl_launch_bk(const Shape& s, const KlArgs& a, const InvertPlan& p, float* k
   const int rpb = 4 * (64 / (DI / 8));
   prof_begin(st, kid.finish);
   hipLaunchKernelGGL((k_kl_finish<T, DI>), dim3((unsigned)((nrows + rpb - 1) / rpb)), dim3(256), 0, st, a.kl_part,
-                     static_cast<const T*>(a.diq_part), a.ids, kl, static_cast<T*>(d_iq), s.topk, nrows);
+                     static_cast<const T*>(a.diq_part), a.ids, kl, static_cast<T*>(d_iq), s.topk, s.nblk, nrows);
   prof_end(st, kid.finish);
   const int64_t nthr = (int64_t)s.nblk * BK * (DI / 8);
   prof_begin(st, kid.reduce);

@@ -13,9 +13,13 @@
 //                     of ceil(count/QI) -> work-item offsets;
 //   4. k_inv_scatter  per tile, one wave walks its queries in order and
 //                     places each pick at offsets[j] + (earlier picks of j):
-//                     entries of a block come out in ascending query order.
-//                     A query never picks a block twice, so the lanes of one
-//                     step touch distinct counters and no atomics are needed;
+//                     entries of a block come out in ascending (query, slot)
+//                     order.  A row may name a block more than once (the
+//                     attention then counts it once per listing): the lanes
+//                     of one step rank themselves among the lower lanes with
+//                     the same id, and the last of them advances the cursor,
+//                     so every entry slot and every cursor has one writer and
+//                     no atomics are needed;
 //   5. k_inv_items    splits each block's entries into work items of at most
 //                     QI queries; a hot block yields many items, which is
 //                     what absorbs the skew.
@@ -129,11 +133,14 @@ __global__ void __launch_bounds__(1024) k_inv_blkscan(InvArgs a) {
   }
 }
 
-// One wave per (b, g, tile).  LDS: cursors [nblk] then the tile's ids.
+// One wave per (b, g, tile).  LDS: cursors [nblk] then the tile's ids, one
+// row of inv_row_pitch(topk) words per query (rows padded to whole 16-byte
+// chunks with -1, so that a step reads its row with 16-byte broadcasts).
 __global__ void __launch_bounds__(64) k_inv_scatter(InvArgs a) {
-  extern __shared__ int32_t sm[];
+  extern __shared__ __attribute__((aligned(16))) int32_t sm[];
   int32_t* cur = sm;
-  int32_t* tids = sm + a.nblk;
+  const int tp = inv_row_pitch(a.topk);
+  int32_t* tids = sm + ((a.nblk + 3) & ~3);
   const int tile = blockIdx.x, bg = blockIdx.y;
   const int b = bg / a.Hkv, g = bg % a.Hkv;
   const int lane = threadIdx.x;
@@ -142,20 +149,34 @@ __global__ void __launch_bounds__(64) k_inv_scatter(InvArgs a) {
   for (int j = lane; j < a.nblk; j += 64) cur[j] = off[j] + pre[j];
   const int qbeg = tile * kInvTile;
   const int nt = min(kInvTile, a.nq - qbeg);
-  for (int e = lane; e < nt * a.topk; e += 64) {
-    const int qq = qbeg + e / a.topk, s = e % a.topk;
-    tids[e] = a.ids[(((int64_t)b * a.Nq + a.q0 + qq) * a.Hkv + g) * a.topk + s];
+  for (int e = lane; e < nt * tp; e += 64) {
+    const int qq = qbeg + e / tp, s = e % tp;
+    tids[e] = s < a.topk ? a.ids[(((int64_t)b * a.Nq + a.q0 + qq) * a.Hkv + g) * a.topk + s] : -1;
   }
   __syncthreads();
   int32_t* ent = a.entries + (int64_t)bg * a.nq * a.topk;
   for (int t = 0; t < nt; ++t) {
-    if (lane < a.topk) {
-      const int j = tids[t * a.topk + lane];
-      if (j >= 0 && j < a.nblk) {
-        const int32_t pos = cur[j];
-        cur[j] = pos + 1;
-        ent[pos] = (qbeg + t) * a.topk + lane;
+    const int32_t* row = tids + t * tp;
+    const int j = lane < a.topk ? row[lane] : -1;
+    const bool ok = j >= 0 && j < a.nblk;
+    // rank among the lower slots of this row that name the same block, and
+    // how many slots name it
+    int rank = 0, cnt = 0;
+    for (int c = 0; c < tp; c += 4) {
+      const int4 v = *reinterpret_cast<const int4*>(row + c);
+      const int vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int eq = vv[u] == j ? 1 : 0;
+        cnt += eq;
+        rank += c + u < lane ? eq : 0;
       }
+    }
+    const int32_t base = ok ? cur[j] : 0;
+    wave_lds_sync();  // every lane has read its cursor before any is advanced
+    if (ok) {
+      ent[base + rank] = (qbeg + t) * a.topk + lane;
+      if (rank == cnt - 1) cur[j] = base + cnt;
     }
     wave_lds_sync();  // the next step may read a cursor another lane just advanced
   }
@@ -239,7 +260,8 @@ hipError_t launch_invert(const Shape& s, const InvertPlan& p, const int32_t* ids
   MSA_INV_LAUNCH(k1, k_inv_hist, dim3(a.n_tiles, BG), dim3(kInvTile), (size_t)s.nblk * 4, st, a)
   MSA_INV_LAUNCH(k2, k_inv_colscan, dim3((s.nblk + 255) / 256, BG), dim3(256), 0, st, a)
   MSA_INV_LAUNCH(k3, k_inv_blkscan, dim3(BG), dim3(1024), 0, st, a)
-  MSA_INV_LAUNCH(k4, k_inv_scatter, dim3(a.n_tiles, BG), dim3(64), (size_t)(s.nblk + kInvTile * s.topk) * 4, st, a)
+  MSA_INV_LAUNCH(k4, k_inv_scatter, dim3(a.n_tiles, BG), dim3(64),
+                 (size_t)(((s.nblk + 3) & ~3) + kInvTile * inv_row_pitch(s.topk)) * 4, st, a)
   if (out.items) {
     MSA_INV_LAUNCH(k5, k_inv_items, dim3(p.items_cap / 256 + 1, BG), dim3(256), 0, st, a)
   }

@@ -236,12 +236,36 @@ __device__ __forceinline__ void sort_asc(int (&a)[N]) {
 // Write one selection row: the first `nsel` (<= k-1) ids of `cand` (KMAX
 // entries; unused ones are INT32_MAX), then the local block L, then -1 up to
 // topk.  `cand` is sorted here.  All candidate ids are < L.
+// The lists admit finite scores only (-inf and NaN never pass the -inf of an
+// empty slot), so a row with fewer than nsel finite scores comes with missing
+// picks; they go to the lowest candidate ids not yet picked -- the order that
+// puts -inf (and NaN, ranked with it) below every finite score, ties to the
+// lower id.
 template <int KMAX>
 __device__ __forceinline__ void write_selection(int (&cand)[KMAX], int nsel, int L, int topk, int32_t* out) {
 #pragma unroll
   for (int p = 0; p < KMAX; ++p)
     if (p >= nsel) cand[p] = INT32_MAX;
   sort_asc<KMAX>(cand);
+  int nv = 0;
+#pragma unroll
+  for (int p = 0; p < KMAX; ++p) nv += cand[p] != INT32_MAX ? 1 : 0;
+  if (nv < nsel) {
+    // The f-th smallest id outside the sorted picks: start at f and step past
+    // every pick at or below the running value (missing picks are INT32_MAX
+    // and never step).
+    int fill[KMAX];
+#pragma unroll
+    for (int p = 0; p < KMAX; ++p) {
+      int c = p - nv;
+#pragma unroll
+      for (int q = 0; q < KMAX; ++q) c += cand[q] <= c ? 1 : 0;
+      fill[p] = p >= nv && p < nsel ? c : cand[p];
+    }
+#pragma unroll
+    for (int p = 0; p < KMAX; ++p) cand[p] = fill[p];
+    sort_asc<KMAX>(cand);
+  }
 #pragma unroll
   for (int p = 0; p <= KMAX; ++p) {
     if (p < topk) {

@@ -51,6 +51,8 @@ struct InvertPlan {
   int qi;            // queries per work item
 };
 constexpr int kInvTile = 256;
+// Words per query row of block ids in the scatter's LDS copy (whole 16-byte chunks).
+__host__ __device__ constexpr int inv_row_pitch(int topk) { return (topk + 3) & ~3; }
 // A KV-outer work item holds at most kItemRows (query, head) rows and at most
 // kItemEntries (query, slot) entries (the entries are staged in LDS).
 constexpr int kItemRows = 2048;

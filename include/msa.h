@@ -41,6 +41,27 @@
  *   - Results are bitwise reproducible for identical inputs and do not depend
  *     on how the library splits the work (query chunks, workspace size).
  *
+ * Block id tables.  The ids msa_index_topk / msa_forward / msa_topk_from_scores
+ * write hold, per (b, i, g) row, min(topk, L+1) distinct blocks in ascending
+ * order -- the local block L and the best candidates -- then -1.  The calls
+ * that take a table (msa_invert, msa_sparse_attention,
+ * msa_sparse_attention_backward, msa_indexer_kl) accept any int32 values and
+ * define the result for every one of them:
+ *   - an id outside [0, nblk) (-1 or any other) selects nothing;
+ *   - a block named twice in a row counts twice: its visible tokens enter the
+ *     softmax once per listing (the output is unchanged and lse grows by
+ *     ln 2; each listing gets its own gradient share), and msa_invert lists
+ *     the row once per listing, in slot order;
+ *   - tokens past the query position are never visible, so a block after the
+ *     query's own contributes nothing;
+ *   - a row with no visible selected token gets out = 0 and lse = -inf, zero
+ *     dq, no dk / dv share, kl = 0 and zero index gradients.
+ * Every schedule gives the same result for such a table, and no id makes a
+ * kernel read or write outside the caller's buffers.
+ *
+ * Block scores given to msa_topk_from_scores may be non-finite: -inf and NaN
+ * rank below every finite score (NaN as -inf), ties to the lower id.
+ *
  * Supported: dtype MSA_BF16 or MSA_F32; block_size in {32, 64, 128} (the
  * pages use 128 and ablate the smaller sizes); d in {64, 128};
  * d_idx in {32, 64, 128}; 1 <= topk <= 32; Hq / Hkv a power of two <= 32;
@@ -146,9 +167,14 @@ msa_status_t msa_block_scores(const msa_problem_t* prob, const void* idx_q, cons
 msa_status_t msa_topk_from_scores(const msa_problem_t* prob, const float* scores, int32_t* block_ids,
                                   void* stream);
 
-/* Index Branch: block scores and Top-k in one call; writes block_ids.
- * Needs the MSA_OP_INDEX_TOPK workspace (zero bytes for most prefill
- * shapes, where scoring and selection run fused). */
+/* Index Branch, steps 1 to 3 in one call (paper summary page, "Method": the
+ * index-q . index-k token scores, Block Max Pooling over each candidate
+ * block, Top-k with the local block always kept; zhichai.net write-up,
+ * sections 2 and 4.1: one index head pair per GQA group, exp-free selection).
+ * Writes block_ids [B, Nq, Hkv, topk] as described under "Block id tables".
+ * Needs the MSA_OP_INDEX_TOPK workspace (zero bytes for most prefill shapes,
+ * where scoring and selection run fused; the block scores otherwise).
+ * Errors: as listed under "Conventions". */
 msa_status_t msa_index_topk(const msa_problem_t* prob, const void* idx_q, const void* idx_k,
                             int32_t* block_ids, void* ws, size_t ws_bytes, void* stream);
 
@@ -157,7 +183,8 @@ msa_status_t msa_index_topk(const msa_problem_t* prob, const void* idx_q, const 
  * (b, g), offsets [B, Hkv, nblk+1] (int32, exclusive prefix of the number of
  * (query, slot) pairs that chose each block) and entries [B, Hkv, Nq*topk]
  * (int32 i*topk + slot, grouped by block, ascending within a block; entries
- * past offsets[nblk] are unspecified).  Deterministic.  Needs the
+ * past offsets[nblk] are unspecified).  Ids outside [0, nblk) are not listed;
+ * a block named twice in a row is listed once per slot.  Deterministic.  Needs the
  * MSA_OP_INVERT workspace (the whole problem in one pass). */
 msa_status_t msa_invert(const msa_problem_t* prob, const int32_t* block_ids, int32_t* offsets,
                         int32_t* entries, void* ws, size_t ws_bytes, void* stream);
@@ -165,12 +192,19 @@ msa_status_t msa_invert(const msa_problem_t* prob, const int32_t* block_ids, int
 /* Main Branch: exact softmax attention of every query head over the visible
  * tokens of its group's blocks in block_ids (paper summary "Method"), in the
  * schedule prob->sched.  Writes out (dtype of the inputs) and, if lse is not
- * NULL, the log-sum-exp of the scaled logits. */
+ * NULL, the log-sum-exp of the scaled logits.  block_ids may be any int32
+ * table (see "Block id tables"). */
 msa_status_t msa_sparse_attention(const msa_problem_t* prob, const void* q, const void* k, const void* v,
                                   const int32_t* block_ids, void* out, float* lse, void* ws, size_t ws_bytes,
                                   void* stream);
 
-/* Index Branch then Main Branch: writes block_ids, out and (optionally) lse. */
+/* The whole MSA forward (paper summary page, "Method"; zhichai.net write-up,
+ * section 2): the Index Branch of msa_index_topk, then the Main Branch of
+ * msa_sparse_attention over the blocks it selected, in one call on one
+ * stream.  Writes block_ids, out and, if lse is not NULL, lse.  Needs the
+ * MSA_OP_FORWARD workspace; given less than the full size (but at least the
+ * minimum msa_workspace_size reports) it processes the queries in chunks
+ * with bitwise the same results.  Errors: as listed under "Conventions". */
 msa_status_t msa_forward(const msa_problem_t* prob, const void* q, const void* k, const void* v,
                          const void* idx_q, const void* idx_k, int32_t* block_ids, void* out, float* lse,
                          void* ws, size_t ws_bytes, void* stream);

@@ -155,7 +155,9 @@ int mo_select(const mo_problem* p, const double* scores, const int64_t* rows, in
         for (int64_t j = 0; j < L; ++j) chosen[n++] = (int32_t)j; /* every candidate */
       } else {
         for (int64_t j = 0; j < L; ++j) {
-          cand[j].s = S[j];
+          /* a NaN score ranks with -inf (lowest, ties to the lower id), as the
+             max-pool's NaN token scores are dropped */
+          cand[j].s = isnan(S[j]) ? -INFINITY : S[j];
           cand[j].j = (int32_t)j;
         }
         qsort(cand, (size_t)L, sizeof(cand_t), by_score_desc_id_asc);
@@ -212,7 +214,8 @@ static double softmax_scale(const mo_problem* p) {
 }
 
 /* T: the visible tokens (t <= pos, t < n_k) of the blocks listed in sel
- * (topk entries, -1 ignored), in list order.  Returns |T|. */
+ * (topk entries; ids outside [0, nblk) ignored), in list order: a block listed
+ * twice puts its tokens in T twice.  Returns |T|. */
 static int64_t visible_tokens(const mo_problem* p, const int32_t* sel, int64_t pos, int64_t* tok) {
   const int64_t Bk = p->block_size, nblk = num_blocks(p);
   int64_t n = 0;
@@ -233,6 +236,10 @@ static double attend_row(const mo_problem* p, const void* q, const void* k, cons
   const int64_t Hq = p->h_q, Hkv = p->h_kv, D = p->d, g = group_of(p, h);
   const double scale = softmax_scale(p);
   const int64_t qbase = ((b * p->n_q + i) * Hq + h) * D;
+  if (n == 0) { /* no visible selected token: zero output, empty sum */
+    for (int64_t c = 0; c < D; ++c) o[c] = 0.0;
+    return -INFINITY;
+  }
   double m = -INFINITY;
   for (int64_t a = 0; a < n; ++a) {
     const int64_t kbase = ((b * p->n_k + tok[a]) * Hkv + g) * D;
@@ -263,12 +270,11 @@ int mo_attend(const mo_problem* p, const void* q, const void* k, const void* v, 
   if ((rc = check_rows(p, rows, n_rows))) return rc;
   if (!q || !k || !v || !ids || !out) return -1;
   const int64_t Hq = p->h_q, Hkv = p->h_kv, D = p->d, K = p->topk, Bk = p->block_size;
-  const int64_t nblk = num_blocks(p);
 
 #pragma omp parallel
   {
     /* Worst case: every block selected. */
-    const int64_t cap = (K < nblk ? K : nblk) * Bk;
+    const int64_t cap = K * Bk; /* a block listed twice contributes its tokens twice */
     double* x = (double*)malloc(sizeof(double) * (size_t)cap);
     int64_t* tok = (int64_t*)malloc(sizeof(int64_t) * (size_t)cap);
 #pragma omp for schedule(dynamic, 4)
@@ -301,14 +307,13 @@ int mo_attend_backward(const mo_problem* p, const void* q, const void* k, const 
   rc = check_rows(p, rows, n_rows);
   if (rc) return rc;
   const int64_t Hq = p->h_q, Hkv = p->h_kv, G = Hq / Hkv, D = p->d, K = p->topk, Bk = p->block_size;
-  const int64_t nblk = num_blocks(p);
   const double scale = softmax_scale(p);
   memset(dk, 0, sizeof(double) * (size_t)(p->batch * p->n_k * Hkv * D));
   memset(dv, 0, sizeof(double) * (size_t)(p->batch * p->n_k * Hkv * D));
 
 #pragma omp parallel
   {
-    const int64_t cap = (K < nblk ? K : nblk) * Bk;
+    const int64_t cap = K * Bk; /* a block listed twice contributes its tokens twice */
     double* x = (double*)malloc(sizeof(double) * (size_t)cap);
     int64_t* tok = (int64_t*)malloc(sizeof(int64_t) * (size_t)cap);
     double* o = (double*)malloc(sizeof(double) * (size_t)D);
@@ -369,12 +374,12 @@ int mo_indexer_kl(const mo_problem* p, const void* q, const void* k, const void*
   rc = check_rows(p, rows, n_rows);
   if (rc) return rc;
   const int64_t Hq = p->h_q, Hkv = p->h_kv, G = Hq / Hkv, D = p->d, DI = p->d_idx, K = p->topk;
-  const int64_t Bk = p->block_size, nblk = num_blocks(p);
+  const int64_t Bk = p->block_size;
   memset(d_ik, 0, sizeof(double) * (size_t)(p->batch * p->n_k * Hkv * DI));
 
 #pragma omp parallel
   {
-    const int64_t cap = (K < nblk ? K : nblk) * Bk;
+    const int64_t cap = K * Bk; /* a block listed twice contributes its tokens twice */
     double* x = (double*)malloc(sizeof(double) * (size_t)cap);
     double* pm = (double*)malloc(sizeof(double) * (size_t)cap);
     double* si = (double*)malloc(sizeof(double) * (size_t)cap);

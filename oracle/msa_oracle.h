@@ -57,12 +57,16 @@ int mo_block_scores(const mo_problem* p, const void* iq, const void* ik, int dty
                     const int64_t* rows, int64_t n_rows, double* scores);
 
 /* Selection from block scores laid out as mo_block_scores writes them.
- * ids: int32 [n_rows][h_kv][topk], ascending, -1 padded. */
+ * ids: int32 [n_rows][h_kv][topk], ascending, -1 padded.  A NaN score ranks
+ * with -inf: below every finite score, ties to the lower id. */
 int mo_select(const mo_problem* p, const double* scores, const int64_t* rows, int64_t n_rows,
               int32_t* ids);
 
 /* Exact softmax attention over the tokens of the blocks listed in ids
- * (int32 [n_rows][h_kv][topk], -1 entries ignored).
+ * (int32 [n_rows][h_kv][topk]).  Any int32 is accepted: ids outside
+ * [0, nblk) are ignored, a block listed twice enters T twice (the output is
+ * unchanged, lse grows by ln 2), tokens past the query position are not
+ * visible.  A row with no visible listed token gets out = 0, lse = -inf.
  * out: double [n_rows][h_q][d]; lse: double [n_rows][h_q] (may be NULL). */
 int mo_attend(const mo_problem* p, const void* q, const void* k, const void* v, int dtype,
               const int32_t* ids, const int64_t* rows, int64_t n_rows, double* out, double* lse);

@@ -8,12 +8,19 @@ Criteria (fixed before any kernel existed):
     difference.  Such rows are counted; failing rows must be zero.
   * attention (computed from the oracle's selection): bf16 max-abs <= 2e-2
     and rel-L2 <= 5e-3; fp32 max-abs <= 1e-4 and rel-L2 <= 1e-4.
+  * attention, row by row (so that a few wrong rows cannot hide in the
+    global figures): the rel-L2 of every (query, head) output row must stay
+    within 1e-2 for bf16 -- the output is rounded to bf16 (2^-9 relative),
+    the KV-outer partials are bf16 (another 2^-9) and P enters the PV product
+    in bf16 (2^-9 per weight) -- and within 1e-4 for fp32; a row whose oracle
+    output is exactly zero (no visible selected token) must be exactly zero.
 """
 import numpy as np
 import torch
 
 TIE_REL = 1e-3
-TOL = {"bf16": dict(max_abs=2e-2, rel_l2=5e-3, lse_abs=2e-2), "f32": dict(max_abs=1e-4, rel_l2=1e-4, lse_abs=1e-4)}
+TOL = {"bf16": dict(max_abs=2e-2, rel_l2=5e-3, lse_abs=2e-2, row_rel_l2=1e-2),
+       "f32": dict(max_abs=1e-4, rel_l2=1e-4, lse_abs=1e-4, row_rel_l2=1e-4)}
 
 
 def host(t):
@@ -67,13 +74,41 @@ def attention_errors(out_gpu, out_ora):
     return float(np.max(np.abs(diff))), float(np.linalg.norm(diff) / max(np.linalg.norm(b), 1e-300))
 
 
+def worst_row(out_gpu, out_ora):
+    """Largest rel-L2 over the output rows (the last axis is d) and its row
+    index; rows whose oracle output is zero count as 0 if the GPU's is zero
+    too and as inf otherwise."""
+    a = np.asarray(out_gpu, dtype=np.float64)
+    b = np.asarray(out_ora, dtype=np.float64)
+    a = a.reshape(-1, a.shape[-1])
+    b = b.reshape(-1, b.shape[-1])
+    nb = np.linalg.norm(b, axis=1)
+    nd = np.linalg.norm(a - b, axis=1)
+    rel = np.where(nb > 0, nd / np.where(nb > 0, nb, 1.0), np.where(nd == 0, 0.0, np.inf))
+    r = int(np.argmax(rel)) if rel.size else 0
+    return (float(rel[r]) if rel.size else 0.0), r
+
+
+def assert_lse(dtype, lse_gpu, lse_ora, what=""):
+    """lse within the tolerance where the oracle's is finite; -inf exactly
+    where it is -inf (rows with no visible selected token)."""
+    a = np.asarray(lse_gpu, dtype=np.float64)
+    b = np.asarray(lse_ora, dtype=np.float64)
+    fin = np.isfinite(b)
+    assert np.array_equal(np.isneginf(a), np.isneginf(b)) and np.all(np.isfinite(a[fin])), f"{what}: lse -inf pattern"
+    d = float(np.max(np.abs(a[fin] - b[fin]))) if fin.any() else 0.0
+    assert d <= TOL[dtype]["lse_abs"], f"{what}: lse max-abs {d:.3e}"
+
+
 def assert_attention(dtype, out_gpu, out_ora, lse_gpu=None, lse_ora=None, what=""):
     tol = TOL[dtype]
     mx, rl = attention_errors(out_gpu, out_ora)
     assert mx <= tol["max_abs"] and rl <= tol["rel_l2"], f"{what}: max-abs {mx:.3e} rel-L2 {rl:.3e} ({dtype})"
+    wr, r = worst_row(out_gpu, out_ora)
+    assert wr <= tol["row_rel_l2"], f"{what}: worst row {r} rel-L2 {wr:.3e} ({dtype})"
     if lse_gpu is not None:
-        d = np.max(np.abs(np.asarray(lse_gpu, dtype=np.float64) - np.asarray(lse_ora, dtype=np.float64)))
-        assert d <= tol["lse_abs"], f"{what}: lse max-abs {d:.3e}"
+        assert_lse(dtype, lse_gpu, lse_ora, what)
+    print(f"{what}: worst row rel-L2 {wr:.2e}")
     return mx, rl
 
 
