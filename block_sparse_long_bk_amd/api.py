@@ -18,6 +18,7 @@ F32, BF16 = 0, 1
 SCHED_AUTO, SCHED_KV_OUTER, SCHED_Q_OUTER = 0, 1, 2
 OP_INDEX_TOPK, OP_ATTENTION, OP_FORWARD, OP_INVERT, OP_BACKWARD, OP_INDEXER_KL = 0, 1, 2, 3, 4, 5
 IDX_PLAIN, IDX_MXFP8 = 0, 1
+NOALLOC_SCRATCH_BYTES = 256 << 20  # MSA_NOALLOC_SCRATCH_BYTES of msa.h
 _IDXF = {"plain": IDX_PLAIN, "mxfp8": IDX_MXFP8}
 _SCHED = {"auto": SCHED_AUTO, "kv_outer": SCHED_KV_OUTER, "q_outer": SCHED_Q_OUTER}
 
@@ -46,6 +47,7 @@ _L = None
 
 EXPORTS = ["msa_status_string", "msa_last_hip_error", "msa_validate", "msa_workspace_size", "msa_block_scores",
            "msa_topk_from_scores", "msa_index_topk", "msa_invert", "msa_sparse_attention", "msa_forward",
+           "msa_forward_noalloc",
            "msa_sparse_attention_backward", "msa_indexer_kl", "msa_mxfp8_quantize", "msa_profile_enable", "msa_profile_reset",
            "msa_profile_count", "msa_profile_read"]
 
@@ -70,6 +72,7 @@ def _lib():
         L.msa_invert.argtypes = [P, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.msa_sparse_attention.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.msa_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.msa_forward_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.msa_sparse_attention_backward.argtypes = [P] + [vp] * 10 + [vp, ctypes.c_size_t, vp]
         L.msa_indexer_kl.argtypes = [P] + [vp] * 6 + [ctypes.c_float] + [vp] * 4 + [ctypes.c_size_t, vp]
         L.msa_mxfp8_quantize.argtypes = [vp, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, vp, vp, vp]
@@ -333,6 +336,25 @@ def forward(p, q, k, v, iq, ik, ids=None, out=None, lse=None, want_lse=True, ws=
     wp, wn = _ws(ws)
     _check(_lib().msa_forward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(iq), _ptr(ik), _ptr(ids), _ptr(out),
                               _ptr(lse), wp, wn, _stream()), "msa_forward")
+    return ids, out, lse
+
+
+def forward_noalloc(p, q, k, v, iq, ik, ids=None, out=None, lse=None, want_lse=True):
+    """msa_forward on the library's own per-GPU scratch (no workspace argument)."""
+    dt = _tdtype(p)
+    _expect(q, (p.batch, p.n_q, p.h_q, p.d), dt, "q")
+    _expect_kv(p, k, "k")
+    _expect_kv(p, v, "v")
+    _expect(iq, (p.batch, p.n_q, p.h_kv, p.d_idx), dt, "idx_q")
+    _expect_ik(p, ik)
+    if ids is None:
+        ids = torch.empty((p.batch, p.n_q, p.h_kv, p.topk), dtype=torch.int32, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((p.batch, p.n_q, p.h_q), dtype=torch.float32, device=q.device)
+    _check(_lib().msa_forward_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(iq), _ptr(ik), _ptr(ids),
+                                      _ptr(out), _ptr(lse), _stream()), "msa_forward_noalloc")
     return ids, out, lse
 
 

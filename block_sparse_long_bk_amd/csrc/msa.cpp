@@ -337,6 +337,8 @@ msa_status_t prof_flush() {
 
 namespace msa {
 
+int record_hip_error(hipError_t e) { return hip_fail(e); }
+
 int prof_register(const char* name) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
   prof_kernels().push_back(ProfKernel{name, 0.0, 0});

@@ -21,6 +21,9 @@ struct Shape {
   float scale;  // softmax scale (natural-log domain)
 };
 
+// Keeps e as this thread's last HIP error (msa_last_hip_error) and returns MSA_ERR_HIP.
+int record_hip_error(hipError_t e);
+
 // Kernel launch bookkeeping for the optional event-based timing.
 void prof_begin(hipStream_t s, int kernel_id);
 void prof_end(hipStream_t s, int kernel_id);

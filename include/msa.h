@@ -209,6 +209,23 @@ msa_status_t msa_forward(const msa_problem_t* prob, const void* q, const void* k
                          const void* idx_q, const void* idx_k, int32_t* block_ids, void* out, float* lse,
                          void* ws, size_t ws_bytes, void* stream);
 
+/* msa_forward for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * same arguments as msa_forward without the workspace: the library uses its
+ * own scratch, one array of MSA_NOALLOC_SCRATCH_BYTES in each GPU's memory
+ * (held from the first call on that GPU until the process ends), processing
+ * the queries in chunks when the whole problem does not fit.  Results are
+ * bitwise those of msa_forward.  The call allocates nothing and calls no
+ * allocating routine.  Every call on one GPU shares that GPU's array: calls
+ * that overlap on one GPU (other host threads, or other streams not ordered
+ * with this one) race and must not be issued.  Errors: as msa_forward, and
+ * MSA_ERR_WORKSPACE when the problem's minimum workspace (msa_workspace_size,
+ * MSA_OP_FORWARD) exceeds MSA_NOALLOC_SCRATCH_BYTES. */
+#define MSA_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+msa_status_t msa_forward_noalloc(const msa_problem_t* prob, const void* q, const void* k, const void* v,
+                                 const void* idx_q, const void* idx_k, int32_t* block_ids, void* out, float* lse,
+                                 void* stream);
+
 /* Gradients of the Main Branch for the fixed selection block_ids (the
  * selection is not differentiable; the pages train the Index Branch by a
  * separate loss -- paper summary page, "Method").  Given the forward's out and

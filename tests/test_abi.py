@@ -21,6 +21,12 @@ def test_header_declares_the_binding_exports():
     assert declared_functions() == sorted(api.EXPORTS)
 
 
+def test_noalloc_scratch_size_matches_header():
+    src = open(os.path.join(ROOT, "include", "msa.h")).read()
+    m = re.search(r"#define MSA_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == api.NOALLOC_SCRATCH_BYTES
+
+
 def test_library_exports_every_declared_symbol():
     L = api.lib()
     for name in declared_functions():
@@ -117,6 +123,16 @@ def test_entry_points_reject_before_any_hip_call():
     assert q(x, api.F32, 4, 64, mis, x, null) == api.MSA_ERR_INVALID_ARG  # codes not 16-byte aligned
     assert q(x, api.F32, -1, 64, x, x, null) == api.MSA_ERR_INVALID_ARG
     assert q(x, api.F32, 0, 64, x, x, null) == api.MSA_OK                 # nothing to do
+    # the forward on the library's own scratch: problems whose least workspace
+    # exceeds the scratch are refused before the GPU is touched
+    na = L.msa_forward_noalloc
+    assert na(ctypes.byref(p), null, x, x, x, x, x, x, null, null) == api.MSA_ERR_INVALID_ARG
+    assert na(ctypes.byref(bad), x, x, x, x, x, x, x, null, null) == api.MSA_ERR_UNSUPPORTED
+    huge = good(dtype="bf16", batch=8, n_q=32768, n_k=32768, h_q=64, h_kv=8, d=128, d_idx=128, topk=32,
+                block_size=32)
+    _, least = api.workspace_size(huge, api.OP_FORWARD)
+    assert least > api.NOALLOC_SCRATCH_BYTES
+    assert na(ctypes.byref(huge), x, x, x, x, x, x, x, null, null) == api.MSA_ERR_WORKSPACE
 
 
 def test_workspace_sizes():
