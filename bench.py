@@ -1,19 +1,36 @@
 """Benchmark of the MSA forward hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill_32k]
-                    [--sched auto|kv_outer|q_outer] [--no-cpu] [--no-decode] [--no-train]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload chunk_16k_at_1m]
+                    [--sched auto|kv_outer|q_outer] [--no-cpu] [--no-legs] [--no-decode] [--no-train]
+                    [--no-topk] [--crossover]
+    python bench.py --summarize-pmc FETCH_DIR WRITE_DIR --pmc-kernel K --pmc-workload W   (no GPU)
+    python bench.py --summarize-stats STATS_DIR                                          (no GPU)
 
 One step = msa_forward (index scores + Top-k, inversion, attention, combine)
 over one batch of the seeded synthetic workload, inputs already in HBM.
-Prints one JSON line.  ``value`` is effective TFLOP/s over the selected,
-unmasked tokens, 4*d per (query head, key), divided by the whole forward
-step time.  The decode leg (16 sequences x 1M cached tokens, one new token
-each) reports microseconds per generated token.  The training legs time the
-Main Branch backward and the Index-Branch KL loss on the same workload and
-selection.  Per-kernel times come from
-hipEvents that libmsa records around each launch on the launch stream.
+``value`` is the metric "effective TFLOP/s over the selected tokens": 4*d
+flops per (query head, selected visible key) -- what the attention computes
+-- divided by the whole forward step time, on the 1M-token-context workload
+(16384 new queries at the end of a 1,048,576-token cache).  Each timed step
+is preceded by a 1 GiB scrub write, so it starts with cold caches; the same
+steps back to back (warm) are reported beside it.
+
+Also on the line, never as ``value``:
+  * ``roofline`` of the dominant kernel of the headline step against its
+    bound (the index tile: MFMA, with the method's flops);
+  * ``selection_check``: the GPU's selection of sampled rows against the
+    fp64 oracle (exact, tie-band and failing rows);
+  * legs: prefill_32k and the skewed 128k prefill (with block-popularity
+    figures), the decode step (16 sequences x 1M tokens; microseconds per
+    token), the standalone Top-k, the training kernels;
+  * ``cpu_baseline``: the oracle timed on a bounded sample of the headline
+    workload, on all host threads and on one.
+Per-kernel times come from hipEvents that libmsa records around each launch
+on the launch stream.
 """
 import argparse
+import csv
+import glob
 import hashlib
 import json
 import math
@@ -27,17 +44,19 @@ import torch
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from block_sparse_long_bk_amd import api, inputs  # noqa: E402
-
 METRIC = "MSA fwd effective TFLOP/s (selected tokens) & decode µs/token @1M ctx"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 matrix
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PROFILES = os.path.join(ROOT, "profiles")
+HEADLINE = "chunk_16k_at_1m"
+SCRUB_BYTES = 1 << 30
 
+
+# ---- work and bytes of the method ------------------------------------------
 
 def selected_tokens(wl, ids):
-    """Sum over (b, i, g) of the visible tokens in the selected blocks."""
+    """Sum over (b, i, g) of the visible tokens of the selected blocks."""
     Bk = wl.block_size
     pos = wl.q_offset + torch.arange(wl.n_q, device=ids.device, dtype=torch.int64).view(1, -1, 1, 1)
     j = ids.to(torch.int64)
@@ -49,53 +68,86 @@ def selected_tokens(wl, ids):
 
 
 def attention_flops(wl, ids):
+    """4*d per (query head, selected visible key): QK^T and PV."""
     G = wl.h_q // wl.h_kv
     return 4.0 * wl.d * G * selected_tokens(wl, ids)
 
 
-def attention_bytes(wl, ids):
-    """Algorithmic HBM bytes of the KV-outer attention and of the combine, per
-    launch over the whole problem: every selected (b, i, g, block) moves the
-    group's G query rows in and G partial rows (bf16/fp32 output + fp32 lse)
-    out; each selected key block is read once per (b, g); the combine reads
-    every partial, the block ids and writes the output and lse."""
-    e = 2 if wl.dtype == "bf16" else 4
-    G = wl.h_q // wl.h_kv
-    valid = ids >= 0
-    nnz = int(valid.sum().item())
-    flat = (torch.arange(wl.batch * wl.h_kv, device=ids.device).view(wl.batch, 1, wl.h_kv, 1) * wl.nblk
-            + ids.clamp(min=0).long())
-    uniq = int(torch.unique(flat[valid]).numel())
-    part_row = wl.d * e + 4
-    kv = nnz * G * wl.d * e + nnz * G * part_row + uniq * wl.block_size * wl.d * e * 2 + nnz * 4
-    comb = nnz * G * part_row + ids.numel() * 4 + wl.batch * wl.n_q * wl.h_q * (wl.d * e + 4)
-    return {"attn_kvouter": kv, "combine": comb, "selected_group_blocks": nnz}
-
-
 def index_flops(wl):
+    """2*d_idx per (query, group, candidate key): every token of the blocks j < L(i)."""
     L = (wl.q_offset + np.arange(wl.n_q, dtype=np.int64)) // wl.block_size
     return 2.0 * wl.d_idx * wl.h_kv * wl.batch * float(L.sum()) * wl.block_size
 
 
-def time_steps(fn, steps, warmup):
+def method_bytes(wl, ids):
+    """HBM bytes the attention step cannot avoid: Q in, every selected K/V
+    block once per (b, g), O and lse out."""
+    e = 2 if wl.dtype == "bf16" else 4
+    valid = ids >= 0
+    flat = (torch.arange(wl.batch * wl.h_kv, device=ids.device).view(wl.batch, 1, wl.h_kv, 1) * wl.nblk
+            + ids.clamp(min=0).long())
+    uniq = int(torch.unique(flat[valid]).numel())
+    q = wl.batch * wl.n_q * wl.h_q * wl.d * e
+    kv = uniq * wl.block_size * wl.d * e * 2
+    o = wl.batch * wl.n_q * wl.h_q * (wl.d * e + 4)
+    return q + kv + o
+
+
+def impl_bytes(wl, ids):
+    """What this implementation's KV-outer pass and combine move by design
+    (each selected (query, group, block) reads the group's G query rows and
+    writes G partial rows; the combine reads the partials back)."""
+    e = 2 if wl.dtype == "bf16" else 4
+    G = wl.h_q // wl.h_kv
+    nnz = int((ids >= 0).sum().item())
+    part_row = wl.d * e + 4
+    return {"attn_kvouter": nnz * G * (wl.d * e + part_row), "combine": nnz * G * part_row}
+
+
+# ---- timing ----------------------------------------------------------------
+
+def _scrub_buffer():
+    return torch.empty(SCRUB_BYTES, dtype=torch.uint8, device="cuda")
+
+
+def time_steps(fn, steps, warmup, scrub=None):
+    """Warm-up, then exactly `steps` timed calls of fn between two device
+    synchronisations.  With `scrub`, each call is preceded by a 1 GiB write
+    (cold caches) and only the calls are timed (events around each); without,
+    the calls run back to back.  Returns (ms per step, wall ms per step,
+    {kernel: (avg ms per launch, launches per step)})."""
+    from block_sparse_long_bk_amd import api
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     api.profile_reset()
-    api.profile_enable(True)
     st = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     torch.cuda.synchronize()
+    api.profile_enable(True)
     t0 = time.perf_counter()
-    e0.record(st)
-    for _ in range(steps):
-        fn()
-    e1.record(st)
+    if scrub is None:
+        ev[0][0].record(st)
+        for _ in range(steps):
+            fn()
+        ev[-1][1].record(st)
+    else:
+        for a, b in ev:
+            api.profile_enable(False)
+            scrub.fill_(1)
+            api.profile_enable(True)
+            a.record(st)
+            fn()
+            b.record(st)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     api.profile_enable(False)
-    kern = {k: (ms / n, n / steps) for k, (ms, n) in api.profile_read().items() if n}
-    return e0.elapsed_time(e1) / steps, wall * 1e3 / steps, kern
+    if scrub is None:
+        ms = ev[0][0].elapsed_time(ev[-1][1]) / steps
+    else:
+        ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    kern = {k: (t / n, n / steps) for k, (t, n) in api.profile_read().items() if n}
+    return ms, wall * 1e3 / steps, kern
 
 
 def source_hash(files):
@@ -103,6 +155,17 @@ def source_hash(files):
     for f in files:
         h.update(open(os.path.join(ROOT, f), "rb").read())
     return h.hexdigest()[:16]
+
+
+TRAFFIC_SOURCES = {
+    "index_tile_topk": ["block_sparse_long_bk_amd/csrc/index.hip", "block_sparse_long_bk_amd/csrc/msa_device.h",
+                        "block_sparse_long_bk_amd/csrc/msa_internal.h"],
+    "attn_kvouter": ["block_sparse_long_bk_amd/csrc/attention.hip", "block_sparse_long_bk_amd/csrc/attn_common.h",
+                     "block_sparse_long_bk_amd/csrc/msa_device.h", "block_sparse_long_bk_amd/csrc/msa_internal.h"],
+}
+# rocprofv3 kernel names of the profiled launch names
+TRACE_NAME = {"index_tile_topk": "k_index_tile", "attn_kvouter": "k_attn_kvouter", "combine": "k_combine",
+              "index_scan": "k_index_scan", "topk_rows": "k_topk", "attn_qouter": "k_attn_qouter"}
 
 
 def measured_traffic(kernel, workload):
@@ -117,36 +180,100 @@ def measured_traffic(kernel, workload):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(wl, x, n_sample):
-    """The fp64 oracle (as it stands) on an evenly spaced sample of queries."""
-    from oracle import oracle as O
+def roofline(kernel, avg_ms, *, flops=None, nbytes=None, peak_tflops=PEAK_BF16_TFLOPS, workload=None, method=None):
+    """Roofline entry of one kernel: MFMA-bound with the method's flops, or
+    HBM-bound with the method's bytes, per launch over its measured average."""
+    if flops is not None:
+        ach = flops / avg_ms / 1e9
+        r = {"bound": "mfma", "achieved": ach, "peak": peak_tflops, "unit": "TFLOP/s", "frac": ach / peak_tflops,
+             "method_flops_per_launch": flops}
+    else:
+        ach = nbytes / avg_ms / 1e6
+        r = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
+             "method_bytes_per_launch": nbytes}
+    r["kernel"] = kernel
+    r["avg_launch_ms"] = avg_ms
+    tr = measured_traffic(kernel, workload) if workload else None
+    r["traffic"] = tr
+    if tr is not None and method:
+        r["traffic_over_method_bytes"] = tr / method
+    return r
 
-    h = {k: v.cpu() for k, v in x.items()}
-    prob = O.problem_of(wl)
-    qi = np.unique(np.linspace(0, wl.n_q - 1, n_sample).astype(np.int64))
+
+# ---- the oracle on sampled rows ----------------------------------------------
+
+def sample_queries(wl, n):
+    """Evenly spaced queries plus the first, the last and those around block
+    boundaries."""
+    Bk = wl.block_size
+    qs = set(np.linspace(0, wl.n_q - 1, max(n - 8, 2)).astype(int).tolist()) | {0, wl.n_q - 1}
+    for p in np.linspace(wl.q_offset, wl.q_offset + wl.n_q - 1, 3).astype(int):
+        b = (p // Bk) * Bk
+        for pos in (b - 1, b, b + 1):
+            if wl.q_offset <= pos < wl.q_offset + wl.n_q:
+                qs.add(int(pos - wl.q_offset))
+    return np.array(sorted(qs)[:max(n, 2)], dtype=np.int64)
+
+
+def oracle_rows(wl, x_host, qi, threads=None):
+    """Index scores, selection and attention of the rows (0, qi) in fp64.
+    Returns (ids, scores, seconds, flops of the attention over those rows)."""
+    from oracle import oracle as O
+    if threads:
+        O.set_num_threads(threads)
+    prob = O.problem_of(wl.with_(batch=1))
     rows = np.stack([np.zeros_like(qi), qi], axis=1)
     t0 = time.perf_counter()
-    s = O.block_scores(prob, h["iq"], h["ik"], rows)
+    s = O.block_scores(prob, x_host["iq"], x_host["ik"], rows)
     ids = O.select(prob, s, rows)
-    O.attend(prob, h["q"], h["k"], h["v"], ids, rows)
+    O.attend(prob, x_host["q"], x_host["k"], x_host["v"], ids, rows)
     dt = time.perf_counter() - t0
-    ids_t = torch.from_numpy(ids).view(len(qi), 1, wl.h_kv, wl.topk)
-    # selected visible tokens for the sampled queries
-    pos = torch.from_numpy(wl.q_offset + qi).view(-1, 1, 1, 1)
-    j = ids_t.to(torch.int64)
+    pos = torch.from_numpy(wl.q_offset + qi).view(-1, 1, 1)
+    j = torch.from_numpy(ids).to(torch.int64)
     n = torch.minimum(pos - j * wl.block_size + 1, torch.full_like(j, wl.block_size))
     n = torch.where(j >= 0, n.clamp(min=0), torch.zeros_like(n))
     flops = 4.0 * wl.d * (wl.h_q // wl.h_kv) * float(n.sum())
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": O.num_threads(), "kind": "oracle",
-            "sample": f"{len(qi)} of {wl.n_q} queries (evenly spaced), all {wl.h_q} heads; index scores, "
-                      f"Top-k and attention in fp64; {dt:.1f} s",
-            "seconds": dt}
+    return ids, s, dt, flops
 
 
-def run_prefill(args):
-    wl = inputs.WORKLOADS[args.workload]
+def host_inputs(x):
+    return {k: v[:1].cpu() for k, v in x.items()}
+
+
+def selection_check(wl, ids_gpu, qi, ids_o, s_o):
+    from tests.parity import check_selection
+    got = ids_gpu[0, torch.from_numpy(qi).to(ids_gpu.device)].cpu().numpy()
+    rows = np.stack([np.zeros_like(qi), qi], axis=1)
+    res = check_selection(wl.with_(batch=1), got, ids_o, s_o, rows=rows)
+    return {"rows": int(len(qi) * wl.h_kv), "exact": res["exact"], "tie_band": res["tie"], "fail": res["fail"]}
+
+
+def cpu_baseline(wl, xh, n_sample, n_sample_1t):
+    """The oracle as it stands, timed on a bounded sample of the workload's
+    queries (all their heads and groups): on every host thread, and on one."""
+    from oracle import oracle as O
+    qi = sample_queries(wl, n_sample)
+    threads = O.num_threads()
+    ids, s, dt, fl = oracle_rows(wl, xh, qi, threads)
+    qi1 = qi[np.linspace(0, len(qi) - 1, n_sample_1t).astype(int)]
+    _, _, dt1, fl1 = oracle_rows(wl, xh, qi1, 1)
+    O.set_num_threads(threads)
+    per_q = dt / len(qi)
+    return ({"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+             "sample": f"{len(qi)} of {wl.n_q} queries of {wl.name} (first, last, block boundaries, evenly spaced), "
+                       f"all {wl.h_q} heads: index scores, Top-k and attention in fp64, {dt:.1f} s",
+             "seconds": dt, "extrapolated_full_step_s": per_q * wl.n_q * wl.batch,
+             "value_1thread": fl1 / dt1 / 1e12, "seconds_1thread": dt1,
+             "sample_1thread": f"{len(qi1)} of those queries on one thread"},
+            qi, ids, s)
+
+
+# ---- legs --------------------------------------------------------------------
+
+def run_forward(wl, args, sched="auto", cold=True):
+    from block_sparse_long_bk_amd import api, inputs
     x = inputs.generate(wl, device="cuda")
-    p = api.problem_of(wl, sched=args.sched)
+    p = api.problem_of(wl, sched=sched)
     ws = api.alloc_workspace(p, api.OP_FORWARD)
     ids = torch.empty((wl.batch, wl.n_q, wl.h_kv, wl.topk), dtype=torch.int32, device="cuda")
     out = torch.empty_like(x["q"])
@@ -157,26 +284,86 @@ def run_prefill(args):
 
     step()
     torch.cuda.synchronize()
-    fl_attn = attention_flops(wl, ids)
-    fl_idx = index_flops(wl)
-    nbytes = attention_bytes(wl, ids)
-    ms, wall_ms, kern = time_steps(step, args.steps, args.warmup)
-    res = dict(wl=wl, x=x, ms=ms, wall_ms=wall_ms, kern=kern, fl_attn=fl_attn, fl_idx=fl_idx, ws=ws.numel(),
-               bytes=nbytes, ids=ids, out=out, lse=lse)
+    r = dict(wl=wl, x=x, ids=ids, out=out, lse=lse, ws_bytes=ws.numel(),
+             fl_attn=attention_flops(wl, ids), fl_idx=index_flops(wl), mbytes=method_bytes(wl, ids),
+             ibytes=impl_bytes(wl, ids))
+    if cold:
+        scrub = _scrub_buffer()
+        r["ms"], r["wall_ms"], r["kern"] = time_steps(step, args.steps, args.warmup, scrub=scrub)
+        del scrub
+    r["ms_warm"], _, r["kern_warm"] = time_steps(step, args.steps, 1)
+    if not cold:
+        r["ms"], r["wall_ms"], r["kern"] = r["ms_warm"], None, r["kern_warm"]
     del ws
-    return res
+    return r
+
+
+def kernels_ms(kern):
+    return {k: round(v[0], 4) for k, v in kern.items()}
+
+
+def forward_summary(r):
+    wl, kern = r["wl"], r["kern"]
+    peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
+    attn_ms = sum(v[0] * v[1] for k, v in kern.items() if k.startswith(("inv_", "attn_")) or k == "combine")
+    out = {"workload": wl.name, "ms_per_step": r["ms"], "ms_per_step_warm": r["ms_warm"],
+           "effective_TFLOPs": r["fl_attn"] / r["ms"] / 1e9,
+           "effective_TFLOPs_warm": r["fl_attn"] / r["ms_warm"] / 1e9,
+           "attention_tflops_per_step": r["fl_attn"] / 1e12, "index_tflops_per_step": r["fl_idx"] / 1e12,
+           "sparse_attention_TFLOPs": r["fl_attn"] / attn_ms / 1e9 if attn_ms else None,
+           "kernels_ms": kernels_ms(kern), "kernels_ms_warm": kernels_ms(r["kern_warm"]),
+           "kernel_launches_per_step": {k: v[1] for k, v in kern.items()},
+           "method_bytes_attention": r["mbytes"], "workspace_bytes": r["ws_bytes"]}
+    it = [k for k in kern if k.startswith("index_tile")]
+    if it:
+        out["index_tile"] = roofline(it[0], kern[it[0]][0], flops=r["fl_idx"], peak_tflops=peak, workload=wl.name)
+    if "attn_kvouter" in kern:
+        ms = kern["attn_kvouter"][0] * kern["attn_kvouter"][1]
+        out["attn_kvouter"] = roofline("attn_kvouter", ms, flops=r["fl_attn"], peak_tflops=peak, workload=wl.name,
+                                       method=r["mbytes"])
+        out["attn_kvouter"]["design_bytes_per_launch"] = r["ibytes"]["attn_kvouter"]
+        out["attn_kvouter"]["design_GBs"] = r["ibytes"]["attn_kvouter"] / ms / 1e6
+    if "combine" in kern:
+        out["combine_GBs"] = r["ibytes"]["combine"] / kern["combine"][0] / kern["combine"][1] / 1e6
+    return out
+
+
+def skew_figures(wl, ids, kern):
+    """Block popularity of the selection and what KV-outer makes of it."""
+    from block_sparse_long_bk_amd import inputs
+    G = wl.h_q // wl.h_kv
+    qi = min(2048 // G, 1024)  # (query, slot) entries per KV-outer work item
+    flat = ids.view(wl.batch, wl.n_q, wl.h_kv, wl.topk).permute(0, 2, 1, 3).reshape(wl.batch * wl.h_kv, -1).long()
+    cnt = torch.stack([torch.bincount(r[r >= 0], minlength=wl.nblk) for r in flat])  # [B*Hkv, nblk]
+    sel = cnt[cnt > 0].double()
+    items = torch.ceil(cnt.double() / qi)
+    hot = inputs.hot_blocks(wl, "cuda")[0] if wl.hot_frac > 0 else None
+    out = {"picks_per_selected_block": {"mean": float(sel.mean()), "p50": float(sel.quantile(0.5)),
+                                        "p99": float(sel.quantile(0.99)), "max": int(sel.max())},
+           "work_items": {"total": int(items.sum()), "max_per_block": int(items.max()),
+                          "p99_per_block": float(items[cnt > 0].quantile(0.99))},
+           "entries_per_item": qi}
+    if hot is not None:
+        on_hot = cnt[:, hot].sum()
+        out["hot_blocks"] = int(hot.numel())
+        out["share_of_picks_on_hot_blocks"] = float(on_hot / cnt.sum())
+        out["picks_per_hot_block"] = {"mean": float(cnt[:, hot].double().mean()), "max": int(cnt[:, hot].max())}
+    sel_keys = selected_tokens(wl, ids) * G
+    if "attn_kvouter" in kern:
+        out["kvouter_ns_per_1k_query_head_keys"] = kern["attn_kvouter"][0] * kern["attn_kvouter"][1] * 1e9 / sel_keys
+    return out
 
 
 def run_training(args, r):
     """The training-side kernels on the same workload and selection: the
-    Main Branch backward (msa_sparse_attention_backward) and the Index-Branch
-    KL loss with its gradients (msa_indexer_kl).  Effective TFLOP/s count the
-    products over the selected, unmasked tokens: backward 5 x 2d per (query
-    head, key) (S, dP, dV, dK, dQ); KL 2d per (query head, key) for the Main
-    Branch probabilities plus 4 x 2 d_idx per (query group, key) (index
-    scores twice, d iq, d ik)."""
+    Main Branch backward and the Index-Branch KL loss with its gradients.
+    Effective TFLOP/s count the products over the selected, unmasked tokens:
+    backward 5 x 2d per (query head, key) (S, dP, dV, dK, dQ); KL 2d per
+    (query head, key) for the Main Branch probabilities plus 4 x 2 d_idx per
+    (query group, key) (index scores twice, d iq, d ik)."""
+    from block_sparse_long_bk_amd import api, inputs
     wl, x, ids = r["wl"], r["x"], r["ids"]
-    p = api.problem_of(wl, sched=args.sched)
+    p = api.problem_of(wl)
     dout = inputs.generate(wl, device="cuda", tensors=("dout",))["dout"]
     sel = selected_tokens(wl, ids)
     G = wl.h_q // wl.h_kv
@@ -204,19 +391,21 @@ def run_training(args, r):
     del ws, kl, d_iq, d_ik
     torch.cuda.empty_cache()
     return {
-        "backward": {"ms_per_step": ms_b, "effective_TFLOPs": fl_b / ms_b / 1e9, "tflops_per_step": fl_b / 1e12,
-                     "mfma_frac": fl_b / ms_b / 1e9 / PEAK_BF16_TFLOPS,
-                     "kernels_ms": {k: round(v[0], 4) for k, v in kern_b.items()}},
-        "indexer_kl": {"ms_per_step": ms_k, "effective_TFLOPs": fl_k / ms_k / 1e9, "tflops_per_step": fl_k / 1e12,
-                       "kernels_ms": {k: round(v[0], 4) for k, v in kern_k.items()}},
+        "backward": {"workload": wl.name, "ms_per_step": ms_b, "effective_TFLOPs": fl_b / ms_b / 1e9,
+                     "tflops_per_step": fl_b / 1e12, "mfma_frac": fl_b / ms_b / 1e9 / PEAK_BF16_TFLOPS,
+                     "kernels_ms": kernels_ms(kern_b)},
+        "indexer_kl": {"workload": wl.name, "ms_per_step": ms_k, "effective_TFLOPs": fl_k / ms_k / 1e9,
+                       "tflops_per_step": fl_k / 1e12, "kernels_ms": kernels_ms(kern_k)},
     }
 
 
 def run_decode(args, idx_format="plain", kv_format="plain"):
-    """decode_16x1m forward steps.  idx_format "mxfp8": the idx_k cache is
-    quantised once (untimed) to MXFP8 by msa_mxfp8_quantize and the index scan
-    reads codes + scales (d_idx + d_idx/32 bytes per key) instead of bf16;
-    kv_format "mxfp8": K and V too (d + d/32 bytes per key and tensor)."""
+    """decode_16x1m forward steps (cold: a 1 GiB scrub before each).
+    idx_format "mxfp8": the idx_k cache is quantised once (untimed) to MXFP8
+    by msa_mxfp8_quantize and the index scan reads codes + scales
+    (d_idx + d_idx/32 bytes per key) instead of bf16; kv_format "mxfp8": K
+    and V too (d + d/32 bytes per key and tensor)."""
+    from block_sparse_long_bk_amd import api, inputs
     wl = inputs.WORKLOADS["decode_16x1m"]
     x = inputs.generate(wl, device="cuda")
     p = api.problem_of(wl, sched="auto", idx_format=idx_format, kv_format=kv_format)
@@ -237,7 +426,10 @@ def run_decode(args, idx_format="plain", kv_format="plain"):
     step()
     torch.cuda.synchronize()
     steps = max(3, args.steps)
-    ms, wall_ms, kern = time_steps(step, steps, args.warmup)
+    scrub = _scrub_buffer()
+    ms, _, kern = time_steps(step, steps, args.warmup, scrub=scrub)
+    del scrub
+    ms_w, _, _ = time_steps(step, steps, 1)
     # algorithmic bytes: idx_k of every candidate block, the selected K/V
     # tokens, the index and attention queries, block scores, ids and outputs
     L = (wl.q_offset + wl.n_q - 1) // wl.block_size
@@ -248,11 +440,54 @@ def run_decode(args, idx_format="plain", kv_format="plain"):
     b_kv = sel * (wl.d + wl.d // 32 if kv_format == "mxfp8" else wl.d * e) * 2
     b_small = wl.batch * (wl.h_kv * wl.d_idx + 2 * wl.h_q * wl.d) * e + wl.batch * wl.h_kv * L * 4 * 2
     total = b_idx + b_kv + b_small
+    res = {"workload": wl.name, "idx_format": idx_format, "kv_format": kv_format,
+           "us_per_token": ms * 1e3 / (wl.batch * wl.n_q), "ms_per_step": ms,
+           "us_per_token_warm": ms_w * 1e3 / (wl.batch * wl.n_q), "algorithmic_bytes": total,
+           "hbm_GBs": total / ms / 1e6, "hbm_frac": total / ms / 1e6 / PEAK_HBM_GBS,
+           "kernels_ms": kernels_ms(kern)}
+    if "index_scan" in kern:
+        res["index_scan"] = roofline("index_scan", kern["index_scan"][0], nbytes=b_idx, workload=wl.name)
     del x, ws, ik
     torch.cuda.empty_cache()
-    return {"workload": wl.name, "idx_format": idx_format, "kv_format": kv_format, "us_per_token": ms * 1e3 / (wl.batch * wl.n_q), "ms_per_step": ms,
-            "algorithmic_bytes": total, "hbm_GBs": total / ms / 1e6, "hbm_frac": total / ms / 1e6 / PEAK_HBM_GBS,
-            "kernels_ms": {k: round(v[0], 4) for k, v in kern.items()}}
+    return res
+
+
+def run_topk(args, cands=(1024, 2048, 4096, 8191), topk=16):
+    """msa_topk_from_scores on its own (the pages benchmark their Top-k
+    kernel separately): rows of C candidate blocks (C*128 context tokens) for
+    the decode case (16 sequences x 8 groups = 128 rows) and for a prefill
+    chunk's worth of rows (262,144 = 256 x 8 x 128), torch.topk on the same
+    rows beside it for scale (it neither forces the local block nor breaks
+    ties by the lower id)."""
+    from block_sparse_long_bk_amd import api
+    res = []
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4242)
+    for C in cands:
+        for case, B, nq in (("decode_128_rows", 16, 1), ("prefill_262144_rows", 256, 128)):
+            rows = B * 8 * nq
+            if case.startswith("prefill") and C > 4096:
+                continue
+            n_k = (C + 1) * 128
+            p = api.problem(B, nq, n_k, 64, 8, 128, 128, topk, dtype="bf16", q_offset=C * 128)
+            S = torch.randn((B, 8, nq, C + 1), generator=g, device="cuda", dtype=torch.float32)
+            ids = torch.empty((B, nq, 8, topk), dtype=torch.int32, device="cuda")
+            ms, _, kern = time_steps(lambda: api.topk_from_scores(p, S, ids), 10, 2)
+            Sv = S[..., :C].reshape(rows, C)
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.topk(Sv, topk - 1, dim=1)
+            ev0.record()
+            for _ in range(10):
+                torch.topk(Sv, topk - 1, dim=1)
+            ev1.record()
+            torch.cuda.synchronize()
+            t_ms = ev0.elapsed_time(ev1) / 10
+            res.append({"case": case, "rows": rows, "candidates": C, "context_tokens": C * 128,
+                        "us": kern["topk_rows"][0] * 1e3, "scores_GBs": rows * C * 4 / kern["topk_rows"][0] / 1e6,
+                        "torch_topk_us": t_ms * 1e3})
+            del S, ids, Sv
+    torch.cuda.empty_cache()
+    return res
 
 
 def run_crossover(args, chunks=(256, 512, 1024, 1460, 2048, 4096, 16384)):
@@ -260,6 +495,7 @@ def run_crossover(args, chunks=(256, 512, 1024, 1460, 2048, 4096, 16384)):
     1M-token chunked-prefill cache (2 % hot blocks).  reuse = c*k*Bk/Nk is the
     average number of reads of a KV token, the quantity whose crossover the
     Fireworks note on KV-stationary attention puts near 2.85."""
+    from block_sparse_long_bk_amd import api, inputs
     base = inputs.WORKLOADS["chunk_16k_at_1m"]
     x = inputs.generate(base, device="cuda")
     rows = []
@@ -290,27 +526,123 @@ def run_crossover(args, chunks=(256, 512, 1024, 1460, 2048, 4096, 16384)):
     return rows
 
 
+# ---- rocprofv3 summaries (no GPU) ---------------------------------------------
+
+def _pmc_rows(d):
+    fs = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    assert fs, f"no counter_collection.csv under {d}"
+    rows = []
+    for f in fs:
+        rows += list(csv.DictReader(open(f)))
+    return rows
+
+
+def summarize_pmc(fetch_dir, write_dir, kernel, workload):
+    """Per-launch HBM bytes of each kernel from a FETCH_SIZE and a WRITE_SIZE
+    run (KiB per dispatch), each scaled by what the counter reads for the
+    plain 1 GiB device copy in the same run; writes the traffic record of
+    `kernel` and prints a markdown table."""
+    per = {}
+    for d, cname in ((fetch_dir, "FETCH_SIZE"), (write_dir, "WRITE_SIZE")):
+        for r in _pmc_rows(d):
+            if r.get("Counter_Name") != cname:
+                continue
+            name = r["Kernel_Name"]
+            key = (name, r.get("Dispatch_Id") or r.get("Correlation_Id"))
+            per.setdefault(cname, {}).setdefault(name, {}).setdefault(key, 0.0)
+            per[cname][name][key] += float(r["Counter_Value"]) * 1024.0
+    # the 1 GiB calibration copy (--calib-copy-mib 1024) is the largest dispatch
+    # of the runtime's device-to-device copy kernel
+    fac = {}
+    for cname in ("FETCH_SIZE", "WRITE_SIZE"):
+        vals = [v for n in per[cname] if "copybuffer" in n.lower() for v in per[cname][n].values()]
+        assert vals, f"no calibration copy in the {cname} run"
+        fac[cname] = float(1 << 30) / max(vals)
+    lines = ["| kernel | launches | scaled read GB | scaled write GB | total GB |", "|---|---:|---:|---:|---:|"]
+    rec_bytes = None
+    for name in sorted(per["FETCH_SIZE"], key=lambda n: -np.mean(list(per["FETCH_SIZE"][n].values()))):
+        f = np.mean(list(per["FETCH_SIZE"][name].values())) * fac["FETCH_SIZE"]
+        w = np.mean(list(per.get("WRITE_SIZE", {}).get(name, {0: 0.0}).values())) * fac["WRITE_SIZE"]
+        short = _short(name)
+        lines.append(f"| {short} | {len(per['FETCH_SIZE'][name])} | {f / 1e9:.3f} | {w / 1e9:.3f} | {(f + w) / 1e9:.3f} |")
+        if TRACE_NAME.get(kernel, kernel) in name:
+            rec_bytes = f + w if rec_bytes is None else max(rec_bytes, f + w)
+    print(f"factors: FETCH_SIZE x {fac['FETCH_SIZE']:.3f}, WRITE_SIZE x {fac['WRITE_SIZE']:.3f}")
+    print("\n".join(lines))
+    if rec_bytes is not None and kernel in TRAFFIC_SOURCES:
+        rec = {"kernel": kernel, "workload": workload, "bytes_per_launch": rec_bytes,
+               "fetch_factor": fac["FETCH_SIZE"], "write_factor": fac["WRITE_SIZE"],
+               "sources": TRAFFIC_SOURCES[kernel], "source_hash": source_hash(TRAFFIC_SOURCES[kernel])}
+        path = os.path.join(PROFILES, f"{kernel}_{workload}_traffic.json")
+        json.dump(rec, open(path, "w"), indent=1)
+        print(f"wrote {path}")
+
+
+KERNELS = ("k_index_tile", "k_index_scan", "k_attn_kvouter", "k_attn_qouter", "k_combine", "k_inv_hist",
+           "k_inv_colscan", "k_inv_blkscan", "k_inv_scatter", "k_inv_items", "k_topk_rows", "k_topk_wg",
+           "k_bwd_rowdot", "k_bwd_split", "k_bwd_fused", "k_bwd_dq_sum", "k_bwd_dkdv_reduce", "k_kl_lse",
+           "k_kl_lse_sum", "k_kl_main", "k_kl_main8", "k_kl_finish", "k_kl_dik_reduce", "k_mxfp8_quantize",
+           "k_fill_neg_inf")
+
+
+def _short(name):
+    """The library's kernel name inside a mangled or demangled symbol."""
+    for k in sorted(KERNELS, key=len, reverse=True):
+        if k in name:
+            return k
+    return name.split("(")[0].split("<")[0].split("::")[-1][:48] or "(unnamed)"
+
+
+def summarize_stats(d):
+    """Markdown table of a rocprofv3 --stats kernel summary."""
+    fs = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    assert fs, f"no kernel_stats.csv under {d}"
+    rows = list(csv.DictReader(open(fs[0])))
+    print("| kernel | calls | avg us | min us | max us | total ms |")
+    print("|---|---:|---:|---:|---:|---:|")
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        name = _short(r["Name"])
+        print(f"| {name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+              f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['TotalDurationNs']) / 1e6:.2f} |")
+
+
+# ---- main --------------------------------------------------------------------
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="prefill_32k", choices=sorted(inputs.WORKLOADS))
+    ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--sched", default="auto", choices=["auto", "kv_outer", "q_outer"])
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-legs", action="store_true", help="skip the prefill_32k and skewed_prefill_128k legs")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-train", action="store_true", help="skip the backward and indexer-loss legs")
-    ap.add_argument("--cpu-sample", type=int, default=8192)
+    ap.add_argument("--no-topk", action="store_true", help="skip the standalone Top-k timing")
+    ap.add_argument("--cpu-sample", type=int, default=256, help="oracle queries of the headline workload")
+    ap.add_argument("--cpu-sample-1thread", type=int, default=3, help="of those, timed again on one thread")
     ap.add_argument("--crossover", action="store_true",
                     help="also time both attention schedules on query chunks at the end of a 1M-token cache")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (reference for HBM counters)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--pmc-kernel", default="index_tile_topk")
+    ap.add_argument("--pmc-workload", default=HEADLINE)
+    ap.add_argument("--summarize-stats", metavar="STATS_DIR")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc, args.pmc_kernel, args.pmc_workload)
+        return
+    if args.summarize_stats:
+        summarize_stats(args.summarize_stats)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this MSA forward path is built and measured on a single GPU "
               "(one GPU's share of the work at its real shape); --gpus must be 1", file=sys.stderr)
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    from block_sparse_long_bk_amd import inputs
 
     if args.calib_copy_mib:
         src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda")
@@ -318,68 +650,56 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    r = run_prefill(args)
-    wl, kern = r["wl"], r["kern"]
-    value = r["fl_attn"] / r["ms"] / 1e9  # TFLOP/s
-    peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
+    wl = inputs.WORKLOADS[args.workload]
+    r = run_forward(wl, args, sched=args.sched)
+    fs = forward_summary(r)
+    kern = r["kern"]
+    value = r["fl_attn"] / r["ms"] / 1e9  # TFLOP/s, cold caches
     dom = max(kern, key=lambda k: kern[k][0] * kern[k][1])
-    # Algorithmic work of the dominant kernel per launch.  The KV-outer kernel
-    # moves (Q rows + partials) ~ 2*(2D+4)*G bytes per selected (query, group,
-    # block) against 4*D*G*128 flops: ~127 flop/B at d=128, below the MI355X
-    # balance of ~312 flop/B, so its roof is HBM; the index kernel's is MFMA.
-    bytes_kv = r["bytes"]["attn_kvouter"]
-    if dom == "attn_kvouter":
-        achieved = bytes_kv / kern[dom][1] / kern[dom][0] / 1e6
-        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
-    elif dom == "combine":
-        achieved = r["bytes"]["combine"] / kern[dom][1] / kern[dom][0] / 1e6
-        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
-    elif dom.startswith("attn_"):
-        achieved = r["fl_attn"] / kern[dom][1] / kern[dom][0] / 1e9
-        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s"}
-    elif dom.startswith("index_tile"):
-        achieved = r["fl_idx"] / kern[dom][0] / 1e9
-        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s"}
-    else:
-        roof = {"bound": "hbm", "achieved": None, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
-    roof["kernel"] = dom
-    roof["algorithmic_bytes_per_launch"] = bytes_kv if dom == "attn_kvouter" else None
-    roof["frac"] = roof["achieved"] / roof["peak"] if roof["achieved"] else None
-    roof["traffic"] = measured_traffic(dom, wl.name)
+    roof = fs.get("index_tile") if dom.startswith("index_tile") else fs.get(dom)
+    if roof is None:
+        roof = {"bound": None, "kernel": dom, "achieved": None, "peak": None, "unit": None, "frac": None,
+                "traffic": None}
     line = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": r["ms"], "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
         "config": {"workload": wl.name, "batch": wl.batch, "n_q": wl.n_q, "n_k": wl.n_k, "q_offset": wl.q_offset,
                    "block_size": wl.block_size, "topk": wl.topk, "h_q": wl.h_q, "h_kv": wl.h_kv, "d": wl.d,
-                   "d_idx": wl.d_idx, "sched": args.sched, "hot_frac": wl.hot_frac},
+                   "d_idx": wl.d_idx, "sched": args.sched, "hot_frac": wl.hot_frac,
+                   "caches": "cold (1 GiB scrub before each timed step)"},
         "roofline": roof,
-        "attention_tflops_per_step": r["fl_attn"] / 1e12, "index_tflops_per_step": r["fl_idx"] / 1e12,
-        "index_TFLOPs": None, "wall_ms_per_step": r["wall_ms"],
-        "attn_kvouter_TFLOPs": (r["fl_attn"] / kern["attn_kvouter"][0] / 1e9) if "attn_kvouter" in kern else None,
-        # the same work over the attention part of the step alone (inversion, attention, combine: the
-        # msa_sparse_attention calls), i.e. without the index scoring and selection
-        "sparse_attention_TFLOPs": r["fl_attn"] / sum(v[0] * v[1] for k, v in kern.items()
-                                                      if k.startswith(("inv_", "attn_")) or k == "combine") / 1e9,
-        "attn_kvouter_GBs": (r["bytes"]["attn_kvouter"] / kern["attn_kvouter"][0] / 1e6)
-        if "attn_kvouter" in kern else None,
-        "combine_GBs": (r["bytes"]["combine"] / kern["combine"][0] / 1e6) if "combine" in kern else None,
-        "algorithmic_bytes": r["bytes"],
-        "kernels_ms": {k: round(v[0], 4) for k, v in kern.items()},
-        "kernel_launches_per_step": {k: v[1] for k, v in kern.items()},
-        "workspace_bytes": r["ws"],
+        "warm": {"value": fs["effective_TFLOPs_warm"], "ms_per_step": r["ms_warm"]},
+        "headline": fs,
     }
-    it = [k for k in kern if k.startswith("index_tile")]
-    if it:
-        line["index_TFLOPs"] = r["fl_idx"] / kern[it[0]][0] / 1e9
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(wl, r["x"], args.cpu_sample)
-    if not args.no_train:
-        # training-side kernels on the same workload (reported beside the
-        # forward figure, never as `value`)
-        line.update(run_training(args, r))
+        xh = host_inputs(r["x"])
+        base, qi, ids_o, s_o = cpu_baseline(wl, xh, args.cpu_sample, args.cpu_sample_1thread)
+        line["cpu_baseline"] = base
+        line["selection_check"] = selection_check(wl, r["ids"], qi, ids_o, s_o)
+        del xh
     del r
     torch.cuda.empty_cache()
+    if not args.no_legs:
+        for name in ("prefill_32k", "skewed_prefill_128k"):
+            rl = run_forward(inputs.WORKLOADS[name], args, sched=args.sched)
+            leg = forward_summary(rl)
+            leg["skew"] = skew_figures(rl["wl"], rl["ids"], rl["kern"])
+            if not args.no_cpu:
+                xh = host_inputs(rl["x"])
+                qi = sample_queries(rl["wl"], 64)
+                ids_o, s_o, _, _ = oracle_rows(rl["wl"], xh, qi)
+                leg["selection_check"] = selection_check(rl["wl"], rl["ids"], qi, ids_o, s_o)
+                del xh
+            line[name] = leg
+            if name == "prefill_32k" and not args.no_train:
+                line.update(run_training(args, rl))
+            del rl
+            torch.cuda.empty_cache()
+        a, b = line["prefill_32k"]["skew"], line["skewed_prefill_128k"]["skew"]
+        if "kvouter_ns_per_1k_query_head_keys" in a and "kvouter_ns_per_1k_query_head_keys" in b:
+            line["skewed_prefill_128k"]["kvouter_time_per_key_vs_prefill_32k"] = (
+                b["kvouter_ns_per_1k_query_head_keys"] / a["kvouter_ns_per_1k_query_head_keys"])
     if args.crossover:
         line["crossover"] = run_crossover(args)
     if not args.no_decode:
@@ -389,6 +709,8 @@ def main():
         line["decode_mxfp8"] = run_decode(args, idx_format="mxfp8")
         # and over an all-MXFP8 cache (index keys, K and V)
         line["decode_mxfp8_cache"] = run_decode(args, idx_format="mxfp8", kv_format="mxfp8")
+    if not args.no_topk:
+        line["topk_standalone"] = run_topk(args)
     print(json.dumps(line), flush=True)
 
 

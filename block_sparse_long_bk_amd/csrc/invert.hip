@@ -133,14 +133,18 @@ __global__ void __launch_bounds__(1024) k_inv_blkscan(InvArgs a) {
   }
 }
 
-// One wave per (b, g, tile).  LDS: cursors [nblk] then the tile's ids, one
+// One wave per (b, g, tile).  LDS: cursors [nblk], then the tile's ids, one
 // row of inv_row_pitch(topk) words per query (rows padded to whole 16-byte
-// chunks with -1, so that a step reads its row with 16-byte broadcasts).
+// chunks with -1, so that a step reads its row with 16-byte broadcasts), then
+// one flag per row: set where the row's valid ids are not strictly ascending,
+// the only rows that can name a block twice (the Index Branch writes its rows
+// ascending, so for them every flag is clear and each step is a single pass).
 __global__ void __launch_bounds__(64) k_inv_scatter(InvArgs a) {
   extern __shared__ __attribute__((aligned(16))) int32_t sm[];
   int32_t* cur = sm;
   const int tp = inv_row_pitch(a.topk);
   int32_t* tids = sm + ((a.nblk + 3) & ~3);
+  int32_t* unsorted = tids + kInvTile * tp;
   const int tile = blockIdx.x, bg = blockIdx.y;
   const int b = bg / a.Hkv, g = bg % a.Hkv;
   const int lane = threadIdx.x;
@@ -154,11 +158,33 @@ __global__ void __launch_bounds__(64) k_inv_scatter(InvArgs a) {
     tids[e] = s < a.topk ? a.ids[(((int64_t)b * a.Nq + a.q0 + qq) * a.Hkv + g) * a.topk + s] : -1;
   }
   __syncthreads();
+  for (int t = lane; t < nt; t += 64) {
+    const int32_t* row = tids + t * tp;
+    int last = -1, bad = 0;
+    for (int s = 0; s < a.topk; ++s) {
+      const int v = row[s];
+      if (v >= 0 && v < a.nblk) {
+        bad |= v <= last ? 1 : 0;
+        last = v;
+      }
+    }
+    unsorted[t] = bad;
+  }
+  __syncthreads();
   int32_t* ent = a.entries + (int64_t)bg * a.nq * a.topk;
   for (int t = 0; t < nt; ++t) {
     const int32_t* row = tids + t * tp;
     const int j = lane < a.topk ? row[lane] : -1;
     const bool ok = j >= 0 && j < a.nblk;
+    if (!__builtin_amdgcn_readfirstlane(unsorted[t])) {  // distinct blocks: one cursor per lane
+      if (ok) {
+        const int32_t pos = cur[j];
+        cur[j] = pos + 1;
+        ent[pos] = (qbeg + t) * a.topk + lane;
+      }
+      wave_lds_sync();  // the next step may read a cursor another lane just advanced
+      continue;
+    }
     // rank among the lower slots of this row that name the same block, and
     // how many slots name it
     int rank = 0, cnt = 0;
@@ -261,7 +287,7 @@ hipError_t launch_invert(const Shape& s, const InvertPlan& p, const int32_t* ids
   MSA_INV_LAUNCH(k2, k_inv_colscan, dim3((s.nblk + 255) / 256, BG), dim3(256), 0, st, a)
   MSA_INV_LAUNCH(k3, k_inv_blkscan, dim3(BG), dim3(1024), 0, st, a)
   MSA_INV_LAUNCH(k4, k_inv_scatter, dim3(a.n_tiles, BG), dim3(64),
-                 (size_t)(((s.nblk + 3) & ~3) + kInvTile * inv_row_pitch(s.topk)) * 4, st, a)
+                 (size_t)(((s.nblk + 3) & ~3) + kInvTile * (inv_row_pitch(s.topk) + 1)) * 4, st, a)
   if (out.items) {
     MSA_INV_LAUNCH(k5, k_inv_items, dim3(p.items_cap / 256 + 1, BG), dim3(256), 0, st, a)
   }

@@ -76,6 +76,10 @@ static int check_rows(const mo_problem* p, const int64_t* rows, int64_t n_rows) 
 
 int mo_num_threads(void) { return omp_get_max_threads(); }
 
+void mo_set_num_threads(int n) {
+  if (n > 0) omp_set_num_threads(n);
+}
+
 /* Steps 1 and 2: token scores and Block Max Pooling. */
 int mo_block_scores(const mo_problem* p, const void* iq, const void* ik, int dtype,
                     const int64_t* rows, int64_t n_rows, double* scores) {

@@ -134,6 +134,9 @@ int mo_mxfp8_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t n_r
 /* Number of OpenMP threads the routines above use. */
 int mo_num_threads(void);
 
+/* Threads the following calls may use (n >= 1; results do not depend on it). */
+void mo_set_num_threads(int n);
+
 #ifdef __cplusplus
 }
 #endif

@@ -128,6 +128,9 @@ class Oracle:
     def num_threads(self):
         return self.L.mo_num_threads()
 
+    def set_num_threads(self, n):
+        self.L.mo_set_num_threads(int(n))
+
     # MXFP8 (OCP Microscaling Formats: 32-element blocks, E8M0 scale, E4M3 codes).
     def e4m3_value(self, code):
         return self.L.mo_e4m3_value(int(code) & 0xFF)
@@ -194,6 +197,10 @@ def num_threads():
     return default().num_threads()
 
 
+def set_num_threads(n):
+    default().set_num_threads(n)
+
+
 def attend_backward(prob, q, k, v, dout, ids, rows=None):
     return default().attend_backward(prob, q, k, v, dout, ids, rows)
 
@@ -223,6 +230,8 @@ def load(path):
     for f in (L.mo_block_scores, L.mo_select, L.mo_attend, L.mo_invert, L.mo_attend_backward, L.mo_indexer_kl):
         f.restype = ctypes.c_int
     L.mo_num_threads.restype = ctypes.c_int
+    L.mo_set_num_threads.argtypes = [ctypes.c_int]
+    L.mo_set_num_threads.restype = None
     L.mo_e4m3_value.argtypes = [ctypes.c_uint8]
     L.mo_e4m3_value.restype = ctypes.c_double
     L.mo_e4m3_encode.argtypes = [ctypes.c_double]

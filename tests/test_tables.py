@@ -258,7 +258,9 @@ def _model_invert(prob, ids):
     """Model of the inversion kernels: per-tile counts, column and block scans,
     then a walk over each tile's queries in which the slots of one query (the
     lanes of one step) rank themselves among the lower slots naming the same
-    block, and the last of them advances that block's cursor."""
+    block, and the last of them advances that block's cursor.  (The kernel
+    takes a single-pass step for rows whose valid ids ascend strictly; there
+    every rank is 0 and every count 1, so the rule below covers it.)"""
     nb, K, Nq = O.nblk(prob), prob.topk, prob.n_q
     ntile = (Nq + TILE - 1) // TILE
     offsets = np.zeros((prob.batch, prob.h_kv, nb + 1), dtype=np.int64)
