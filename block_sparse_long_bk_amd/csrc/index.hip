@@ -12,11 +12,15 @@
 //  * k_index_tile -- prefill.  A workgroup owns 512 consecutive queries of one
 //    group (their index queries stay in VGPRs as the MFMA B operand) and sweeps
 //    the candidate key blocks in order.  Each 128 x d_idx key block is staged
-//    once in LDS (double buffered) and multiplied on the matrix cores as
-//    S^T = K_blk * Q^T, so each lane's accumulators hold one query's scores for
-//    16 keys and the max pool is an in-register max plus one lane swap.  The
-//    token scores never leave registers; the block score goes straight into the
-//    lane's running Top-k list, so the score matrix never reaches HBM.
+//    once in LDS (global -> LDS transfers three blocks ahead where rows are
+//    256 bytes, else through registers, double buffered) and multiplied on the
+//    matrix cores as S^T = K_blk * Q^T, so each lane's accumulators hold one
+//    query's scores for 16 keys and the max pool is an in-register max plus
+//    one lane swap.  The token scores never leave registers; the block score
+//    goes straight into the lane's running Top-k list, so the score matrix
+//    never reaches HBM.  The 32-key M-tiles of all blocks run as one pipeline
+//    (the products of the next M-tile are issued before the max-pool and
+//    Top-k insertion of the current one, across block boundaries too).
 //  * k_index_scan -- decode / few queries.  Streams idx_k block by block (each
 //    128-token block of all groups is one contiguous span), VALU dot products
 //    against the few index queries kept in LDS; writes block scores, which
@@ -39,7 +43,7 @@ struct TileArgs {
   int64_t q_offset;
 };
 
-constexpr int kTileWaves = 8;
+constexpr int kTileWaves = 8;  // waves per workgroup of the MFMA tile kernel
 
 // Global -> registers -> LDS staging of one 128-token key block (16-byte
 // chunks; CPR chunks per token row, row stride `rowb` bytes in HBM).
@@ -122,20 +126,29 @@ __device__ __forceinline__ void mx_lstore(const u32x4 (&stage)[LOADS], const uin
 // a wave writes 16 bytes at the wave's LDS base + 16 L), four blocks deep, no
 // staging registers.  Rows are unpadded; chunk c of row r sits at position
 // c ^ (r % 16), so the 16 rows read by a quarter-wave hit distinct banks.
-constexpr int kDmaBufs = 4;
 constexpr int kDmaRowBytes = 256;
+// Blocks in flight: four with eight waves (one workgroup per CU), two with four
+// waves (two workgroups per CU, 64 KB of LDS each).
+template <int WAVES> constexpr int dma_bufs() { return WAVES == 8 ? 4 : 2; }
 
-__device__ __forceinline__ void dma_issue_block(char* buf, const char* ikb, int j, int64_t rowb, int nk, int wave,
-                                                int lane) {
+// One wave's share of a key block's transfer: PER 1 KB slots of 4 rows each
+// (32 / WAVES slots per wave).  Tokens past n_k (a partial last block, only
+// when blocks are smaller than a chunk) re-read token n_k - 1.
+template <int WAVES>
+struct DmaLane {
+  static constexpr int PER = 32 / WAVES;
+  __device__ __forceinline__ void issue(char* buf, const char* ikb, int j, int64_t rowb, int nk, int wave,
+                                        int lane) const {
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int slot = wave * 4 + u;  // 1 KB slot = 4 rows
-    const int r = slot * 4 + lane / 16;
-    const int c = (lane & 15) ^ (r & 15);
-    const char* src = ikb + min((int64_t)j * kChunk + r, (int64_t)nk - 1) * rowb + c * 16;
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src), buf + slot * 1024, 16, 0, 0);
+    for (int u = 0; u < PER; ++u) {
+      const int slot = wave * PER + u;
+      const int r = slot * 4 + lane / 16;
+      const int c = (lane & 15) ^ (r & 15);
+      const char* src = ikb + min((int64_t)j * kChunk + r, (int64_t)nk - 1) * rowb + c * 16;
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src), buf + slot * 1024, 16, 0, 0);
+    }
   }
-}
+};
 
 // Fragment of 8 elements starting at element e (multiple of 8) of row r of a
 // swizzled 256-byte-row buffer.
@@ -151,9 +164,8 @@ __device__ __forceinline__ frag_t<T> dma_frag(const char* buf, int r, int e) {
   }
 }
 
-template <typename T, int DI, int NT, int KMAX, bool WRITE_S, bool TOPK, bool MX>
-__global__ void __launch_bounds__(kTileWaves * 64) k_index_tile(TileArgs a) {
-  constexpr int WAVES = kTileWaves;
+template <typename T, int DI, int NT, int KMAX, bool WRITE_S, bool TOPK, bool MX, int WAVES>
+__global__ void __launch_bounds__(WAVES * 64, 2) k_index_tile(TileArgs a) {
   constexpr int TQ = WAVES * NT * 32;  // queries per workgroup
   constexpr int ROW_BYTES = DI * (int)sizeof(T);
   constexpr int PITCH = ROW_BYTES + 16;  // padded LDS row: conflict-free 16-byte reads
@@ -162,15 +174,17 @@ __global__ void __launch_bounds__(kTileWaves * 64) k_index_tile(TileArgs a) {
   constexpr int CHUNKS = kChunk * CPR;
   constexpr int NTHR = WAVES * 64;
   constexpr int LOADS = (CHUNKS + NTHR - 1) / NTHR;
-  constexpr bool DMA = !MX && ROW_BYTES == kDmaRowBytes && WAVES == 8;  // 8 waves x 4 loads = one block
+  constexpr bool DMA = !MX && ROW_BYTES == kDmaRowBytes && (WAVES == 8 || WAVES == 4);  // 32 loads = one block
+  constexpr int DPW = 32 / WAVES;  // DMA loads per wave per block
   constexpr int MCPR = DI / 16;  // MXFP8: 16-byte code chunks per key row
   constexpr int MCHUNKS = kChunk * MCPR;
   constexpr int MLOADS = (MCHUNKS + NTHR - 1) / NTHR;
-  constexpr int NBUF = DMA ? kDmaBufs : 2;
+  constexpr int NBUF = DMA ? dma_bufs<WAVES>() : 2;
   constexpr int BUFB = DMA ? kChunk * kDmaRowBytes : kChunk * PITCH;
   __shared__ __attribute__((aligned(16))) char lds[NBUF][BUFB];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: slot arithmetic on the scalar unit
   const int g = blockIdx.x % a.Hkv;
   const int tile = a.n_tiles - 1 - (int)(blockIdx.x / a.Hkv);  // heaviest tiles first
   const int b = blockIdx.y;
@@ -205,7 +219,104 @@ __global__ void __launch_bounds__(kTileWaves * 64) k_index_tile(TileArgs a) {
   TopList<KMAX> list;
   list.init();
 
-  if (j_end > 0) {
+  if constexpr (DMA && KMAX <= 16) {
+    // The M-tiles of all key blocks as one pipeline (two accumulator sets,
+    // two fragment sets): the products of M-tile m + 1 are issued before the
+    // max-pool of m, and the fragments of m + 2 are read meanwhile -- across
+    // block boundaries too.  The barrier that makes block j + 1 visible sits
+    // in block j, after the products of its last M-tile are issued (every LDS
+    // read of block j has then been consumed, so block j + 4's transfer can
+    // reuse its buffer), and the block's last max-pool and Top-k insertion run
+    // while the first products of block j + 1 are on the matrix core.
+    if (j_end > 0) {
+      DmaLane<WAVES> dl;
+      const int64_t rowb = krow * (int64_t)sizeof(T);
+#pragma unroll
+      for (int sb = 0; sb < NBUF - 1; ++sb)
+        if (sb < j_end) dl.issue(lds[sb], ikb, sb, rowb, a.Nk, wave, lane);
+      // block j has landed and is visible; then block j + NBUF - 1 is issued
+      // into the buffer of block j - 1
+      auto gate = [&](int j) {
+        if (!WRITE_S && j + NBUF - 2 < j_end) wait_vmcnt<DPW * (NBUF - 2)>();
+        else wait_vmcnt<0>();
+        __syncthreads();
+        if (j + NBUF - 1 < j_end) dl.issue(lds[(j + NBUF - 1) % NBUF], ikb, j + NBUF - 1, rowb, a.Nk, wave, lane);
+      };
+      const int arow = lane & 31;
+      auto frag = [&](const char* buf, int mt, int ks) -> frag_t<T> {
+        return dma_frag<T>(buf, mt * 32 + arow, 16 * ks + 8 * half);
+      };
+      frag_t<T> A[2][KSTEPS];
+      f32x16 acc[2][NT];
+      auto products = [&](int set) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[set][nt] = mma0(A[set][0], bq[nt][0]);
+#pragma unroll
+        for (int ks = 1; ks < KSTEPS; ++ks)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) mma(A[set][ks], bq[nt][ks], acc[set][nt]);
+      };
+      gate(0);
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) A[0][ks] = frag(lds[0], 0, ks);
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) A[1][ks] = frag(lds[0], 1, ks);
+      products(0);
+      for (int j = 0; j < j_end; ++j) {
+        const char* bufc = lds[j % NBUF];
+        const char* bufn = lds[(j + 1) % NBUF];
+        const bool more = j + 1 < j_end;
+        float run[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) run[nt] = -__builtin_huge_valf();
+        const int bpm = a.bk / 32, bpc = kChunk / a.bk;
+        auto pool = [&](int set, int mt) {
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) run[nt] = max16(acc[set][nt], run[nt]);
+          if (((mt + 1) & (bpm - 1)) == 0) {
+            float own;
+            if (NT == 2) {
+              const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(run[0]), __float_as_uint(run[1]), false,
+                                                              false);
+              own = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+            } else {
+              own = pair32_max(run[0]);
+            }
+            const int jb = j * bpc + mt / bpm;
+            if (jb < L_own) {
+              if (TOPK) list.offer(own, jb);
+              if (WRITE_S) a.scores[(((int64_t)b * a.Hkv + g) * a.Nq + q_own) * a.nblk + jb] = own;
+            }
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) run[nt] = -__builtin_huge_valf();
+          }
+        };
+        // M-tile 0 of block j was issued in the previous round (or above).
+        products(1);
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) A[0][ks] = frag(bufc, 2, ks);
+        pool(0, 0);
+        products(0);
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) A[1][ks] = frag(bufc, 3, ks);
+        pool(1, 1);
+        products(1);
+        if (more) {
+          gate(j + 1);
+#pragma unroll
+          for (int ks = 0; ks < KSTEPS; ++ks) A[0][ks] = frag(bufn, 0, ks);
+        }
+        pool(0, 2);
+        if (more) {
+          products(0);
+#pragma unroll
+          for (int ks = 0; ks < KSTEPS; ++ks) A[1][ks] = frag(bufn, 1, ks);
+        }
+        pool(1, 3);
+      }
+    }
+  } else if (j_end > 0) {
+    DmaLane<WAVES> dl;
     u32x4 stage[LOADS];
     u32x4 mstage[MLOADS];
     uint32_t mscl[MLOADS];
@@ -216,7 +327,7 @@ __global__ void __launch_bounds__(kTileWaves * 64) k_index_tile(TileArgs a) {
     } else if constexpr (DMA) {
 #pragma unroll
       for (int sb = 0; sb < NBUF - 1; ++sb)
-        if (sb < j_end) dma_issue_block(lds[sb], ikb, sb, krow * (int64_t)sizeof(T), a.Nk, wave, lane);
+        if (sb < j_end) dl.issue(lds[sb], ikb, sb, krow * (int64_t)sizeof(T), a.Nk, wave, lane);
     } else {
       tile_gload<LOADS, CPR, CHUNKS, NTHR>(stage, ikb, 0, krow * (int64_t)sizeof(T), a.Nk, tid);
       tile_lstore<LOADS, CPR, CHUNKS, NTHR, PITCH>(stage, lds[0], tid);
@@ -227,11 +338,11 @@ __global__ void __launch_bounds__(kTileWaves * 64) k_index_tile(TileArgs a) {
       if constexpr (DMA) {
         // Block j has landed once at most the loads of the later blocks in
         // flight remain; then every wave's share is visible after the barrier.
-        if (!WRITE_S && j + NBUF - 2 < j_end) wait_vmcnt<4 * (NBUF - 2)>();
+        if (!WRITE_S && j + NBUF - 2 < j_end) wait_vmcnt<DPW * (NBUF - 2)>();
         else wait_vmcnt<0>();
         __syncthreads();
         if (j + NBUF - 1 < j_end)
-          dma_issue_block(lds[(j + NBUF - 1) % NBUF], ikb, j + NBUF - 1, krow * (int64_t)sizeof(T), a.Nk, wave, lane);
+          dl.issue(lds[(j + NBUF - 1) % NBUF], ikb, j + NBUF - 1, krow * (int64_t)sizeof(T), a.Nk, wave, lane);
       } else if constexpr (MX) {
         if (j + 1 < j_end) mx_gload<MLOADS, MCPR, MCHUNKS, NTHR, DI>(mstage, mscl, ikc, iks, j + 1, a.Hkv, a.Nk, tid);
       } else {
@@ -247,6 +358,35 @@ __global__ void __launch_bounds__(kTileWaves * 64) k_index_tile(TileArgs a) {
         if constexpr (DMA) return dma_frag<T>(bufc, mt * 32 + arow, 16 * ks + 8 * half);
         else return load8(reinterpret_cast<const T*>(bufc + (mt * 32 + arow) * PITCH) + 8 * half + 16 * ks);
       };
+      // Max-pool of M-tile mt (accumulator set mt & 1) and, after the last
+      // M-tile of a key block, the block score into the Top-k list.
+      auto pool = [&](const f32x16 (&accm)[NT], int mt) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) run[nt] = max16(accm[nt], run[nt]);
+        if (((mt + 1) & (bpm - 1)) == 0) {
+          // Last M-tile of a key block.  Each half of the wave saw half of the
+          // block's keys; swap halves so that lane l ends with the full block
+          // max of query q0 + wave*NT*32 + l.
+          float own;
+          if (NT == 2) {
+            // one v_permlane32_swap: lane l < 32 pairs run[0] of lanes l and
+            // l + 32, lane l >= 32 pairs run[1] of lanes l - 32 and l
+            const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(run[0]), __float_as_uint(run[1]), false,
+                                                            false);
+            own = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+          } else {
+            own = pair32_max(run[0]);
+          }
+          const int jb = j * bpc + mt / bpm;  // blocks arrive in increasing order
+          if (jb < L_own) {
+            if (TOPK) list.offer(own, jb);
+            if (WRITE_S) a.scores[(((int64_t)b * a.Hkv + g) * a.Nq + q_own) * a.nblk + jb] = own;
+          }
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) run[nt] = -__builtin_huge_valf();
+        }
+      };
+      {
       // Software pipeline over the four M-tiles: the products of M-tile mt+1
       // are issued before the max-pool of mt, so the VALU work of one tile
       // runs while the matrix core works on the next (two accumulator sets;
@@ -285,30 +425,8 @@ __global__ void __launch_bounds__(kTileWaves * 64) k_index_tile(TileArgs a) {
             for (int ks = 0; ks < KSTEPS; ++ks) A[(mt + 1) & 1][ks] = frag(mt + 1, ks);
           }
         }
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) run[nt] = max16(acc[mt & 1][nt], run[nt]);
-        if (((mt + 1) & (bpm - 1)) == 0) {
-          // Last M-tile of a key block.  Each half of the wave saw half of the
-          // block's keys; swap halves so that lane l ends with the full block
-          // max of query q0 + wave*NT*32 + l.
-          float own;
-          if (NT == 2) {
-            // one v_permlane32_swap: lane l < 32 pairs run[0] of lanes l and
-            // l + 32, lane l >= 32 pairs run[1] of lanes l - 32 and l
-            const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(run[0]), __float_as_uint(run[1]), false,
-                                                            false);
-            own = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-          } else {
-            own = pair32_max(run[0]);
-          }
-          const int jb = j * bpc + mt / bpm;  // blocks arrive in increasing order
-          if (jb < L_own) {
-            if (TOPK) list.offer(own, jb);
-            if (WRITE_S) a.scores[(((int64_t)b * a.Hkv + g) * a.Nq + q_own) * a.nblk + jb] = own;
-          }
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) run[nt] = -__builtin_huge_valf();
-        }
+        pool(acc[mt & 1], mt);
+      }
       }
       if constexpr (MX) {
         if (j + 1 < j_end) mx_lstore<T, MLOADS, MCPR, MCHUNKS, NTHR, PITCH>(mstage, mscl, lds[(j + 1) & 1], tid);
@@ -488,11 +606,11 @@ hipError_t tile_dispatch(const Shape& s, const TileArgs& a, dim3 grid, hipStream
   constexpr int NT = (DI * (int)sizeof(T) <= 256) ? 2 : 1;
   const int kneed = s.topk - 1;
   if (!TOPK || kneed <= 8) {
-    hipLaunchKernelGGL((k_index_tile<T, DI, NT, 8, WRITE_S, TOPK, MX>), grid, dim3(kTileWaves * 64), 0, st, a);
+    hipLaunchKernelGGL((k_index_tile<T, DI, NT, 8, WRITE_S, TOPK, MX, kTileWaves>), grid, dim3(kTileWaves * 64), 0, st, a);
   } else if (kneed <= 16) {
-    hipLaunchKernelGGL((k_index_tile<T, DI, NT, 16, WRITE_S, TOPK, MX>), grid, dim3(kTileWaves * 64), 0, st, a);
+    hipLaunchKernelGGL((k_index_tile<T, DI, NT, 16, WRITE_S, TOPK, MX, kTileWaves>), grid, dim3(kTileWaves * 64), 0, st, a);
   } else {
-    hipLaunchKernelGGL((k_index_tile<T, DI, NT, 32, WRITE_S, TOPK, MX>), grid, dim3(kTileWaves * 64), 0, st, a);
+    hipLaunchKernelGGL((k_index_tile<T, DI, NT, 32, WRITE_S, TOPK, MX, kTileWaves>), grid, dim3(kTileWaves * 64), 0, st, a);
   }
   return hipGetLastError();
 }
