@@ -78,16 +78,6 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
-// s_waitcnt lgkmcnt(N): at most N LDS / scalar-memory operations of this wave
-// outstanding (vmcnt and expcnt left at their maximum).  Scalar loads can
-// return out of order, so while one may be pending the compiler waits for
-// every LDS read at each use; a lgkmcnt(0) ahead of a loop that issues no
-// scalar loads lets it count the loop's LDS reads exactly.
-template <int N>
-__device__ __forceinline__ void wait_lgkmcnt() {
-  static_assert(N >= 0 && N < 16, "lgkmcnt range");
-  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (N << 8));
-}
 __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
 
 // Running max over 16 values as a chain of three-input maxima (v_max3_f32).
