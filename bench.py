@@ -270,11 +270,25 @@ def cpu_baseline(wl, xh, n_sample, n_sample_1t):
 
 # ---- legs --------------------------------------------------------------------
 
+def chunk_workspace_bytes(p, n_chunk):
+    """Workspace bytes that make the attention run in query chunks of (about)
+    n_chunk queries: the library takes the largest chunk that fits."""
+    from block_sparse_long_bk_amd import api
+    full, least = api.workspace_size(p, api.OP_FORWARD)
+    if n_chunk >= p.n_q:
+        return full
+    per_q = (full - least) / max(p.n_q - 256, 1)  # the least workspace holds a 256-query chunk
+    return int(least + per_q * (n_chunk - 256)) + (1 << 20)
+
+
 def run_forward(wl, args, sched="auto", cold=True):
     from block_sparse_long_bk_amd import api, inputs
     x = inputs.generate(wl, device="cuda")
     p = api.problem_of(wl, sched=sched)
-    ws = api.alloc_workspace(p, api.OP_FORWARD)
+    if getattr(args, "chunk_queries", 0):
+        ws = torch.empty(chunk_workspace_bytes(p, args.chunk_queries), dtype=torch.uint8, device="cuda")
+    else:
+        ws = api.alloc_workspace(p, api.OP_FORWARD)
     ids = torch.empty((wl.batch, wl.n_q, wl.h_kv, wl.topk), dtype=torch.int32, device="cuda")
     out = torch.empty_like(x["q"])
     lse = torch.empty((wl.batch, wl.n_q, wl.h_q), dtype=torch.float32, device="cuda")
@@ -620,6 +634,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-train", action="store_true", help="skip the backward and indexer-loss legs")
     ap.add_argument("--no-topk", action="store_true", help="skip the standalone Top-k timing")
+    ap.add_argument("--chunk-queries", type=int, default=0,
+                    help="give the forward only the workspace for attention chunks of about this many queries")
     ap.add_argument("--cpu-sample", type=int, default=256, help="oracle queries of the headline workload")
     ap.add_argument("--cpu-sample-1thread", type=int, default=3, help="of those, timed again on one thread")
     ap.add_argument("--crossover", action="store_true",
@@ -667,6 +683,7 @@ def main():
         "config": {"workload": wl.name, "batch": wl.batch, "n_q": wl.n_q, "n_k": wl.n_k, "q_offset": wl.q_offset,
                    "block_size": wl.block_size, "topk": wl.topk, "h_q": wl.h_q, "h_kv": wl.h_kv, "d": wl.d,
                    "d_idx": wl.d_idx, "sched": args.sched, "hot_frac": wl.hot_frac,
+                   "chunk_queries": args.chunk_queries or wl.n_q,
                    "caches": "cold (1 GiB scrub before each timed step)"},
         "roofline": roof,
         "warm": {"value": fs["effective_TFLOPs_warm"], "ms_per_step": r["ms_warm"]},
