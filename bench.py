@@ -17,7 +17,9 @@ steps back to back (warm) are reported beside it.
 
 Also on the line, never as ``value``:
   * ``roofline`` of the dominant kernel of the headline step against its
-    bound (the index tile: MFMA, with the method's flops);
+    bound (the index tile: MFMA, with the method's flops), with
+    ``frac_of_achievable`` against ``achievable_peaks``: what a 2 GiB device
+    copy and the library's bf16 8192^3 matmul reach on the same GPU;
   * ``selection_check``: the GPU's selection of sampled rows against the
     fp64 oracle (exact, tie-band and failing rows);
   * legs: prefill_32k and the skewed 128k prefill (with block-popularity
@@ -269,6 +271,38 @@ def cpu_baseline(wl, xh, n_sample, n_sample_1t):
 
 
 # ---- legs --------------------------------------------------------------------
+
+def achievable_peaks():
+    """What this GPU reaches on plain work, as a second reference beside the
+    published peaks: a 2 GiB device-to-device copy (read + write GB/s, like
+    the mixed traffic of the KV-outer pass) and a dense bf16 8192^3 matmul
+    from the installed library (TFLOP/s at whatever clock the chip holds
+    under it)."""
+    src = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    a = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
+    for _ in range(2):
+        dst.copy_(src)
+        torch.matmul(a, b)
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    e[0].record()
+    for _ in range(5):
+        dst.copy_(src)
+    e[1].record()
+    e[2].record()
+    for _ in range(10):
+        torch.matmul(a, b)
+    e[3].record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * src.numel() * 5 / e[0].elapsed_time(e[1]) / 1e6
+    mm_tflops = 2.0 * 8192 ** 3 * 10 / e[2].elapsed_time(e[3]) / 1e9
+    del src, dst, a, b
+    torch.cuda.empty_cache()
+    return {"copy_GBs": copy_gbs, "bf16_matmul_TFLOPs": mm_tflops,
+            "note": "2 GiB device copy (read + write) and torch.matmul bf16 8192^3 on this GPU"}
+
 
 def chunk_workspace_bytes(p, n_chunk):
     """Workspace bytes that make the attention run in query chunks of (about)
@@ -666,6 +700,9 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    # the probes stay out of profiled runs: their 2 GiB copy would pass for the
+    # calibration copy of a counter run
+    peaks = None if (args.no_legs or args.calib_copy_mib) else achievable_peaks()
     wl = inputs.WORKLOADS[args.workload]
     r = run_forward(wl, args, sched=args.sched)
     fs = forward_summary(r)
@@ -676,6 +713,9 @@ def main():
     if roof is None:
         roof = {"bound": None, "kernel": dom, "achieved": None, "peak": None, "unit": None, "frac": None,
                 "traffic": None}
+    elif roof.get("achieved") is not None and peaks is not None:
+        ref = peaks["bf16_matmul_TFLOPs"] if roof["bound"] == "mfma" else peaks["copy_GBs"]
+        roof["frac_of_achievable"] = roof["achieved"] / ref
     line = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": r["ms"], "higher_is_better": True, "scaling": "weak",
@@ -686,6 +726,7 @@ def main():
                    "chunk_queries": args.chunk_queries or wl.n_q,
                    "caches": "cold (1 GiB scrub before each timed step)"},
         "roofline": roof,
+        "achievable_peaks": peaks,
         "warm": {"value": fs["effective_TFLOPs_warm"], "ms_per_step": r["ms_warm"]},
         "headline": fs,
     }
