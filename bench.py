@@ -32,6 +32,7 @@ on the launch stream.
 """
 import argparse
 import csv
+import gc
 import glob
 import hashlib
 import json
@@ -268,6 +269,143 @@ def cpu_baseline(wl, xh, n_sample, n_sample_1t):
              "value_1thread": fl1 / dt1 / 1e12, "seconds_1thread": dt1,
              "sample_1thread": f"{len(qi1)} of those queries on one thread"},
             qi, ids, s)
+
+
+# Oracle coverage per workload for the full protocol run (--cpu-protocol):
+# "all" = every query; a number = that many sampled queries.
+PROTOCOL = (("tiny_f32_4k", "all", 4096), ("prefill_32k", "all", 2048), ("skewed_prefill_128k", 1024, 256),
+            ("decode_16x1m", "all", 1), ("chunk_16k_at_1m", 256, 64))
+
+
+def protocol_queries(wl, cover):
+    """Every query, or a stratified sample: for the skewed prefill a quarter
+    in the first 16 blocks, a quarter in the last 16 and the rest evenly
+    spaced with the block boundaries; otherwise sample_queries."""
+    if cover == "all":
+        return np.arange(wl.n_q, dtype=np.int64)
+    if wl.hot_frac > 0 and wl.q_offset == 0:
+        head = min(16 * wl.block_size, wl.n_q)
+        qs = set(np.linspace(0, head - 1, cover // 4).astype(int).tolist())
+        qs |= set(np.linspace(wl.n_q - head, wl.n_q - 1, cover // 4).astype(int).tolist())
+        qs |= set(sample_queries(wl, cover - len(qs)).tolist())
+        return np.array(sorted(qs), dtype=np.int64)
+    return sample_queries(wl, cover)
+
+
+def _host_info():
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    aff = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return {"cpu_model": model, "cpu_count": os.cpu_count(), "affinity": aff}
+
+
+def cpu_baseline_protocol(args):
+    """The oracle timed per stage (index scores + selection, then attention)
+    with the query coverage of the measurement protocol, and every covered
+    GPU row of msa_forward checked against it: selection row by row, then the
+    attention output, lse and per-row rel-L2 (from the oracle's selection
+    where a row lies in the tie band)."""
+    from oracle import oracle as O
+    from tests.parity import TOL, check_selection
+    from block_sparse_long_bk_amd import api, inputs
+    info = dict(_host_info(), threads=O.num_threads())
+    print(f"[protocol] host {info}", flush=True)
+    res = {"host": info, "workloads": {}}
+    for name, cover, chunk in PROTOCOL:
+        wl = inputs.WORKLOADS[name]
+        x = inputs.generate(wl, device="cuda")
+        p = api.problem_of(wl, sched="auto")
+        ids, out, lse = api.forward(p, x["q"], x["k"], x["v"], x["iq"], x["ik"])
+        torch.cuda.synchronize()
+        prob = O.problem_of(wl.with_(batch=1))
+        tol = TOL[wl.dtype]
+        st = dict(rows=0, exact=0, tie=0, fail=0, t_select=0.0, t_attend=0.0, flops=0.0, queries=0,
+                  max_abs=0.0, d2=0.0, r2=0.0, worst_row=0.0, lse_abs=0.0, lse_pattern_ok=True)
+        qi_all = protocol_queries(wl, cover)
+        for b in range(wl.batch):
+            xh = {k: v[b:b + 1].cpu() for k, v in x.items()}
+            ids_b, out_b, lse_b = ids[b].cpu(), out[b].cpu(), lse[b].cpu()
+            for c0 in range(0, len(qi_all), chunk):
+                qi = qi_all[c0:c0 + chunk]
+                rows = np.stack([np.zeros_like(qi), qi], axis=1)
+                t0 = time.perf_counter()
+                s_o = O.block_scores(prob, xh["iq"], xh["ik"], rows)
+                ids_o = O.select(prob, s_o, rows)
+                t1 = time.perf_counter()
+                o_o, l_o = O.attend(prob, xh["q"], xh["k"], xh["v"], ids_o, rows)
+                t2 = time.perf_counter()
+                st["t_select"] += t1 - t0
+                st["t_attend"] += t2 - t1
+                st["queries"] += len(qi)
+                got = ids_b[torch.from_numpy(qi)].numpy()
+                sel = check_selection(wl.with_(batch=1), got, ids_o, s_o, rows=rows)
+                for k in ("exact", "tie", "fail"):
+                    st[k] += sel[k]
+                st["rows"] += len(qi) * wl.h_kv
+                pos = torch.from_numpy(wl.q_offset + qi).view(-1, 1, 1)
+                j = torch.from_numpy(ids_o).to(torch.int64)
+                n = torch.minimum(pos - j * wl.block_size + 1, torch.full_like(j, wl.block_size))
+                n = torch.where(j >= 0, n.clamp(min=0), torch.zeros_like(n))
+                st["flops"] += 4.0 * wl.d * (wl.h_q // wl.h_kv) * float(n.sum())
+                o_g = out_b[torch.from_numpy(qi)].to(torch.float64).numpy()
+                l_g = lse_b[torch.from_numpy(qi)].to(torch.float64).numpy()
+                if not np.array_equal(got, ids_o):
+                    # tie-band rows: the attention of the oracle's selection
+                    tbl = ids[b:b + 1].clone()
+                    tbl[0, torch.from_numpy(qi).cuda()] = torch.from_numpy(ids_o).cuda()
+                    o2, l2 = api.sparse_attention(api.problem_of(wl.with_(batch=1), sched="auto"),
+                                                  x["q"][b:b + 1], x["k"][b:b + 1], x["v"][b:b + 1], tbl)
+                    o_g = o2[0, torch.from_numpy(qi).cuda()].cpu().to(torch.float64).numpy()
+                    l_g = l2[0, torch.from_numpy(qi).cuda()].cpu().to(torch.float64).numpy()
+                diff = o_g - o_o
+                st["max_abs"] = max(st["max_abs"], float(np.max(np.abs(diff))))
+                st["d2"] += float(np.sum(diff * diff))
+                st["r2"] += float(np.sum(o_o * o_o))
+                a2 = o_g.reshape(-1, wl.d)
+                b2 = o_o.reshape(-1, wl.d)
+                nb = np.linalg.norm(b2, axis=1)
+                nd = np.linalg.norm(a2 - b2, axis=1)
+                rel = np.where(nb > 0, nd / np.where(nb > 0, nb, 1.0), np.where(nd == 0, 0.0, np.inf))
+                st["worst_row"] = max(st["worst_row"], float(rel.max()))
+                fin = np.isfinite(l_o)
+                st["lse_pattern_ok"] &= bool(np.array_equal(np.isneginf(l_g), np.isneginf(l_o))
+                                             and np.all(np.isfinite(l_g[fin])))
+                if fin.any():
+                    st["lse_abs"] = max(st["lse_abs"], float(np.max(np.abs(l_g[fin] - l_o[fin]))))
+                print(f"[protocol] {name} b={b} queries {c0}..{c0 + len(qi) - 1}: select {t1 - t0:.1f} s, "
+                      f"attend {t2 - t1:.1f} s, selection {sel['exact']}/{len(qi) * wl.h_kv} exact "
+                      f"{sel['tie']} tie {sel['fail']} fail", flush=True)
+            del xh
+        rl2 = (st["d2"] / st["r2"]) ** 0.5 if st["r2"] > 0 else 0.0
+        per_q = (st["t_select"] + st["t_attend"]) / st["queries"]
+        total_q = wl.n_q * wl.batch
+        res["workloads"][name] = {
+            "coverage": (f"every query ({total_q})" if cover == "all"
+                         else f"{len(qi_all)} of {wl.n_q} queries, stratified"),
+            "queries": st["queries"], "seconds_select": st["t_select"], "seconds_attend": st["t_attend"],
+            "oracle_TFLOPs": st["flops"] / (st["t_select"] + st["t_attend"]) / 1e12,
+            "full_config_s": per_q * total_q, "full_config_s_is": "measured" if cover == "all" else "extrapolated",
+            "selection": {"rows": st["rows"], "exact": st["exact"], "tie_band": st["tie"], "fail": st["fail"]},
+            "attention": {"max_abs": st["max_abs"], "rel_l2": rl2, "worst_row_rel_l2": st["worst_row"],
+                          "lse_max_abs": st["lse_abs"], "lse_neg_inf_pattern": st["lse_pattern_ok"],
+                          "within_tolerance": bool(st["fail"] == 0 and st["max_abs"] <= tol["max_abs"]
+                                                   and rl2 <= tol["rel_l2"]
+                                                   and st["worst_row"] <= tol["row_rel_l2"]
+                                                   and st["lse_abs"] <= tol["lse_abs"] and st["lse_pattern_ok"]),
+                          "tolerance": tol},
+        }
+        print(f"[protocol] {name}: {json.dumps(res['workloads'][name])}", flush=True)
+        del x, ids, out, lse
+        gc.collect()
+        torch.cuda.empty_cache()
+    return res
 
 
 # ---- legs --------------------------------------------------------------------
@@ -672,6 +810,9 @@ def main():
                     help="give the forward only the workspace for attention chunks of about this many queries")
     ap.add_argument("--cpu-sample", type=int, default=256, help="oracle queries of the headline workload")
     ap.add_argument("--cpu-sample-1thread", type=int, default=3, help="of those, timed again on one thread")
+    ap.add_argument("--cpu-protocol", action="store_true",
+                    help="only the oracle with the protocol's coverage per workload (every query of the tiny "
+                         "and 32K prefills, all decode sequences), timed per stage, every covered row checked")
     ap.add_argument("--crossover", action="store_true",
                     help="also time both attention schedules on query chunks at the end of a 1M-token cache")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -694,6 +835,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     from block_sparse_long_bk_amd import inputs
 
+    if args.cpu_protocol:
+        print(json.dumps({"cpu_baseline_protocol": cpu_baseline_protocol(args)}), flush=True)
+        return
     if args.calib_copy_mib:
         src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
