@@ -23,6 +23,8 @@
 // out as one partial per (row, slot), summed in slot order (k_bwd_dq_sum); dk
 // and dv as fp32 partials per item, summed per block in item order
 // (k_bwd_dkdv_reduce).  No atomics.
+#include <type_traits>
+
 #include "attn_common.h"
 
 namespace msa {
@@ -270,23 +272,32 @@ __global__ void __launch_bounds__(256, 1) k_bwd_fused(BwdArgs a) {
         mma(load8(qr + 16 * ks), kf[ks], s);
         mma(load8(dr + 16 * ks), vf[ks], dp);
       }
-      // P and dS in place; accumulator position e is tile row 8(e/4) + 4h + e%4
+      // P and dS in place; accumulator position e is tile row 8(e/4) + 4h + e%4.
+      // The mask is applied only when some row of the tile sits before one of
+      // this wave's keys (its local block, or a row past the item's end).
+      auto p_ds = [&](auto masked) {
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int r0 = 8 * q4 + 4 * half;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(row_lse2 + r0);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(row_d + r0);
-        const int4 p4 = *reinterpret_cast<const int4*>(row_pos + r0);
-        const int pp[4] = {p4.x, p4.y, p4.z, p4.w};
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int r0 = 8 * q4 + 4 * half;
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(row_lse2 + r0);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(row_d + r0);
+          int4 p4{};
+          if constexpr (decltype(masked)::value) p4 = *reinterpret_cast<const int4*>(row_pos + r0);
+          const int pp[4] = {p4.x, p4.y, p4.z, p4.w};
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int e = 4 * q4 + c;
-          const float p = my_key <= pp[c] ? exp2_fast(fmaf(s[e], a.c_log2, -l4[c])) : 0.f;
-          s[e] = p;
-          dp[e] = p * (dp[e] - d4[c]);
-          *reinterpret_cast<T*>(lds + X::DS_OFF + (r0 + c) * X::SPITCH + kk * (int)sizeof(T)) = from_f32<T>(dp[e]);
+          for (int c = 0; c < 4; ++c) {
+            const int e = 4 * q4 + c;
+            const float x = exp2_fast(fmaf(s[e], a.c_log2, -l4[c]));
+            float p = x;
+            if constexpr (decltype(masked)::value) p = my_key <= pp[c] ? x : 0.f;
+            s[e] = p;
+            dp[e] = p * (dp[e] - d4[c]);
+            *reinterpret_cast<T*>(lds + X::DS_OFF + (r0 + c) * X::SPITCH + kk * (int)sizeof(T)) = from_f32<T>(dp[e]);
+          }
         }
-      }
+      };
+      if (__any((int64_t)my_pos < key0 + kg * 32 + 31)) p_ds(std::true_type{});
+      else p_ds(std::false_type{});
       // dV += P^T dO, dK += dS^T Q
 #pragma unroll
       for (int aa = 0; aa < 2; ++aa) {
@@ -447,21 +458,30 @@ __global__ void __launch_bounds__(512, 1) k_bwd_split(BwdArgs a) {
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) mma(load8(xr + 16 * ks), kv[ks], xs);
       if (role == 0) {
-        // P in place; accumulator position e is tile row 8(e/4) + 4h + e%4
+        // P in place; accumulator position e is tile row 8(e/4) + 4h + e%4.
+        // The mask is applied only when some row of the tile sits before one
+        // of this wave's keys (its local block, or a row past the item's end).
+        auto p_of = [&](auto masked) {
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int r0 = 8 * q4 + 4 * half;
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(row_lse2 + r0);
-          const int4 p4 = *reinterpret_cast<const int4*>(row_pos + r0);
-          const int pp[4] = {p4.x, p4.y, p4.z, p4.w};
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int r0 = 8 * q4 + 4 * half;
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(row_lse2 + r0);
+            int4 p4{};
+            if constexpr (decltype(masked)::value) p4 = *reinterpret_cast<const int4*>(row_pos + r0);
+            const int pp[4] = {p4.x, p4.y, p4.z, p4.w};
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const int e = 4 * q4 + c;
-            const float p = my_key <= pp[c] ? exp2_fast(fmaf(xs[e], a.c_log2, -l4[c])) : 0.f;
-            xs[e] = p;
-            pex[kg][e][lane] = p;
+            for (int c = 0; c < 4; ++c) {
+              const int e = 4 * q4 + c;
+              const float x = exp2_fast(fmaf(xs[e], a.c_log2, -l4[c]));
+              float p = x;
+              if constexpr (decltype(masked)::value) p = my_key <= pp[c] ? x : 0.f;
+              xs[e] = p;
+              pex[kg][e][lane] = p;
+            }
           }
-        }
+        };
+        if (__any((int64_t)my_pos < key0 + kg * 32 + 31)) p_of(std::true_type{});
+        else p_of(std::false_type{});
       }
     }
     __syncthreads();  // P of every key group is in LDS

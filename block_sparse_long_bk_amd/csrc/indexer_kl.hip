@@ -624,7 +624,10 @@ __global__ void __launch_bounds__(512, 1) k_kl_main8(KlArgs a) {
       pf.qls[u] = a.lse[qrow];
     }
   };
-  auto heads = [&](int hn, f32x16& pm) {
+  // masked: some row of the tile sits before one of this wave's keys (its
+  // local block, or a row past the item's end); otherwise every product is
+  // visible and the mask is skipped (the same sums, bit for bit).
+  auto heads = [&](int hn, f32x16& pm, bool masked) {
     for (int hl = hs; hl < hn; hl += 2) {
       // the key fragments are read anew for each head: kept from one head to
       // the next they would hold 32 registers through the whole tile
@@ -635,17 +638,26 @@ __global__ void __launch_bounds__(512, 1) k_kl_main8(KlArgs a) {
       for (int ks = 1; ks < D / 16; ++ks) mma(load8(qr + 16 * ks), load8(krow + 16 * ks), s);
       // masked positions: the exponent is clamped at 0 (visible ones never
       // exceed it) so that the product with the 0/1 mask stays finite
+      if (masked) {
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int r0 = 8 * q4 + 4 * half;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&row_lsm[hl][r0]);
-        const int4 p4 = *reinterpret_cast<const int4*>(row_pos + r0);
-        const int pp[4] = {p4.x, p4.y, p4.z, p4.w};
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int r0 = 8 * q4 + 4 * half;
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&row_lsm[hl][r0]);
+          const int4 p4 = *reinterpret_cast<const int4*>(row_pos + r0);
+          const int pp[4] = {p4.x, p4.y, p4.z, p4.w};
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int e = 4 * q4 + c;
-          const float m = my_key <= pp[c] ? 1.f : 0.f;
-          pm[e] = fmaf(m, exp2_fast(fminf(fmaf(s[e], a.c_log2, -l4[c]), 0.f)), pm[e]);
+          for (int c = 0; c < 4; ++c) {
+            const int e = 4 * q4 + c;
+            const float m = my_key <= pp[c] ? 1.f : 0.f;
+            pm[e] = fmaf(m, exp2_fast(fminf(fmaf(s[e], a.c_log2, -l4[c]), 0.f)), pm[e]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&row_lsm[hl][8 * q4 + 4 * half]);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) pm[4 * q4 + c] += exp2_fast(fminf(fmaf(s[4 * q4 + c], a.c_log2, -l4[c]), 0.f));
         }
       }
     }
@@ -700,8 +712,9 @@ __global__ void __launch_bounds__(512, 1) k_kl_main8(KlArgs a) {
     }
     __syncthreads();
     fetch(tile + 1);  // past the last tile: entry 0's rows, never stored
+    const bool masked = __any((int64_t)row_pos[lane & 31] < key0 + kg * 32 + 31);
     f32x16 pm = f32x16{};
-    if (has_keys) heads(hn0, pm);
+    if (has_keys) heads(hn0, pm, masked);
     // further head chunks (groups of more than HC heads), fetched here
     for (int h0 = HC; h0 < a.G; h0 += HC) {
       const int hn = min(HC, a.G - h0);
@@ -730,7 +743,7 @@ __global__ void __launch_bounds__(512, 1) k_kl_main8(KlArgs a) {
         }
       }
       __syncthreads();
-      if (has_keys) heads(hn, pm);
+      if (has_keys) heads(hn, pm, masked);
     }
     __syncthreads();  // every wave is past the heads: the query-row area is free
     if (has_keys && hs == 1) {
