@@ -113,6 +113,15 @@ def _scrub_buffer():
     return torch.empty(SCRUB_BYTES, dtype=torch.uint8, device="cuda")
 
 
+_LAST_STEP_MS = []  # per-step times of the last cold (scrubbed) timing
+
+
+def step_spread(per):
+    """min / median / max of per-step times (ms)."""
+    return {"min": float(np.min(per)), "median": float(np.median(per)), "max": float(np.max(per)),
+            "steps": len(per)} if per else None
+
+
 def time_steps(fn, steps, warmup, scrub=None):
     """Warm-up, then exactly `steps` timed calls of fn between two device
     synchronisations.  With `scrub`, each call is preceded by a 1 GiB write
@@ -148,7 +157,9 @@ def time_steps(fn, steps, warmup, scrub=None):
     if scrub is None:
         ms = ev[0][0].elapsed_time(ev[-1][1]) / steps
     else:
-        ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        per = [a.elapsed_time(b) for a, b in ev]
+        _LAST_STEP_MS[:] = per
+        ms = float(np.mean(per))
     kern = {k: (t / n, n / steps) for k, (t, n) in api.profile_read().items() if n}
     return ms, wall * 1e3 / steps, kern
 
@@ -476,6 +487,7 @@ def run_forward(wl, args, sched="auto", cold=True):
     if cold:
         scrub = _scrub_buffer()
         r["ms"], r["wall_ms"], r["kern"] = time_steps(step, args.steps, args.warmup, scrub=scrub)
+        r["cold_steps"] = step_spread(_LAST_STEP_MS)
         del scrub
     r["ms_warm"], _, r["kern_warm"] = time_steps(step, args.steps, 1)
     if not cold:
@@ -500,6 +512,8 @@ def forward_summary(r):
            "kernels_ms": kernels_ms(kern), "kernels_ms_warm": kernels_ms(r["kern_warm"]),
            "kernel_launches_per_step": {k: v[1] for k, v in kern.items()},
            "method_bytes_attention": r["mbytes"], "workspace_bytes": r["ws_bytes"]}
+    if r.get("cold_steps"):
+        out["cold_step_ms"] = r["cold_steps"]
     it = [k for k in kern if k.startswith("index_tile")]
     if it:
         out["index_tile"] = roofline(it[0], kern[it[0]][0], flops=r["fl_idx"], peak_tflops=peak, workload=wl.name)
@@ -614,6 +628,7 @@ def run_decode(args, idx_format="plain", kv_format="plain"):
     steps = max(3, args.steps)
     scrub = _scrub_buffer()
     ms, _, kern = time_steps(step, steps, args.warmup, scrub=scrub)
+    spread = step_spread(_LAST_STEP_MS)
     del scrub
     ms_w, _, _ = time_steps(step, steps, 1)
     # algorithmic bytes: idx_k of every candidate block, the selected K/V
@@ -630,7 +645,7 @@ def run_decode(args, idx_format="plain", kv_format="plain"):
            "us_per_token": ms * 1e3 / (wl.batch * wl.n_q), "ms_per_step": ms,
            "us_per_token_warm": ms_w * 1e3 / (wl.batch * wl.n_q), "algorithmic_bytes": total,
            "hbm_GBs": total / ms / 1e6, "hbm_frac": total / ms / 1e6 / PEAK_HBM_GBS,
-           "kernels_ms": kernels_ms(kern)}
+           "kernels_ms": kernels_ms(kern), "cold_step_ms": spread}
     if "index_scan" in kern:
         res["index_scan"] = roofline("index_scan", kern["index_scan"][0], nbytes=b_idx, workload=wl.name)
     del x, ws, ik
@@ -797,7 +812,7 @@ def summarize_stats(d):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--sched", default="auto", choices=["auto", "kv_outer", "q_outer"])
