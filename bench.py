@@ -19,7 +19,8 @@ Also on the line, never as ``value``:
   * ``roofline`` of the dominant kernel of the headline step against its
     bound (the index tile: MFMA, with the method's flops), with
     ``frac_of_achievable`` against ``achievable_peaks``: what a 2 GiB device
-    copy and the library's bf16 8192^3 matmul reach on the same GPU;
+    copy, a 2 GiB fill and the library's bf16 8192^3 matmul reach on the
+    same GPU;
   * ``selection_check``: the GPU's selection of sampled rows against the
     fp64 oracle (exact, tie-band and failing rows);
   * legs: prefill_32k and the skewed 128k prefill (with block-popularity
@@ -435,7 +436,7 @@ def achievable_peaks():
         dst.copy_(src)
         torch.matmul(a, b)
     torch.cuda.synchronize()
-    e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
     e[0].record()
     for _ in range(5):
         dst.copy_(src)
@@ -444,13 +445,19 @@ def achievable_peaks():
     for _ in range(10):
         torch.matmul(a, b)
     e[3].record()
+    e[4].record()
+    for _ in range(5):
+        dst.fill_(1)
+    e[5].record()
     torch.cuda.synchronize()
     copy_gbs = 2 * src.numel() * 5 / e[0].elapsed_time(e[1]) / 1e6
     mm_tflops = 2.0 * 8192 ** 3 * 10 / e[2].elapsed_time(e[3]) / 1e9
+    write_gbs = dst.numel() * 5 / e[4].elapsed_time(e[5]) / 1e6
     del src, dst, a, b
     torch.cuda.empty_cache()
-    return {"copy_GBs": copy_gbs, "bf16_matmul_TFLOPs": mm_tflops,
-            "note": "2 GiB device copy (read + write) and torch.matmul bf16 8192^3 on this GPU"}
+    return {"copy_GBs": copy_gbs, "write_GBs": write_gbs, "bf16_matmul_TFLOPs": mm_tflops,
+            "note": "2 GiB device copy (read + write), 2 GiB fill (write only) and torch.matmul bf16 8192^3 on "
+                    "this GPU"}
 
 
 def chunk_workspace_bytes(p, n_chunk):
