@@ -814,6 +814,65 @@ def summarize_stats(d):
               f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['TotalDurationNs']) / 1e6:.2f} |")
 
 
+def summarize_sq(dir_a, dir_b):
+    """Per-kernel SQ figures from two rocprofv3 --pmc passes over the same
+    command: pass A with SQ_WAVE_CYCLES, SQ_VALU_MFMA_BUSY_CYCLES,
+    SQ_WAIT_INST_ANY, SQ_INSTS_MFMA, SQ_INSTS_VALU, GRBM_GUI_ACTIVE; pass B
+    with SQ_WAIT_INST_LDS, SQ_ACTIVE_INST_LDS, SQ_LDS_BANK_CONFLICT.  Counters
+    are chip totals per dispatch; the k-th dispatch of a kernel in pass B is
+    matched with its k-th dispatch in pass A.  Per dispatch: clock =
+    GRBM_GUI_ACTIVE / 8 XCDs / dispatch time; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES
+    / (1024 SIMDs x GRBM_GUI_ACTIVE / 8); VALU per MFMA = (SQ_INSTS_VALU -
+    SQ_INSTS_MFMA) / SQ_INSTS_MFMA; waits as fractions of SQ_WAVE_CYCLES; LDS
+    conflicts = SQ_LDS_BANK_CONFLICT / SQ_ACTIVE_INST_LDS.  Prints min-max over
+    the dispatches of each library kernel."""
+    def dispatches(d):
+        per = {}
+        for r in _pmc_rows(d):
+            key = r.get("Dispatch_Id") or r.get("Correlation_Id")
+            e = per.setdefault(key, {"name": _short(r["Kernel_Name"]), "c": {},
+                                     "ns": float(r["End_Timestamp"]) - float(r["Start_Timestamp"])})
+            e["c"][r["Counter_Name"]] = e["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        out = {}
+        for key in sorted(per, key=lambda k: int(k)):
+            e = per[key]
+            if e["name"].startswith("k_"):
+                out.setdefault(e["name"], []).append(e)
+        return out
+    A, B = dispatches(dir_a), dispatches(dir_b)
+
+    def rng(v, fmt):
+        v = [x for x in v if x is not None and math.isfinite(x)]
+        if not v:
+            return "–"
+        lo, hi = min(v), max(v)
+        return fmt.format(lo) if fmt.format(lo) == fmt.format(hi) else fmt.format(lo) + "–" + fmt.format(hi)
+    print("| kernel | dispatches | dispatch ms | clock GHz | MFMA busy | VALU / MFMA | wait on a dependency | "
+          "wait on LDS | LDS bank conflicts |")
+    print("|---|---:|---:|---:|---:|---:|---:|---:|---:|")
+    for name, da in sorted(A.items(), key=lambda kv: -sum(e["ns"] for e in kv[1])):
+        db = B.get(name, [])
+        ms, clk, busy, vpm, wdep, wlds, conf = [], [], [], [], [], [], []
+        for i, e in enumerate(da):
+            c = e["c"]
+            act = c.get("GRBM_GUI_ACTIVE", 0.0) / 8
+            ms.append(e["ns"] / 1e6)
+            # (the GRBM window also covers the dispatch itself: no clock for short ones)
+            clk.append(act / e["ns"] if e["ns"] > 1e5 and act else None)
+            busy.append(c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (1024 * act) if act else None)
+            nm = c.get("SQ_INSTS_MFMA", 0.0)
+            vpm.append((c.get("SQ_INSTS_VALU", 0.0) - nm) / nm if nm else None)
+            wc = c.get("SQ_WAVE_CYCLES", 0.0)
+            wdep.append(c.get("SQ_WAIT_INST_ANY", 0.0) / wc if wc else None)
+            if i < len(db):
+                cb = db[i]["c"]
+                wlds.append(cb.get("SQ_WAIT_INST_LDS", 0.0) / wc if wc else None)
+                al = cb.get("SQ_ACTIVE_INST_LDS", 0.0)
+                conf.append(cb.get("SQ_LDS_BANK_CONFLICT", 0.0) / al if al else None)
+        print(f"| {name} | {len(da)} | {rng(ms, '{:.3f}')} | {rng(clk, '{:.2f}')} | {rng(busy, '{:.3f}')} | "
+              f"{rng(vpm, '{:.1f}')} | {rng(wdep, '{:.2f}')} | {rng(wlds, '{:.3f}')} | {rng(conf, '{:.2f}')} |")
+
+
 # ---- main --------------------------------------------------------------------
 
 def main():
@@ -843,12 +902,18 @@ def main():
     ap.add_argument("--pmc-kernel", default="index_tile_topk")
     ap.add_argument("--pmc-workload", default=HEADLINE)
     ap.add_argument("--summarize-stats", metavar="STATS_DIR")
+    ap.add_argument("--summarize-sq", nargs=2, metavar=("PASS_A_DIR", "PASS_B_DIR"))
+    ap.add_argument("--legs", default="prefill_32k,skewed_prefill_128k",
+                    help="comma-separated prefill legs (the backward and indexer loss run with prefill_32k)")
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc, args.pmc_kernel, args.pmc_workload)
         return
     if args.summarize_stats:
         summarize_stats(args.summarize_stats)
+        return
+    if args.summarize_sq:
+        summarize_sq(*args.summarize_sq)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this MSA forward path is built and measured on a single GPU "
@@ -905,7 +970,7 @@ def main():
     del r
     torch.cuda.empty_cache()
     if not args.no_legs:
-        for name in ("prefill_32k", "skewed_prefill_128k"):
+        for name in [n for n in args.legs.split(",") if n]:
             rl = run_forward(inputs.WORKLOADS[name], args, sched=args.sched)
             leg = forward_summary(rl)
             leg["skew"] = skew_figures(rl["wl"], rl["ids"], rl["kern"])
@@ -920,7 +985,8 @@ def main():
                 line.update(run_training(args, rl))
             del rl
             torch.cuda.empty_cache()
-        a, b = line["prefill_32k"]["skew"], line["skewed_prefill_128k"]["skew"]
+        a = line.get("prefill_32k", {}).get("skew", {})
+        b = line.get("skewed_prefill_128k", {}).get("skew", {})
         if "kvouter_ns_per_1k_query_head_keys" in a and "kvouter_ns_per_1k_query_head_keys" in b:
             line["skewed_prefill_128k"]["kvouter_time_per_key_vs_prefill_32k"] = (
                 b["kvouter_ns_per_1k_query_head_keys"] / a["kvouter_ns_per_1k_query_head_keys"])
