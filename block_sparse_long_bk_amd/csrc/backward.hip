@@ -578,20 +578,38 @@ __global__ void __launch_bounds__(256) k_bwd_dq_sum(const T* __restrict__ part, 
   float acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-  // Eight slots per round, all their loads issued before any is used (a
+  // Sixteen slots per round, all their loads issued before any is used (a
   // slot past topk re-reads the last one, an unselected slot is read and not
-  // added); the sum runs in slot order.
-  for (int s0 = 0; s0 < topk; s0 += 8) {
-    frag_t<T> x[8];
-    bool ok[8];
+  // added); the sum runs in slot order.  Partials are read exactly once, so
+  // the loads are non-temporal.
+  // The slot ids are read four per load where a row of them is 16-byte
+  // aligned (topk a multiple of 4).
+  constexpr int RND = 16;
+  for (int s0 = 0; s0 < topk; s0 += RND) {
+    int idv[RND];
+    if ((topk & 3) == 0) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+      for (int q = 0; q < RND / 4; ++q) {
+        const int4 t = s0 + 4 * q < topk ? *reinterpret_cast<const int4*>(sel + s0 + 4 * q) : int4{-1, -1, -1, -1};
+        idv[4 * q] = t.x;
+        idv[4 * q + 1] = t.y;
+        idv[4 * q + 2] = t.z;
+        idv[4 * q + 3] = t.w;
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < RND; ++u) idv[u] = s0 + u < topk ? sel[s0 + u] : -1;
+    }
+    frag_t<T> x[RND];
+    bool ok[RND];
+#pragma unroll
+    for (int u = 0; u < RND; ++u) {
       const int sl = min(s0 + u, topk - 1);
-      ok[u] = s0 + u < topk && (unsigned)sel[sl] < (unsigned)nblk;  // ids outside [0, nblk) have no partial
-      x[u] = load8(p + (int64_t)sl * D);
+      ok[u] = (unsigned)idv[u] < (unsigned)nblk;  // slots past topk and ids outside [0, nblk) have no partial
+      x[u] = __builtin_nontemporal_load(reinterpret_cast<const frag_t<T>*>(p + (int64_t)sl * D));
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < RND; ++u)
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[e] = ok[u] ? acc[e] + to_f32(x[u][e]) : acc[e];
   }
