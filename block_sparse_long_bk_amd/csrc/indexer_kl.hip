@@ -626,7 +626,8 @@ __global__ void __launch_bounds__(512, 1) k_kl_main8(KlArgs a) {
   };
   // masked: some row of the tile sits before one of this wave's keys (its
   // local block, or a row past the item's end); otherwise every product is
-  // visible and the mask is skipped (the same sums, bit for bit).
+  // visible and both the mask and the clamp are skipped (a visible exponent
+  // exceeds 0 only by the rounding of the recomputed score).
   auto heads = [&](int hn, f32x16& pm, bool masked) {
     for (int hl = hs; hl < hn; hl += 2) {
       // the key fragments are read anew for each head: kept from one head to
@@ -657,7 +658,7 @@ __global__ void __launch_bounds__(512, 1) k_kl_main8(KlArgs a) {
         for (int q4 = 0; q4 < 4; ++q4) {
           const f32x4 l4 = *reinterpret_cast<const f32x4*>(&row_lsm[hl][8 * q4 + 4 * half]);
 #pragma unroll
-          for (int c = 0; c < 4; ++c) pm[4 * q4 + c] += exp2_fast(fminf(fmaf(s[4 * q4 + c], a.c_log2, -l4[c]), 0.f));
+          for (int c = 0; c < 4; ++c) pm[4 * q4 + c] += exp2_fast(fmaf(s[4 * q4 + c], a.c_log2, -l4[c]));
         }
       }
     }
