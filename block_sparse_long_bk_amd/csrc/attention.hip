@@ -486,23 +486,22 @@ __global__ void __launch_bounds__(256) k_combine(CombArgs a) {
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
   float W = 0.f;
   const T* po = static_cast<const T*>(a.part_o) + prow * a.S * D + sub * 8;
-  // Up to sixteen slots per round: all their loads are issued before any is
-  // used.  Partials are read exactly once, so the loads are non-temporal.
-  constexpr int RND = SMAX < 16 ? SMAX : 16;
+  // Eight slots per round: all their loads are issued before any is used.
+  // Partials are read exactly once, so the loads are non-temporal.
 #pragma unroll
-  for (int s0 = 0; s0 < SMAX; s0 += RND) {
+  for (int s0 = 0; s0 < SMAX; s0 += 8) {
     if (s0 < a.S) {
-      frag_t<T> v[RND];
-      float w[RND];
+      frag_t<T> v[8];
+      float w[8];
 #pragma unroll
-      for (int u = 0; u < RND; ++u) {
+      for (int u = 0; u < 8; ++u) {
         const int s = s0 + u;
         w[u] = ls[s] == -__builtin_huge_valf() ? 0.f : exp2_fast((ls[s] - Mref) * kLog2e);
         v[u] = s < a.S ? __builtin_nontemporal_load(reinterpret_cast<const frag_t<T>*>(po + (int64_t)s * D))
                        : zero_frag<T>();
       }
 #pragma unroll
-      for (int u = 0; u < RND; ++u) {
+      for (int u = 0; u < 8; ++u) {
         W += w[u];
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] = w[u] != 0.f ? fmaf(w[u], to_f32(v[u][e]), acc[e]) : acc[e];
