@@ -9,7 +9,9 @@ at a random offset, batch 1 or 2, hot blocks or sharp logits now and then,
 and the AUTO, KV-outer or query-outer schedule.  Selection must match row by
 row (tie band allowed and counted); attention is then compared, from the
 oracle's selection where a row lies in the tie band, under the same
-tolerances as every other parity test.
+tolerances as every other parity test.  The attention backward and the
+Index-Branch loss are checked on the same draws (alternate cases), for the
+oracle's selection, under their own tests' tolerances.
 """
 import numpy as np
 import pytest
@@ -60,3 +62,44 @@ def test_random_problem(i):
     mx, rl = assert_attention(wl.dtype, to_f64(out).reshape(out_o.shape), out_o,
                               host(lse).numpy().reshape(lse_o.shape), lse_o, what=f"random_{i}/{sched}")
     print(f"case {i}: selection {res['exact']} exact, {res['tie']} tie; max-abs {mx:.2e} rel-L2 {rl:.2e}")
+
+
+@pytest.mark.parametrize("i", range(0, N_CASES, 2))
+def test_random_backward(i):
+    """The attention backward on the same random problems (every other one),
+    for the oracle's selection, under the backward tests' tolerances."""
+    from tests.test_gpu_backward import attended_keys, check, run_backward
+    wl, _ = draw(i)
+    print(f"case {i}: {wl}", flush=True)
+    x = inputs.generate(wl, device="cuda", tensors=("q", "k", "v", "iq", "ik", "dout"))
+    h = {k: host(v) for k, v in x.items()}
+    prob = O.problem_of(wl)
+    ids = O.select(prob, O.block_scores(prob, h["iq"], h["ik"]))
+    rq, rk, rv = O.attend_backward(prob, h["q"], h["k"], h["v"], h["dout"], ids)
+    dq, dk, dv = run_backward(wl, x, ids)
+    errs = [check(wl.dtype, dq, rq, "dq"), check(wl.dtype, dk, rk, "dk"), check(wl.dtype, dv, rv, "dv")]
+    unseen = ~attended_keys(wl, ids)
+    assert np.all(to_f64(dk)[unseen] == 0) and np.all(to_f64(dv)[unseen] == 0), "gradients at unattended keys"
+    print(f"case {i}: (max-abs/max, rel-L2) dq {errs[0]}, dk {errs[1]}, dv {errs[2]}")
+
+
+@pytest.mark.parametrize("i", range(1, N_CASES, 2))
+def test_random_indexer_kl(i):
+    """The Index-Branch loss and its gradients on the other random problems,
+    for the oracle's selection, under the indexer-loss tests' tolerances."""
+    from tests.test_gpu_indexer_kl import LOSS_SCALE, check, run_kl, selected_keys
+    wl, _ = draw(i)
+    print(f"case {i}: {wl}", flush=True)
+    x = inputs.generate(wl, device="cuda")
+    h = {k: host(v) for k, v in x.items()}
+    prob = O.problem_of(wl)
+    ids = O.select(prob, O.block_scores(prob, h["iq"], h["ik"]))
+    rkl, riq, rik = O.indexer_kl(prob, h["q"], h["k"], h["iq"], h["ik"], ids, loss_scale=LOSS_SCALE)
+    kl, d_iq, d_ik = run_kl(wl, x, ids)
+    got = host(kl).numpy().astype(np.float64).reshape(-1, wl.h_kv)
+    err = float(np.max(np.abs(got - rkl)))
+    assert err <= 1e-4 * float(np.max(rkl)) + 1e-6, f"kl: max-abs {err:.3e}, max kl {np.max(rkl):.3e}"
+    e_q = check(wl.dtype, d_iq, riq.reshape(d_iq.shape), "d_iq")
+    e_k = check(wl.dtype, d_ik, rik, "d_ik")
+    assert np.all(to_f64(d_ik)[~selected_keys(wl, ids)] == 0), "d_ik at unselected keys"
+    print(f"case {i}: kl max-abs {err:.2e}, d_iq {e_q}, d_ik {e_k}")
