@@ -11,7 +11,9 @@ row (tie band allowed and counted); attention is then compared, from the
 oracle's selection where a row lies in the tie band, under the same
 tolerances as every other parity test.  The attention backward and the
 Index-Branch loss are checked on the same draws (alternate cases), for the
-oracle's selection, under their own tests' tolerances.
+oracle's selection, under their own tests' tolerances, and alternate cases
+run the whole forward over an all-MXFP8 cache that the oracle's quantiser
+built (the oracle scores and attends over the exactly decoded values).
 """
 import numpy as np
 import pytest
@@ -103,3 +105,37 @@ def test_random_indexer_kl(i):
     e_k = check(wl.dtype, d_ik, rik, "d_ik")
     assert np.all(to_f64(d_ik)[~selected_keys(wl, ids)] == 0), "d_ik at unselected keys"
     print(f"case {i}: kl max-abs {err:.2e}, d_iq {e_q}, d_ik {e_k}")
+
+
+def _mx_cache(t):
+    """The oracle's MXFP8 cache of a tensor (codes then scales, as the library
+    takes it) and its exactly dequantised values."""
+    codes, scales = O.mx_quantize(host(t))
+    cache = torch.from_numpy(np.concatenate([codes.reshape(-1), scales.reshape(-1)])).cuda()
+    return cache, np.ascontiguousarray(O.mx_dequantize(codes, scales).reshape(tuple(t.shape)))
+
+
+@pytest.mark.parametrize("i", range(0, N_CASES, 2))
+def test_random_all_mxfp8_cache(i):
+    """msa_forward over an all-MXFP8 cache (index keys, K and V) on the same
+    random problems: the oracle selects and attends over the exactly decoded
+    caches it built itself."""
+    wl, sched = draw(i)
+    print(f"case {i}: {wl} sched={sched}", flush=True)
+    x = inputs.generate(wl, device="cuda")
+    (ikc, ik64), (kc, k64), (vc, v64) = _mx_cache(x["ik"]), _mx_cache(x["k"]), _mx_cache(x["v"])
+    p = api.problem_of(wl, sched=sched, idx_format="mxfp8", kv_format="mxfp8")
+    ids, out, lse = api.forward(p, x["q"], kc, vc, x["iq"], ikc)
+    torch.cuda.synchronize()
+    prob = O.problem_of(wl)
+    s_o = O.block_scores(prob, np.ascontiguousarray(to_f64(x["iq"])), ik64)
+    ids_o = O.select(prob, s_o)
+    res = check_selection(wl, host(ids).numpy().reshape(wl.batch * wl.n_q, wl.h_kv, wl.topk), ids_o, s_o)
+    assert res["fail"] == 0, res
+    if res["tie"]:
+        out, lse = api.sparse_attention(p, x["q"], kc, vc, torch.from_numpy(ids_o.reshape(tuple(ids.shape))).cuda())
+        torch.cuda.synchronize()
+    o_o, l_o = O.attend(prob, np.ascontiguousarray(to_f64(x["q"])), k64, v64, ids_o)
+    mx, rl = assert_attention(wl.dtype, to_f64(out).reshape(o_o.shape), o_o, host(lse).numpy().reshape(l_o.shape),
+                              l_o, what=f"random_{i}/mxfp8/{sched}")
+    print(f"case {i}: selection {res['exact']} exact, {res['tie']} tie; max-abs {mx:.2e} rel-L2 {rl:.2e}")
