@@ -65,7 +65,9 @@
  * Supported: dtype MSA_BF16 or MSA_F32; block_size in {32, 64, 128} (the
  * pages use 128 and ablate the smaller sizes); d in {64, 128};
  * d_idx in {32, 64, 128}; 1 <= topk <= 32; Hq / Hkv a power of two <= 32;
- * 0 <= q_offset and q_offset + Nq <= Nk.
+ * 0 <= q_offset and q_offset + Nq <= Nk; nblk = ceil(Nk / Bk) <= 16384 (2M
+ * tokens at Bk = 128); B * Hkv <= 65535; Nq * topk and Nq * Hkv below 2^31.
+ * Outside these (but otherwise valid) a call returns MSA_ERR_UNSUPPORTED.
  *
  * Index keys may instead be an MXFP8 cache (idx_format = MSA_IDX_MXFP8; the
  * MiniMax write-up pairs MSA with MXFP8 caches for long-context decode,
