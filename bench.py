@@ -27,7 +27,9 @@ Also on the line, never as ``value``:
     figures), the decode step (16 sequences x 1M tokens; microseconds per
     token), the standalone Top-k, the training kernels;
   * ``cpu_baseline``: the oracle timed on a bounded sample of the headline
-    workload, on all host threads and on one.
+    workload, on all host threads and on one; the oracle's selection checks
+    of the headline and of each prefill leg are made in this leg (and skipped
+    with it, --no-cpu).
 Per-kernel times come from hipEvents that libmsa records around each launch
 on the launch stream.
 """
@@ -975,10 +977,14 @@ def main():
             leg = forward_summary(rl)
             leg["skew"] = skew_figures(rl["wl"], rl["ids"], rl["kern"])
             if not args.no_cpu:
+                # part of the CPU-baseline leg (the oracle runs only there):
+                # the oracle's selection of 64 sampled queries of this workload
                 xh = host_inputs(rl["x"])
                 qi = sample_queries(rl["wl"], 64)
                 ids_o, s_o, _, _ = oracle_rows(rl["wl"], xh, qi)
-                leg["selection_check"] = selection_check(rl["wl"], rl["ids"], qi, ids_o, s_o)
+                chk = selection_check(rl["wl"], rl["ids"], qi, ids_o, s_o)
+                line.setdefault("cpu_baseline", {}).setdefault("leg_selection_checks", {})[name] = chk
+                leg["selection_check"] = chk
                 del xh
             line[name] = leg
             if name == "prefill_32k" and not args.no_train:
