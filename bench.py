@@ -19,8 +19,8 @@ Also on the line, never as ``value``:
   * ``roofline`` of the dominant kernel of the headline step against its
     bound (the index tile: MFMA, with the method's flops), with
     ``frac_of_achievable`` against ``achievable_peaks``: what a 2 GiB device
-    copy, a 2 GiB fill and the library's bf16 8192^3 matmul reach on the
-    same GPU;
+    copy, a 2 GiB fill and the library's best bf16 matmul (of three shapes)
+    reach on the same GPU;
   * ``selection_check``: the GPU's selection of sampled rows against the
     fp64 oracle (exact, tie-band and failing rows);
   * legs: prefill_32k and the skewed 128k prefill (with block-popularity
@@ -427,39 +427,37 @@ def cpu_baseline_protocol(args):
 def achievable_peaks():
     """What this GPU reaches on plain work, as a second reference beside the
     published peaks: a 2 GiB device-to-device copy (read + write GB/s, like
-    the mixed traffic of the KV-outer pass) and a dense bf16 8192^3 matmul
-    from the installed library (TFLOP/s at whatever clock the chip holds
-    under it)."""
+    the mixed traffic of the KV-outer pass), a 2 GiB fill (write only), and
+    the installed library's dense bf16 matmul at three shapes (TFLOP/s at
+    whatever clock the chip holds under it; the best is the reference)."""
+    def timed(fn, reps):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
     src = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
-    a = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
-    b = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
-    for _ in range(2):
-        dst.copy_(src)
-        torch.matmul(a, b)
-    torch.cuda.synchronize()
-    e = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
-    e[0].record()
-    for _ in range(5):
-        dst.copy_(src)
-    e[1].record()
-    e[2].record()
-    for _ in range(10):
-        torch.matmul(a, b)
-    e[3].record()
-    e[4].record()
-    for _ in range(5):
-        dst.fill_(1)
-    e[5].record()
-    torch.cuda.synchronize()
-    copy_gbs = 2 * src.numel() * 5 / e[0].elapsed_time(e[1]) / 1e6
-    mm_tflops = 2.0 * 8192 ** 3 * 10 / e[2].elapsed_time(e[3]) / 1e9
-    write_gbs = dst.numel() * 5 / e[4].elapsed_time(e[5]) / 1e6
-    del src, dst, a, b
+    copy_gbs = 2 * src.numel() / timed(lambda: dst.copy_(src), 5) / 1e6
+    write_gbs = dst.numel() / timed(lambda: dst.fill_(1), 5) / 1e6
+    del src, dst
     torch.cuda.empty_cache()
-    return {"copy_GBs": copy_gbs, "write_GBs": write_gbs, "bf16_matmul_TFLOPs": mm_tflops,
-            "note": "2 GiB device copy (read + write), 2 GiB fill (write only) and torch.matmul bf16 8192^3 on "
-                    "this GPU"}
+    mm = {}
+    for m, n, k in ((8192, 8192, 8192), (16384, 16384, 8192), (32768, 8192, 8192)):
+        a = torch.randn(m, k, device="cuda", dtype=torch.bfloat16)
+        b = torch.randn(k, n, device="cuda", dtype=torch.bfloat16)
+        mm[f"{m}x{n}x{k}"] = 2.0 * m * n * k / timed(lambda: torch.matmul(a, b), 8) / 1e9
+        del a, b
+        torch.cuda.empty_cache()
+    return {"copy_GBs": copy_gbs, "write_GBs": write_gbs, "bf16_matmul_TFLOPs": max(mm.values()),
+            "bf16_matmul_by_shape": mm,
+            "note": "2 GiB device copy (read + write), 2 GiB fill (write only) and the best of torch.matmul bf16 "
+                    "at three shapes on this GPU"}
 
 
 def chunk_workspace_bytes(p, n_chunk):
