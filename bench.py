@@ -281,7 +281,7 @@ def cpu_baseline(wl, xh, n_sample, n_sample_1t):
                        f"all {wl.h_q} heads: index scores, Top-k and attention in fp64, {dt:.1f} s",
              "seconds": dt, "extrapolated_full_step_s": per_q * wl.n_q * wl.batch,
              "value_1thread": fl1 / dt1 / 1e12, "seconds_1thread": dt1,
-             "sample_1thread": f"{len(qi1)} of those queries on one thread"},
+             "sample_1thread": f"{len(qi1)} of those queries on one thread", "host": _host_info()},
             qi, ids, s)
 
 
